@@ -1,0 +1,278 @@
+"""fp64 CPU oracle of one SSD / Saguaro verify-and-pre-speculate round.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path (the
+HIP library under ``lossless_rejection_sampling_ssd_amd`` and its binding) never
+imports it, and the two share no code.
+
+This module is argument marshalling around ``ssd_oracle.c`` (plain C, IEEE double).
+It takes numpy arrays: fp32 logits as ``float32``, bf16 logits as their raw 16-bit
+patterns in ``uint16`` arrays, shaped ``[B, K+1, V]`` (a row stride ``ld`` larger
+than V is passed through ``ld``).  See ``ssd_oracle.c`` for the method, the passages
+of the two summaries of "Speculative Speculative Decoding" each step follows, and
+every reading taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+
+F32, BF16 = 0, 1
+PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
+ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE = 1, 2, 4
+E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
+FANOUT_EPS = 1e-9
+
+
+def build(force: bool = False) -> str:
+    """Compile ``ssd_oracle.c`` with gcc (fp64, OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, u64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+        L.orc_philox4x64_10.argtypes = [P, P, P]
+        L.orc_uniform.argtypes = [u64, u64, i32, i64, i64]
+        L.orc_uniform.restype = dbl
+        L.orc_uniform_u32.argtypes = [u64, u64, i32, i64, i64]
+        L.orc_uniform_u32.restype = ctypes.c_uint32
+        L.orc_fanout.argtypes = [i32, i32, dbl, P, P]
+        L.orc_fanout.restype = i32
+        L.orc_softmax.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, P, P, P]
+        L.orc_build_cache.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P]
+        L.orc_saguaro.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P, dbl, P, P]
+        L.orc_draft_sample.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P, dbl, u64, u64, P, P]
+        L.orc_verify.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, P, P, P, P, P, P, P, i32, P, P,
+                                 dbl, u64, u64, P, P, P, P]
+        L.orc_residual_sample.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, P, P, P, P, P, P, i32, P,
+                                          P, dbl, P, u64, u64, P, P, P, P, P]
+        L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, P, P, P, P]
+        L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i32,
+                                P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logit_info(z):
+    """(dtype code, B, K, V, ld) of a logit array [B, K+1, V] (possibly a view with a
+    larger row stride)."""
+    if z.dtype == np.float32:
+        code, item = F32, 4
+    elif z.dtype == np.uint16:
+        code, item = BF16, 2
+    else:
+        raise TypeError("logits must be float32 or uint16 (bf16 bit patterns)")
+    if z.ndim != 3:
+        raise ValueError("logits must be [B, K+1, V]")
+    B, K1, V = z.shape
+    if z.strides[2] != item or z.strides[1] % item or z.strides[0] != z.strides[1] * K1:
+        raise ValueError("logits rows must be unit-stride with a uniform row stride")
+    return code, B, K1 - 1, V, z.strides[1] // item
+
+
+def _base(z):
+    return z.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------
+def philox4x64_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    lib().orc_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform(seed, round_, purpose, b, i) -> float:
+    return lib().orc_uniform(seed, round_, purpose, b, i)
+
+
+def uniform_u32(seed, round_, purpose, b, i) -> int:
+    return lib().orc_uniform_u32(seed, round_, purpose, b, i)
+
+
+def fanout(K: int, Bf: int, r: float):
+    """Returns (F [K+1] int32, smallest remainder gap)."""
+    F = np.zeros(K + 1, dtype=np.int32)
+    gap = ctypes.c_double(0.0)
+    rc = lib().orc_fanout(K, Bf, r, _ptr(F), ctypes.byref(gap))
+    if rc != 0:
+        raise ValueError("bad fan-out arguments")
+    return F, gap.value
+
+
+def softmax(z, T: float, want_probs: bool = False):
+    code, B, K, V, ld = _logit_info(z)
+    R = B * (K + 1)
+    m = np.zeros(R)
+    s = np.zeros(R)
+    a = np.zeros(R, dtype=np.int32)
+    probs = np.zeros((B, K + 1, V)) if want_probs else None
+    lib().orc_softmax(B, K, V, ld, code, _base(z), T, _ptr(m), _ptr(s), _ptr(a), _ptr(probs))
+    shp = (B, K + 1)
+    return m.reshape(shp), s.reshape(shp), a.reshape(shp), probs
+
+
+def build_cache(zq, T: float, F):
+    code, B, K, V, ld = _logit_info(zq)
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    Bf = int(F.sum())
+    ids = np.zeros((B, Bf), dtype=np.int32)
+    mass = np.zeros((B, K + 1))
+    lib().orc_build_cache(B, K, V, ld, code, _base(zq), T, _ptr(F), Bf, _ptr(ids), _ptr(mass))
+    return ids, mass
+
+
+def saguaro(zq, T: float, F, cache_ids, cache_mass, C: float, want_qprime: bool = False):
+    code, B, K, V, ld = _logit_info(zq)
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
+    cache_mass = np.ascontiguousarray(cache_mass, dtype=np.float64)
+    Z = np.zeros((B, K + 1))
+    qp = np.zeros((B, K + 1, V)) if want_qprime else None
+    lib().orc_saguaro(B, K, V, ld, code, _base(zq), T, _ptr(F), int(F.sum()), _ptr(cache_ids),
+                      _ptr(cache_mass), C, _ptr(Z), _ptr(qp))
+    return Z, qp
+
+
+def draft_sample(zq, T: float, F, cache_ids, Z, C: float, seed: int, round_: int):
+    """Harness step: draft tokens sampled from the reweighted draft law q'."""
+    code, B, K, V, ld = _logit_info(zq)
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
+    Z = np.ascontiguousarray(Z, dtype=np.float64)
+    d = np.zeros((B, K), dtype=np.int32)
+    flags = np.zeros((B, K), dtype=np.uint8)
+    lib().orc_draft_sample(B, K, V, ld, code, _base(zq), T, _ptr(F), int(F.sum()), _ptr(cache_ids),
+                           _ptr(Z), C, seed, round_, _ptr(d), _ptr(flags))
+    return d, flags
+
+
+def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_):
+    code, B, K, V, ld = _logit_info(zp)
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    pm, ps, pa = (np.ascontiguousarray(x) for x in pstats[:3])
+    qm, qs, qa = (np.ascontiguousarray(x) for x in qstats[:3])
+    draft = np.ascontiguousarray(draft, dtype=np.int32)
+    cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
+    Z = np.ascontiguousarray(Z, dtype=np.float64)
+    acc = np.zeros(B, dtype=np.int32)
+    aprob = np.zeros((B, K))
+    err = np.zeros(B, dtype=np.int32)
+    exc = np.zeros(B, dtype=np.uint8)
+    lib().orc_verify(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(draft), _ptr(pm), _ptr(ps), _ptr(pa),
+                     _ptr(qm), _ptr(qs), _ptr(qa), _ptr(F), int(F.sum()), _ptr(cache_ids), _ptr(Z), C,
+                     seed, round_, _ptr(acc), _ptr(aprob), _ptr(err), _ptr(exc))
+    return acc, aprob, err, exc
+
+
+def residual_sample(zp, zq, T, pstats, qstats, F, cache_ids, Z, C, accept_len, seed, round_,
+                    want_resid: bool = False):
+    code, B, K, V, ld = _logit_info(zp)
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    pm, ps, pa = (np.ascontiguousarray(x) for x in pstats[:3])
+    qm, qs, qa = (np.ascontiguousarray(x) for x in qstats[:3])
+    cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
+    Z = np.ascontiguousarray(Z, dtype=np.float64)
+    accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
+    bonus = np.zeros(B, dtype=np.int32)
+    zr = np.zeros(B)
+    resid = np.zeros((B, V)) if want_resid else None
+    err = np.zeros(B, dtype=np.int32)
+    exc = np.zeros(B, dtype=np.uint8)
+    lib().orc_residual_sample(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(pm), _ptr(ps), _ptr(pa),
+                              _ptr(qm), _ptr(qs), _ptr(qa), _ptr(F), int(F.sum()), _ptr(cache_ids),
+                              _ptr(Z), C, _ptr(accept_len), seed, round_, _ptr(bonus), _ptr(zr),
+                              _ptr(resid), _ptr(err), _ptr(exc))
+    return bonus, zr, resid, err, exc
+
+
+def cache_lookup(K, V, F, cache_ids, accept_len, bonus, fallback_uniform, seed, round_):
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
+    accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
+    bonus = np.ascontiguousarray(bonus, dtype=np.int32)
+    B = accept_len.shape[0]
+    hit = np.zeros(B, dtype=np.uint8)
+    slot = np.zeros(B, dtype=np.int32)
+    fb = np.zeros((B, K), dtype=np.int32)
+    err = np.zeros(B, dtype=np.int32)
+    lib().orc_cache_lookup(B, K, V, _ptr(F), int(F.sum()), _ptr(cache_ids), _ptr(accept_len), _ptr(bonus),
+                           int(bool(fallback_uniform)), seed, round_, _ptr(hit), _ptr(slot), _ptr(fb), _ptr(err))
+    return hit, slot, fb, err
+
+
+@dataclass
+class RoundResult:
+    p_max: np.ndarray
+    p_sum: np.ndarray
+    p_arg: np.ndarray
+    q_max: np.ndarray
+    q_sum: np.ndarray
+    q_arg: np.ndarray
+    cache_ids: np.ndarray
+    cache_mass: np.ndarray
+    Z: np.ndarray
+    accept_len: np.ndarray
+    accept_prob: np.ndarray
+    bonus: np.ndarray
+    resid_mass: np.ndarray
+    hit: np.ndarray
+    slot: np.ndarray
+    fallback_tokens: np.ndarray
+    err: np.ndarray
+    exc: np.ndarray
+
+
+def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap=None) -> RoundResult:
+    """One whole round in the method's order.  ``exc`` holds the per-sequence
+    exception bits E1..E5 decided from the oracle's own fp64 values."""
+    code, B, K, V, ld = _logit_info(zp)
+    code2, B2, K2, V2, ld2 = _logit_info(zq)
+    if (code, B, K, V, ld) != (code2, B2, K2, V2, ld2):
+        raise ValueError("p and q logits must have the same layout")
+    F = np.ascontiguousarray(F, dtype=np.int32)
+    Bf = int(F.sum())
+    draft = np.ascontiguousarray(draft, dtype=np.int32)
+    R = (B, K + 1)
+    out = RoundResult(
+        p_max=np.zeros(R), p_sum=np.zeros(R), p_arg=np.zeros(R, np.int32),
+        q_max=np.zeros(R), q_sum=np.zeros(R), q_arg=np.zeros(R, np.int32),
+        cache_ids=np.zeros((B, Bf), np.int32), cache_mass=np.zeros(R), Z=np.zeros(R),
+        accept_len=np.zeros(B, np.int32), accept_prob=np.zeros((B, K)), bonus=np.zeros(B, np.int32),
+        resid_mass=np.zeros(B), hit=np.zeros(B, np.uint8), slot=np.zeros(B, np.int32),
+        fallback_tokens=np.zeros((B, K), np.int32), err=np.zeros(B, np.int32), exc=np.zeros(B, np.uint8))
+    o = out
+    lib().orc_round(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(F), Bf, C, _ptr(draft), seed,
+                    round_idx, int(bool(fallback_uniform)), _ptr(o.p_max), _ptr(o.p_sum), _ptr(o.p_arg),
+                    _ptr(o.q_max), _ptr(o.q_sum), _ptr(o.q_arg), _ptr(o.cache_ids), _ptr(o.cache_mass),
+                    _ptr(o.Z), _ptr(o.accept_len), _ptr(o.accept_prob), _ptr(o.bonus), _ptr(o.resid_mass),
+                    _ptr(o.hit), _ptr(o.slot), _ptr(o.fallback_tokens), _ptr(o.err), _ptr(o.exc))
+    if fanout_gap is not None and fanout_gap < FANOUT_EPS:
+        o.exc |= E4_FANOUT_TIE
+    return out

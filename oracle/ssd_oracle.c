@@ -1,0 +1,557 @@
+/*
+ * ssd_oracle.c -- plain fp64 CPU oracle of one verify-and-pre-speculate round of
+ * Speculative Speculative Decoding (SSD) with the Saguaro algorithm.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The product path
+ * (the HIP library and its Python binding) never calls it, and this file shares no
+ * code, header, table or constant generator with that path.
+ *
+ * Sources.  The method is described by two summaries of the paper "Speculative
+ * Speculative Decoding" (Kumar, Dao, May):
+ *   [zh]  gist.science/zh/paper/2603.03251, technical part, section 2 (Methodology:
+ *         basic flow; Challenge 1 geometric fan-out; Challenge 2 Saguaro sampling;
+ *         Challenge 3 fallback), section 1 (the round is lossless);
+ *   [nl]  gist.science/nl/paper/2603.03251, technical part, section 2 (Kernprincipes)
+ *         and section 3 A (geometric fan-out), 3 B (Saguaro sampling), 3 C (fallback).
+ * The pages assert losslessness and name the parts; they print no formula.  The
+ * formulas below are the standard lossless speculative-sampling construction that
+ * the lossless claim requires (accept with min(1, p/q'), resample from the
+ * normalised residual max(p - q', 0), sample from p when every draft token is
+ * accepted), with q' the Saguaro-reweighted draft law the draft actually samples
+ * from.  Every reading of a step the pages leave open is marked READING below.
+ *
+ * Arithmetic: every probability is computed in IEEE double.  bf16 and fp32 inputs
+ * are widened exactly.  The code follows the steps in the order of the round:
+ *   fan-out -> softmax -> speculation cache -> Saguaro reweight -> verify ->
+ *   bonus (residual) -> cache lookup,
+ * with one plain loop per definition; the only library routines used are qsort
+ * (sorting candidate ids) and exp/pow/floor from libm.
+ *
+ * Pins: the Python tests check these functions against closed forms, numpy
+ * library routines, exact enumeration on tiny vocabularies and numpy's own
+ * Philox4x64 generator.  No function here is "parity unpinned".
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Purposes of the counter-based uniforms (key word 1). */
+#define ORC_PURPOSE_ACCEPT 0
+#define ORC_PURPOSE_BONUS 1
+#define ORC_PURPOSE_DRAFT 2
+#define ORC_PURPOSE_FALLBACK 3
+
+/* Data-dependent error bits (per sequence). */
+#define ORC_ERR_TOKEN_RANGE 1   /* a draft token outside [0, V) */
+#define ORC_ERR_QPRIME_ZERO 2   /* q'(d) == 0 for a tested draft token */
+#define ORC_ERR_LEN_RANGE 4     /* accept_len outside [0, K] given to a step */
+
+/* Near-tie / range exception bits (per sequence), decided from fp64 values. */
+#define ORC_E1_ACCEPT_TIE 1
+#define ORC_E2_CDF_TIE 2
+#define ORC_E3_DEGENERATE_RESIDUAL 4
+#define ORC_E4_FANOUT_TIE 8
+#define ORC_E5_TINY_PROB 16
+
+#define ORC_TIE_EPS 1e-5
+#define ORC_RESID_EPS 1e-5
+#define ORC_FANOUT_EPS 1e-9
+#define ORC_TINY 1e-30
+
+/* ------------------------------------------------------------------------- */
+/* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ * 1, 2, 3", SC'11): ten rounds of two 64x64->128 multiplications per round with the
+ * published multipliers, the key bumped by the published Weyl constants between
+ * rounds. */
+static void mulhilo64(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
+    unsigned __int128 p = (unsigned __int128)a * (unsigned __int128)b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        uint64_t hi0, lo0, hi1, lo1;
+        mulhilo64(M0, c0, &hi0, &lo0);
+        mulhilo64(M1, c2, &hi1, &lo1);
+        uint64_t n0 = hi1 ^ c1 ^ k0;
+        uint64_t n1 = lo1;
+        uint64_t n2 = hi0 ^ c3 ^ k1;
+        uint64_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += W0; k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* First output word for key (seed, purpose) and counter (round, b, i, 0). */
+static uint64_t philox_word(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
+    uint64_t ctr[4] = {round, (uint64_t)b, (uint64_t)i, 0};
+    uint64_t key[2] = {seed, (uint64_t)purpose};
+    uint64_t out[4];
+    orc_philox4x64_10(ctr, key, out);
+    return out[0];
+}
+
+/* READING: one uniform per (sequence, position, purpose); the top 24 bits of the
+ * first output word scaled by 2^-24, a value in [0, 1) that fp32 holds exactly. */
+double orc_uniform(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
+    return (double)(philox_word(seed, round, purpose, b, i) >> 40) * (1.0 / 16777216.0);
+}
+
+uint32_t orc_uniform_u32(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
+    return (uint32_t)(philox_word(seed, round, purpose, b, i) >> 32);
+}
+
+/* ------------------------------------------------------------------------- */
+static double load_logit(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Row r = b*(K+1) + i of a [B, K+1, V] logit tensor with row stride ld, widened to
+ * double into out[V]. */
+static void load_row(const void* logits, int dtype, int64_t ld, int64_t r, int V, double* out) {
+    for (int x = 0; x < V; ++x) out[x] = load_logit(logits, dtype, r * ld + x);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Geometric fan-out ([zh] section 2, Challenge 1; [nl] section 3 A): the budget B_f
+ * of cached bonus candidates is split over acceptance lengths k = 0..K in
+ * proportion to r^k.  READING: integer shares by the largest-remainder method,
+ * remainders compared largest first with ties to the lower k.
+ * Returns 0 on success, -1 on bad arguments.  *min_gap (nullable) receives the
+ * smallest distance between two remainders, for the fan-out near-tie case. */
+int orc_fanout(int K, int Bf, double r, int32_t* F, double* min_gap) {
+    if (K < 1 || Bf < 0 || !(r > 0.0) || !(r <= 1.0)) return -1;
+    double f[64], rem[64], wsum = 0.0;
+    int given[64];
+    if (K + 1 > 64) return -1;
+    for (int k = 0; k <= K; ++k) wsum += pow(r, (double)k);
+    int total = 0;
+    for (int k = 0; k <= K; ++k) {
+        f[k] = (double)Bf * pow(r, (double)k) / wsum;
+        F[k] = (int32_t)floor(f[k]);
+        rem[k] = f[k] - floor(f[k]);
+        given[k] = 0;
+        total += F[k];
+    }
+    int left = Bf - total;
+    for (int n = 0; n < left; ++n) {
+        int best = -1;
+        for (int k = 0; k <= K; ++k) {
+            if (given[k]) continue;
+            if (best < 0 || rem[k] > rem[best]) best = k;
+        }
+        F[best] += 1;
+        given[best] = 1;
+    }
+    if (min_gap) {
+        double g = INFINITY;
+        for (int a = 0; a <= K; ++a)
+            for (int c = a + 1; c <= K; ++c) {
+                double d = fabs(rem[a] - rem[c]);
+                if (d < g) g = d;
+            }
+        *min_gap = g;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Temperature softmax of one row ([zh] section 2 and section 4 name temperature as
+ * an axis of the method; the round consumes p = softmax(z_p / T) and
+ * q = softmax(z_q / T)).  READING: T = 0 is the greedy limit, a one-hot law on the
+ * lowest id among the maxima. */
+static void softmax_row(const double* z, int V, double T, double* m_out, double* s_out,
+                        int32_t* arg_out, double* prob /* nullable */) {
+    double m = z[0];
+    int arg = 0;
+    for (int x = 1; x < V; ++x)
+        if (z[x] > m) { m = z[x]; arg = x; }
+    double s;
+    if (T > 0.0) {
+        s = 0.0;
+        for (int x = 0; x < V; ++x) s += exp((z[x] - m) / T);
+        if (prob)
+            for (int x = 0; x < V; ++x) prob[x] = exp((z[x] - m) / T) / s;
+    } else {
+        s = 1.0;
+        if (prob)
+            for (int x = 0; x < V; ++x) prob[x] = (x == arg) ? 1.0 : 0.0;
+    }
+    *m_out = m;
+    *s_out = s;
+    *arg_out = arg;
+}
+
+/* Probability of token x in a row whose statistics are (m, s, arg). */
+static double row_prob(double zx, int x, double m, double s, int arg, double T) {
+    if (T > 0.0) return exp((zx - m) / T) / s;
+    return (x == arg) ? 1.0 : 0.0;
+}
+
+void orc_softmax(int B, int K, int V, int64_t ld, int dtype, const void* logits, double T,
+                 double* row_max, double* row_sum, int32_t* row_argmax, double* probs) {
+    const int64_t R = (int64_t)B * (K + 1);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        double* z = (double*)malloc(sizeof(double) * V);
+        load_row(logits, dtype, ld, r, V, z);
+        softmax_row(z, V, T, &row_max[r], &row_sum[r], &row_argmax[r],
+                    probs ? probs + r * (int64_t)V : NULL);
+        free(z);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Speculation cache ([zh] section 2, flow step 2-3 and Challenge 1; [nl] section 2
+ * and 3 A): an outcome is (k accepted, bonus token); for each k the cache holds
+ * F_k candidate bonus tokens.  READING: the candidates for length k are the F_k ids
+ * of largest draft logit z_q[b, k, .] (ties to the lower id), i.e. the top-F of the
+ * draft law at that position before reweighting, stored in that order at
+ * cache_ids[b, O_k .. O_k + F_k - 1] with O_k = F_0 + ... + F_{k-1}.  The cached
+ * draft mass is M_k = sum over the candidates of q_k(x). */
+typedef struct { double v; int id; } orc_cand;
+
+static int cand_cmp(const void* pa, const void* pb) {
+    const orc_cand* a = (const orc_cand*)pa;
+    const orc_cand* b = (const orc_cand*)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->id < b->id) ? -1 : (a->id > b->id);
+}
+
+void orc_build_cache(int B, int K, int V, int64_t ld, int dtype, const void* q_logits, double T,
+                     const int32_t* F, int Bf, int32_t* cache_ids, double* cache_mass) {
+    (void)Bf;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bk = 0; bk < (int64_t)B * (K + 1); ++bk) {
+        int b = (int)(bk / (K + 1)), k = (int)(bk % (K + 1));
+        int Ok = 0;
+        for (int j = 0; j < k; ++j) Ok += F[j];
+        double* z = (double*)malloc(sizeof(double) * V);
+        orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * V);
+        load_row(q_logits, dtype, ld, bk, V, z);
+        double m, s;
+        int32_t arg;
+        softmax_row(z, V, T, &m, &s, &arg, NULL);
+        for (int x = 0; x < V; ++x) { c[x].v = z[x]; c[x].id = x; }
+        qsort(c, V, sizeof(orc_cand), cand_cmp);
+        double M = 0.0;
+        for (int j = 0; j < F[k]; ++j) {
+            cache_ids[(int64_t)b * Bf + Ok + j] = c[j].id;
+            M += row_prob(z[c[j].id], c[j].id, m, s, arg, T);
+        }
+        cache_mass[bk] = M;
+        free(c);
+        free(z);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Saguaro sampling ([zh] section 2, Challenge 2; [nl] section 3 B): the draft law
+ * is reweighted by a factor C on the cached top-F tokens and renormalised, which
+ * moves residual mass onto the cached tokens.  READING: C in (0, 1],
+ *   Z_k = 1 - (1 - C) M_k,   q'_k(x) = q_k(x) * (C if x in S_k else 1) / Z_k. */
+static int in_cache(const int32_t* ids, int n, int x) {
+    for (int j = 0; j < n; ++j)
+        if (ids[j] == x) return 1;
+    return 0;
+}
+
+void orc_saguaro(int B, int K, int V, int64_t ld, int dtype, const void* q_logits, double T,
+                 const int32_t* F, int Bf, const int32_t* cache_ids, const double* cache_mass,
+                 double C, double* Z, double* q_prime /* nullable [B, K+1, V] */) {
+    const int64_t R = (int64_t)B * (K + 1);
+    for (int64_t r = 0; r < R; ++r) Z[r] = 1.0 - (1.0 - C) * cache_mass[r];
+    if (!q_prime) return;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        int b = (int)(r / (K + 1)), k = (int)(r % (K + 1));
+        int Ok = 0;
+        for (int j = 0; j < k; ++j) Ok += F[j];
+        const int32_t* S = cache_ids + (int64_t)b * Bf + Ok;
+        double* z = (double*)malloc(sizeof(double) * V);
+        load_row(q_logits, dtype, ld, r, V, z);
+        double m, s;
+        int32_t arg;
+        softmax_row(z, V, T, &m, &s, &arg, NULL);
+        for (int x = 0; x < V; ++x) {
+            double w = in_cache(S, F[k], x) ? C : 1.0;
+            q_prime[r * V + x] = row_prob(z[x], x, m, s, arg, T) * w / Z[r];
+        }
+        free(z);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Inverse-CDF selection: the smallest j whose running sum of w exceeds u * total,
+ * ids scanned in ascending order; if rounding leaves no such j, the largest j with
+ * w_j > 0.  *gap (nullable) receives min(|C(j*) - u|, |C(j*-1) - u|) with
+ * C(j) = cumsum_j / total, the distance of u to the two CDF steps around j*. */
+static int inverse_cdf(const double* w, int V, double total, double u, double* gap) {
+    double target = u * total, run = 0.0, prev = 0.0;
+    int pick = -1;
+    for (int j = 0; j < V; ++j) {
+        prev = run;
+        run += w[j];
+        if (run > target) { pick = j; break; }
+    }
+    if (pick < 0) {
+        for (int j = V - 1; j >= 0; --j)
+            if (w[j] > 0.0) { pick = j; break; }
+        if (pick < 0) pick = V - 1;
+        prev = total - w[pick];
+        run = total;
+    }
+    if (gap) {
+        double a = fabs(run / total - u), c = fabs(prev / total - u);
+        *gap = a < c ? a : c;
+    }
+    return pick;
+}
+
+/* Draft tokens for a synthetic round (harness step, not part of the timed round):
+ * the draft samples d_i from its Saguaro-reweighted law q'_i ([zh] section 2,
+ * Challenge 2: the reweighting is applied while the draft samples) by inverse CDF
+ * with u = U(seed, round, b, i, DRAFT).  At T = 0 the draft is greedy. */
+void orc_draft_sample(int B, int K, int V, int64_t ld, int dtype, const void* q_logits, double T,
+                      const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
+                      uint64_t seed, uint64_t round, int32_t* draft, uint8_t* tie_flags /* [B,K] */) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bi = 0; bi < (int64_t)B * K; ++bi) {
+        int b = (int)(bi / K), i = (int)(bi % K);
+        int64_t r = (int64_t)b * (K + 1) + i;
+        int Oi = 0;
+        for (int j = 0; j < i; ++j) Oi += F[j];
+        const int32_t* S = cache_ids + (int64_t)b * Bf + Oi;
+        double* z = (double*)malloc(sizeof(double) * V);
+        double* w = (double*)malloc(sizeof(double) * V);
+        load_row(q_logits, dtype, ld, r, V, z);
+        double m, s;
+        int32_t arg;
+        softmax_row(z, V, T, &m, &s, &arg, NULL);
+        uint8_t flag = 0;
+        if (T > 0.0) {
+            double tot = 0.0;
+            for (int x = 0; x < V; ++x) {
+                w[x] = row_prob(z[x], x, m, s, arg, T) * (in_cache(S, F[i], x) ? C : 1.0) / Z[r];
+                tot += w[x];
+            }
+            double u = orc_uniform(seed, round, ORC_PURPOSE_DRAFT, b, i), gap;
+            draft[bi] = inverse_cdf(w, V, tot, u, &gap);
+            if (gap < ORC_TIE_EPS) flag = ORC_E2_CDF_TIE;
+        } else {
+            draft[bi] = arg;
+        }
+        if (tie_flags) tie_flags[bi] = flag;
+        free(w);
+        free(z);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Lossless verification ([zh] section 2, flow steps 2 and 4; [nl] section 2): the
+ * target checks the K draft tokens of a sequence in order; the outcome is the
+ * accepted length k.  READING (standard lossless speculative sampling):
+ *   ratio_i = p_i(d_i) / q'_i(d_i), accept iff U(seed, round, b, i, ACCEPT) < ratio_i,
+ *   k = first rejected position, or K when all are accepted;
+ *   accept_prob_i = min(1, ratio_i).  At T = 0: accept iff d_i = argmax p_i.
+ * Per sequence, e1 receives the accept near-tie and tiny-probability bits for the
+ * positions tested (0 .. min(k, K-1)). */
+void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
+                const void* q_logits, double T, const int32_t* draft,
+                const double* p_max, const double* p_sum, const int32_t* p_arg,
+                const double* q_max, const double* q_sum, const int32_t* q_arg,
+                const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
+                uint64_t seed, uint64_t round, int32_t* accept_len, double* accept_prob,
+                int32_t* err, uint8_t* exc) {
+    for (int b = 0; b < B; ++b) {
+        int k = K, e = 0, x_flags = 0;
+        int Oi = 0;
+        for (int i = 0; i < K; ++i) {
+            int64_t r = (int64_t)b * (K + 1) + i;
+            int d = draft[(int64_t)b * K + i];
+            const int32_t* S = cache_ids + (int64_t)b * Bf + Oi;
+            Oi += F[i];
+            double ratio;
+            int ok = 1;
+            if (d < 0 || d >= V) {
+                e |= ORC_ERR_TOKEN_RANGE;
+                ok = 0;
+                ratio = 0.0;
+            } else if (T > 0.0) {
+                double p = row_prob(load_logit(p_logits, dtype, r * ld + d), d, p_max[r], p_sum[r], p_arg[r], T);
+                double q = row_prob(load_logit(q_logits, dtype, r * ld + d), d, q_max[r], q_sum[r], q_arg[r], T);
+                double qp = q * (in_cache(S, F[i], d) ? C : 1.0) / Z[r];
+                if (qp <= 0.0) {
+                    e |= ORC_ERR_QPRIME_ZERO;
+                    ok = 0;
+                    ratio = 0.0;
+                } else {
+                    ratio = p / qp;
+                }
+                if (k == K) {
+                    /* no earlier rejection: this position is tested */
+                    double u = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b, i);
+                    if (fabs(u - ratio) < ORC_TIE_EPS) x_flags |= ORC_E1_ACCEPT_TIE;
+                    if (p < ORC_TINY || qp < ORC_TINY) x_flags |= ORC_E5_TINY_PROB;
+                }
+            } else {
+                ratio = (d == p_arg[r]) ? 1.0 : 0.0;
+            }
+            if (accept_prob) accept_prob[(int64_t)b * K + i] = ratio < 1.0 ? ratio : 1.0;
+            if (k == K) {
+                int acc;
+                if (!ok) acc = 0;
+                else if (T > 0.0) acc = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b, i) < ratio;
+                else acc = (d == p_arg[r]);
+                if (!acc) k = i;
+            }
+        }
+        accept_len[b] = k;
+        if (err) err[b] |= e;
+        if (exc) exc[b] |= (uint8_t)x_flags;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Bonus token ([zh] section 2, flow step 2 and Challenge 2: the bonus comes from the
+ * residual distribution; [nl] section 3 B).  READING (standard): with k the accepted
+ * length,
+ *   k < K:  w(x) = max(p_k(x) - q'_k(x), 0), Z_r = sum w; if Z_r == 0 (only through
+ *           rounding) w = p_k;
+ *   k = K:  w = p_K, Z_r = sum w;
+ * bonus = inverse CDF of w at u = U(seed, round, b, k, BONUS).  At T = 0 the bonus is
+ * argmax p_k.  resid (nullable [B, V]) receives w, resid_mass receives Z_r. */
+void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
+                         const void* q_logits, double T,
+                         const double* p_max, const double* p_sum, const int32_t* p_arg,
+                         const double* q_max, const double* q_sum, const int32_t* q_arg,
+                         const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
+                         const int32_t* accept_len, uint64_t seed, uint64_t round, int32_t* bonus,
+                         double* resid_mass, double* resid, int32_t* err, uint8_t* exc) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        int k = accept_len[b];
+        if (k < 0 || k > K) {
+            bonus[b] = -1;
+            if (resid_mass) resid_mass[b] = 0.0;
+            if (err) err[b] |= ORC_ERR_LEN_RANGE;
+            continue;
+        }
+        int64_t r = (int64_t)b * (K + 1) + k;
+        if (!(T > 0.0)) {
+            bonus[b] = p_arg[r];
+            if (resid_mass) resid_mass[b] = 1.0;
+            if (resid)
+                for (int x = 0; x < V; ++x) resid[(int64_t)b * V + x] = (x == p_arg[r]) ? 1.0 : 0.0;
+            continue;
+        }
+        int Ok = 0;
+        for (int j = 0; j < k; ++j) Ok += F[j];
+        const int32_t* S = cache_ids + (int64_t)b * Bf + Ok;
+        double* w = (double*)malloc(sizeof(double) * V);
+        double Zr = 0.0;
+        for (int x = 0; x < V; ++x) {
+            double p = row_prob(load_logit(p_logits, dtype, r * ld + x), x, p_max[r], p_sum[r], p_arg[r], T);
+            if (k < K) {
+                double q = row_prob(load_logit(q_logits, dtype, r * ld + x), x, q_max[r], q_sum[r], q_arg[r], T);
+                double qp = q * (in_cache(S, F[k], x) ? C : 1.0) / Z[r];
+                w[x] = p - qp > 0.0 ? p - qp : 0.0;
+            } else {
+                w[x] = p;
+            }
+            Zr += w[x];
+        }
+        uint8_t x_flags = 0;
+        if (k < K && Zr < ORC_RESID_EPS) x_flags |= ORC_E3_DEGENERATE_RESIDUAL;
+        if (Zr <= 0.0) {
+            Zr = 0.0;
+            for (int x = 0; x < V; ++x) {
+                w[x] = row_prob(load_logit(p_logits, dtype, r * ld + x), x, p_max[r], p_sum[r], p_arg[r], T);
+                Zr += w[x];
+            }
+        }
+        double u = orc_uniform(seed, round, ORC_PURPOSE_BONUS, b, k), gap;
+        bonus[b] = inverse_cdf(w, V, Zr, u, &gap);
+        if (gap < ORC_TIE_EPS) x_flags |= ORC_E2_CDF_TIE;
+        if (resid_mass) resid_mass[b] = Zr;
+        if (resid)
+            for (int x = 0; x < V; ++x) resid[(int64_t)b * V + x] = w[x];
+        if (exc) exc[b] |= x_flags;
+        free(w);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Cache lookup ([zh] section 2, flow step 4: hit returns the pre-speculated tokens,
+ * miss falls back; Challenge 3: at large batch the fallback is a fast speculator,
+ * e.g. random tokens; [nl] section 2 and 3 C).  hit = bonus in S_k, slot = O_k +
+ * position in S_k or -1.  READING: on a miss with the uniform fallback the next
+ * draft is K tokens floor(U32 * V / 2^32) with U32 = U32(seed, round, b, j,
+ * FALLBACK); otherwise the fallback tokens are -1. */
+void orc_cache_lookup(int B, int K, int V, const int32_t* F, int Bf, const int32_t* cache_ids,
+                      const int32_t* accept_len, const int32_t* bonus, int fallback_uniform,
+                      uint64_t seed, uint64_t round, uint8_t* hit, int32_t* slot,
+                      int32_t* fallback_tokens, int32_t* err) {
+    for (int b = 0; b < B; ++b) {
+        int k = accept_len[b];
+        int h = 0, sl = -1;
+        if (k < 0 || k > K) {
+            if (err) err[b] |= ORC_ERR_LEN_RANGE;
+        } else {
+            int Ok = 0;
+            for (int j = 0; j < k; ++j) Ok += F[j];
+            for (int j = 0; j < F[k]; ++j)
+                if (cache_ids[(int64_t)b * Bf + Ok + j] == bonus[b]) { h = 1; sl = Ok + j; break; }
+        }
+        hit[b] = (uint8_t)h;
+        slot[b] = sl;
+        for (int j = 0; j < K; ++j) {
+            int32_t t = -1;
+            if (!h && fallback_uniform) {
+                uint64_t x = orc_uniform_u32(seed, round, ORC_PURPOSE_FALLBACK, b, j);
+                t = (int32_t)((x * (uint64_t)V) >> 32);
+            }
+            fallback_tokens[(int64_t)b * K + j] = t;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* The whole round in the order of the method: softmax (both models), cache build,
+ * Saguaro reweight, verify, bonus, lookup.  All outputs in double / int. */
+void orc_round(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
+               const void* q_logits, double T, const int32_t* F, int Bf, double C,
+               const int32_t* draft, uint64_t seed, uint64_t round, int fallback_uniform,
+               double* p_max, double* p_sum, int32_t* p_arg, double* q_max, double* q_sum,
+               int32_t* q_arg, int32_t* cache_ids, double* cache_mass, double* Z,
+               int32_t* accept_len, double* accept_prob, int32_t* bonus, double* resid_mass,
+               uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* err, uint8_t* exc) {
+    orc_softmax(B, K, V, ld, dtype, p_logits, T, p_max, p_sum, p_arg, NULL);
+    orc_softmax(B, K, V, ld, dtype, q_logits, T, q_max, q_sum, q_arg, NULL);
+    orc_build_cache(B, K, V, ld, dtype, q_logits, T, F, Bf, cache_ids, cache_mass);
+    orc_saguaro(B, K, V, ld, dtype, q_logits, T, F, Bf, cache_ids, cache_mass, C, Z, NULL);
+    for (int b = 0; b < B; ++b) { err[b] = 0; exc[b] = 0; }
+    orc_verify(B, K, V, ld, dtype, p_logits, q_logits, T, draft, p_max, p_sum, p_arg, q_max, q_sum,
+               q_arg, F, Bf, cache_ids, Z, C, seed, round, accept_len, accept_prob, err, exc);
+    orc_residual_sample(B, K, V, ld, dtype, p_logits, q_logits, T, p_max, p_sum, p_arg, q_max, q_sum,
+                        q_arg, F, Bf, cache_ids, Z, C, accept_len, seed, round, bonus, resid_mass,
+                        NULL, err, exc);
+    orc_cache_lookup(B, K, V, F, Bf, cache_ids, accept_len, bonus, fallback_uniform, seed, round,
+                     hit, slot, fallback_tokens, err);
+}

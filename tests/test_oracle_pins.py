@@ -1,0 +1,367 @@
+"""Pins of the fp64 oracle against things other than itself: numpy library
+routines, an independent generator implementation, brute force and closed forms.
+CPU only."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_logits(rng, B, K, V, scale=2.0, dtype="f32"):
+    z = (rng.standard_normal((B, K + 1, V)) * scale).astype(np.float32)
+    if dtype == "bf16":
+        # round-to-nearest-even to bf16 bits (the oracle widens them exactly)
+        u = z.view(np.uint32).astype(np.uint64)
+        rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        return rounded
+    return z
+
+
+def _widen(z):
+    if z.dtype == np.uint16:
+        return (z.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return z.astype(np.float64)
+
+
+# --------------------------------------------------------------------------- RNG
+def test_philox_matches_numpy(orc):
+    """P11: Philox4x64-10 equals numpy's independent implementation (numpy's
+    generator increments its counter before producing a block)."""
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        ctr = rng.integers(1, 2**63, size=4, dtype=np.uint64)
+        key = rng.integers(0, 2**63, size=2, dtype=np.uint64)
+        mine = orc.philox4x64_10(ctr, key)
+        bg = np.random.Philox(key=key, counter=ctr - np.array([1, 0, 0, 0], dtype=np.uint64))
+        assert np.array_equal(mine, bg.random_raw(4))
+
+
+def test_uniform_definition_and_ks(orc):
+    """P11: u = (first word >> 40) * 2^-24 from numpy's Philox; uniform on [0,1)."""
+    seed, rnd = 0x55D3, 17
+    us = []
+    for b in range(40):
+        for i in range(50):
+            u = orc.uniform(seed, rnd, orc.PURPOSE_ACCEPT, b, i)
+            bg = np.random.Philox(key=np.array([seed, orc.PURPOSE_ACCEPT], dtype=np.uint64),
+                                  counter=np.array([rnd - 1, b, i, 0], dtype=np.uint64))
+            w0 = int(bg.random_raw(1)[0])
+            assert u == (w0 >> 40) / 2.0**24
+            assert orc.uniform_u32(seed, rnd, orc.PURPOSE_ACCEPT, b, i) == w0 >> 32
+            us.append(u)
+    from scipy import stats
+    assert stats.kstest(us, "uniform").pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------- fan-out
+def _lr_bruteforce(K, Bf, r):
+    """Largest-remainder apportionment characterised independently: among all
+    floor/ceil roundings of f_k = Bf r^k / sum r^j that sum to Bf, the one with the
+    smallest L1 distance to f; among equals the one rounding lower k up first."""
+    w = np.array([r**k for k in range(K + 1)])
+    f = Bf * w / w.sum()
+    fl = np.floor(f).astype(int)
+    best = None
+    for ups in itertools.product([0, 1], repeat=K + 1):
+        F = fl + np.array(ups)
+        if F.sum() != Bf:
+            continue
+        cost = np.abs(F - f).sum()
+        key = (round(cost, 12), tuple(-u for u in ups))
+        if best is None or key < best[0]:
+            best = (key, F)
+    return best[1], f
+
+
+@pytest.mark.parametrize("K,Bf,r", [(4, 16, 0.7), (5, 32, 0.6), (8, 64, 0.7), (6, 96, 0.8),
+                                    (4, 32, 0.5), (3, 10, 1.0), (1, 0, 0.3), (7, 5, 0.9), (2, 7, 0.25)])
+def test_fanout_largest_remainder(orc, K, Bf, r):
+    """P6: sum F = Bf, F non-increasing in k, |F_k - f_k| < 1, and F is the L1-closest
+    integer rounding of the geometric shares (brute force)."""
+    F, gap = orc.fanout(K, Bf, r)
+    ref, f = _lr_bruteforce(K, Bf, r)
+    assert F.sum() == Bf
+    assert np.all(np.diff(F) <= 0)
+    assert np.all(np.abs(F - f) < 1)
+    if gap > 1e-9:
+        assert np.array_equal(F, ref)
+
+
+def test_fanout_golden(orc):
+    """P6: the fan-out of the five workloads, stored by tests/golden/make_golden.py."""
+    with open(os.path.join(GOLDEN, "fanout_workloads.json")) as fh:
+        g = json.load(fh)
+    for row in g["rows"]:
+        F, _ = orc.fanout(row["K"], row["Bf"], row["r"])
+        assert F.tolist() == row["F"]
+
+
+# --------------------------------------------------------------------------- softmax
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.0, 0.5, 1.0, 1.7])
+def test_softmax_matches_numpy(orc, dtype, T):
+    """P1 / P10: softmax equals numpy exp((z - max)/T) / sum; greedy equals np.argmax
+    (first maximum); sum p = 1."""
+    rng = np.random.default_rng(2)
+    z = _rand_logits(rng, 3, 2, 257, 3.0, dtype)
+    m, s, a, probs = orc.softmax(z, T, want_probs=True)
+    zz = _widen(z)
+    ref_arg = np.argmax(zz, axis=-1)
+    assert np.array_equal(a, ref_arg)
+    assert np.array_equal(m, zz.max(-1))
+    if T > 0:
+        e = np.exp((zz - zz.max(-1, keepdims=True)) / T)
+        ref = e / e.sum(-1, keepdims=True)
+        np.testing.assert_allclose(probs, ref, rtol=0, atol=1e-15)
+    else:
+        ref = np.zeros_like(zz)
+        np.put_along_axis(ref, ref_arg[..., None], 1.0, axis=-1)
+        assert np.array_equal(probs, ref)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, atol=1e-13)
+
+
+def test_softmax_ties_and_padded_rows(orc):
+    """Greedy ties go to the lower id; a row stride larger than V is honoured."""
+    z = np.zeros((1, 2, 16), dtype=np.float32)
+    z[0, 0, [3, 9]] = 5.0
+    z[0, 1, :] = -1.0
+    _, _, a, _ = orc.softmax(z, 0.0)
+    assert a.tolist() == [[3, 0]]
+    big = np.full((2, 3, 40), np.nan, dtype=np.float32)
+    rng = np.random.default_rng(3)
+    big[:, :, :33] = rng.standard_normal((2, 3, 33))
+    view = big[:, :, :33]
+    m1, s1, a1, _ = orc.softmax(view, 1.0)
+    m2, s2, a2, _ = orc.softmax(np.ascontiguousarray(view), 1.0)
+    assert np.array_equal(a1, a2) and np.array_equal(m1, m2) and np.array_equal(s1, s2)
+
+
+# --------------------------------------------------------------------------- cache
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topF_matches_lexsort(orc, dtype):
+    """P8: S_k = the first F_k ids of np.lexsort((ids, -z)); M_k = sum of q over them."""
+    rng = np.random.default_rng(4)
+    K, V = 4, 300
+    z = _rand_logits(rng, 3, K, V, 2.0, dtype)
+    if dtype == "bf16":
+        # heavy bf16 ties: quantise further so many equal values appear
+        z = (z & 0xFFE0).astype(np.uint16)
+    F, _ = orc.fanout(K, 40, 0.6)
+    T = 0.9
+    ids, mass = orc.build_cache(z, T, F)
+    zz = _widen(z)
+    _, _, _, probs = orc.softmax(z, T, want_probs=True)
+    O = np.concatenate([[0], np.cumsum(F)])
+    for b in range(3):
+        for k in range(K + 1):
+            order = np.lexsort((np.arange(V), -zz[b, k]))
+            ref = order[:F[k]]
+            assert ids[b, O[k]:O[k + 1]].tolist() == ref.tolist()
+            np.testing.assert_allclose(mass[b, k], probs[b, k, ref].sum(), atol=1e-14)
+
+
+def test_topF_greedy_mass(orc):
+    """At T = 0 the cached mass is 1 when F_k >= 1 (the argmax is cached first) and 0
+    when F_k = 0."""
+    rng = np.random.default_rng(5)
+    z = _rand_logits(rng, 2, 3, 50)
+    F = np.array([3, 0, 2, 1], dtype=np.int32)
+    ids, mass = orc.build_cache(z, 0.0, F)
+    assert mass.tolist() == [[1.0, 0.0, 1.0, 1.0]] * 2
+    assert ids[:, 0].tolist() == np.argmax(z[:, 0], -1).tolist()
+
+
+# --------------------------------------------------------------------------- Saguaro
+@pytest.mark.parametrize("C", [0.2, 0.5, 1.0])
+def test_saguaro_invariants(orc, C):
+    """P7: sum q' = 1; q'/q is C/Z on S_k and 1/Z elsewhere; C = 1 gives q' = q."""
+    rng = np.random.default_rng(6)
+    K, V, T = 3, 120, 1.0
+    z = _rand_logits(rng, 2, K, V)
+    F, _ = orc.fanout(K, 20, 0.7)
+    ids, mass = orc.build_cache(z, T, F)
+    Z, qp = orc.saguaro(z, T, F, ids, mass, C, want_qprime=True)
+    _, _, _, q = orc.softmax(z, T, want_probs=True)
+    np.testing.assert_allclose(qp.sum(-1), 1.0, atol=1e-13)
+    O = np.concatenate([[0], np.cumsum(F)])
+    for b in range(2):
+        for k in range(K + 1):
+            S = set(ids[b, O[k]:O[k + 1]].tolist())
+            ratio = qp[b, k] / q[b, k]
+            for x in range(V):
+                want = (C if x in S else 1.0) / Z[b, k]
+                assert abs(ratio[x] - want) < 1e-12 * max(1.0, want)
+            np.testing.assert_allclose(Z[b, k], 1 - (1 - C) * q[b, k, list(S)].sum(), atol=1e-14)
+    if C == 1.0:
+        np.testing.assert_allclose(qp, q, atol=1e-15)
+
+
+def test_saguaro_empty_cache_is_identity(orc):
+    """F_k = 0 leaves q'_k = q_k."""
+    rng = np.random.default_rng(7)
+    z = _rand_logits(rng, 1, 2, 40)
+    F = np.array([0, 0, 0], dtype=np.int32)
+    ids, mass = orc.build_cache(z, 1.0, F)
+    Z, qp = orc.saguaro(z, 1.0, F, ids, mass, 0.3, want_qprime=True)
+    _, _, _, q = orc.softmax(z, 1.0, want_probs=True)
+    assert np.all(Z == 1.0)
+    np.testing.assert_allclose(qp, q, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- residual / sampler
+def _setup(orc, rng, B, K, V, T, C, Bf=12, r=0.7, scale=2.0, corr_noise=0.8):
+    zq = (rng.standard_normal((B, K + 1, V)) * scale).astype(np.float32)
+    zp = (zq + rng.standard_normal((B, K + 1, V)) * corr_noise).astype(np.float32)
+    F, _ = orc.fanout(K, Bf, r)
+    ids, mass = orc.build_cache(zq, T, F)
+    Z, qp = orc.saguaro(zq, T, F, ids, mass, C, want_qprime=True)
+    ps = orc.softmax(zp, T, want_probs=True)
+    qs = orc.softmax(zq, T, want_probs=True)
+    return zp, zq, F, ids, mass, Z, qp, ps, qs
+
+
+@pytest.mark.parametrize("T", [0.8, 1.0])
+def test_residual_invariants_and_searchsorted(orc, T):
+    """P5 / P9: w >= 0 and sums to Z_r; after a rejection w(d_k) = 0 and bonus != d_k;
+    the bonus equals np.searchsorted(cumsum(w), u * Z_r, 'right')."""
+    rng = np.random.default_rng(8)
+    B, K, V, C = 64, 3, 50, 0.4
+    zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, T, C)
+    seed, rnd = 99, 3
+    d, _ = orc.draft_sample(zq, T, F, ids, Z, C, seed, rnd)
+    acc, aprob, err, exc = orc.verify(zp, zq, T, d, ps, qs, F, ids, Z, C, seed, rnd)
+    assert np.all(err == 0)
+    bonus, zr, resid, err2, exc2 = orc.residual_sample(zp, zq, T, ps, qs, F, ids, Z, C, acc, seed, rnd,
+                                                       want_resid=True)
+    p = ps[3]
+    n_rej = 0
+    for b in range(B):
+        k = acc[b]
+        w = resid[b]
+        assert np.all(w >= 0)
+        np.testing.assert_allclose(w.sum(), zr[b], rtol=1e-12)
+        if k < K:
+            n_rej += 1
+            ref = np.maximum(p[b, k] - qp[b, k], 0.0)
+            np.testing.assert_allclose(w, ref, atol=1e-15)
+            assert w[d[b, k]] == 0.0
+            assert bonus[b] != d[b, k]
+        else:
+            np.testing.assert_allclose(w, p[b, K], atol=1e-15)
+        u = orc.uniform(seed, rnd, orc.PURPOSE_BONUS, b, k)
+        j = int(np.searchsorted(np.cumsum(w), u * zr[b], side="right"))
+        if not (exc2[b] & orc.E2_CDF_TIE):
+            assert bonus[b] == j
+    assert n_rej > 10
+
+
+def test_residual_greedy_and_bad_len(orc):
+    """At T = 0 the bonus is argmax p_k; an accepted length outside [0, K] is an
+    error with bonus -1."""
+    rng = np.random.default_rng(9)
+    B, K, V = 5, 2, 30
+    zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, 0.0, 0.5)
+    acc = np.array([0, 1, 2, 3, -1], dtype=np.int32)
+    bonus, zr, _, err, _ = orc.residual_sample(zp, zq, 0.0, ps, qs, F, ids, Z, 0.5, acc, 1, 1)
+    for b in range(3):
+        assert bonus[b] == np.argmax(zp[b, acc[b]])
+    assert bonus[3] == -1 and bonus[4] == -1
+    assert err[3] == orc.ERR_LEN_RANGE and err[4] == orc.ERR_LEN_RANGE
+
+
+def test_draft_sampler_searchsorted(orc):
+    """P9 for the draft sampler: d_i = searchsorted(cumsum(q'_i), u, 'right')."""
+    rng = np.random.default_rng(10)
+    B, K, V, T, C = 20, 3, 40, 1.0, 0.5
+    zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, T, C)
+    d, flags = orc.draft_sample(zq, T, F, ids, Z, C, 5, 6)
+    for b in range(B):
+        for i in range(K):
+            u = orc.uniform(5, 6, orc.PURPOSE_DRAFT, b, i)
+            c = np.cumsum(qp[b, i])
+            j = int(np.searchsorted(c, u * c[-1], side="right"))
+            if not flags[b, i]:
+                assert d[b, i] == j
+    dg, _ = orc.draft_sample(zq, 0.0, F, ids, Z, C, 5, 6)
+    assert np.array_equal(dg, np.argmax(zq[:, :K], -1))
+
+
+# --------------------------------------------------------------------------- verify
+def test_verify_bruteforce(orc):
+    """Accepted length is the first i with u_i >= p_i(d_i)/q'_i(d_i) (python loop over
+    the oracle's own probabilities and numpy's Philox words); accept_prob =
+    min(1, ratio); bad tokens are errors that reject."""
+    rng = np.random.default_rng(11)
+    B, K, V, T, C, seed, rnd = 40, 4, 25, 1.0, 0.5, 7, 11
+    zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, T, C)
+    d = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    d[3, 2] = V + 5
+    d[4, 0] = -1
+    acc, aprob, err, exc = orc.verify(zp, zq, T, d, ps, qs, F, ids, Z, C, seed, rnd)
+    p = ps[3]
+    for b in range(B):
+        k = K
+        for i in range(K):
+            x = d[b, i]
+            if not (0 <= x < V):
+                ratio, ok = 0.0, False
+            else:
+                ratio, ok = p[b, i, x] / qp[b, i, x], True
+            bg = np.random.Philox(key=np.array([seed, 0], dtype=np.uint64),
+                                  counter=np.array([rnd - 1, b, i, 0], dtype=np.uint64))
+            u = (int(bg.random_raw(1)[0]) >> 40) / 2.0**24
+            np.testing.assert_allclose(aprob[b, i], min(1.0, ratio), rtol=1e-12)
+            if k == K and not (ok and u < ratio):
+                k = i
+        if not (exc[b] & orc.E1_ACCEPT_TIE):
+            assert acc[b] == k
+    assert err[3] == orc.ERR_TOKEN_RANGE and err[4] == orc.ERR_TOKEN_RANGE
+    assert acc[4] == 0
+
+
+def test_verify_greedy(orc):
+    """T = 0: accept iff d_i = argmax p_i."""
+    rng = np.random.default_rng(12)
+    B, K, V = 30, 4, 6
+    zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, 0.0, 0.5)
+    ap = np.argmax(zp, -1)
+    d = np.where(rng.random((B, K)) < 0.7, ap[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    acc, aprob, err, _ = orc.verify(zp, zq, 0.0, d, ps, qs, F, ids, Z, 0.5, 1, 1)
+    for b in range(B):
+        k = next((i for i in range(K) if d[b, i] != ap[b, i]), K)
+        assert acc[b] == k
+        assert aprob[b].tolist() == [1.0 if d[b, i] == ap[b, i] else 0.0 for i in range(K)]
+
+
+# --------------------------------------------------------------------------- lookup
+def test_lookup_bruteforce(orc):
+    """P12: hit = bonus in S_k by set membership, slot = O_k + position; uniform
+    fallback = (U32 * V) >> 32 on a miss, -1 otherwise."""
+    rng = np.random.default_rng(13)
+    B, K, V = 200, 3, 20
+    F = np.array([5, 3, 2, 0], dtype=np.int32)
+    Bf = int(F.sum())
+    ids = np.stack([rng.permutation(V)[:Bf] for _ in range(B)]).astype(np.int32)
+    acc = rng.integers(0, K + 1, B).astype(np.int32)
+    bonus = rng.integers(0, V, B).astype(np.int32)
+    for mode in (0, 1):
+        hit, slot, fb, err = orc.cache_lookup(K, V, F, ids, acc, bonus, mode, 3, 4)
+        O = np.concatenate([[0], np.cumsum(F)])
+        for b in range(B):
+            S = ids[b, O[acc[b]]:O[acc[b] + 1]].tolist()
+            h = bonus[b] in S
+            assert hit[b] == h
+            assert slot[b] == (O[acc[b]] + S.index(bonus[b]) if h else -1)
+            for j in range(K):
+                if h or not mode:
+                    assert fb[b, j] == -1
+                else:
+                    u32 = orc.uniform_u32(3, 4, orc.PURPOSE_FALLBACK, b, j)
+                    assert fb[b, j] == (u32 * V) >> 32
+                    assert 0 <= fb[b, j] < V
+        assert np.all(err == 0)
+    assert 0 < hit.sum() < B
