@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the fused verify-and-pre-speculate round (SSD / Saguaro) on one
+MI355X: rounds per second and achieved HBM bandwidth of the vocabulary pass.
+
+One step is one whole round over one batch: softmax statistics of both models,
+top-F speculation cache with geometric fan-out, Saguaro reweighting, lossless
+verification, residual bonus sampling and cache lookup (two HIP kernels).  Inputs
+(seeded synthetic logits, draft tokens from the library's own Saguaro sampler) are
+resident in HBM before timing; the timed loop rotates over distinct logit buffers
+totalling more than the 256 MB last-level cache so that rows come from HBM.
+
+Prints one JSON line on stdout.  With --gpus above 1 it exits: this build measures
+one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c3", help="c1..c5 (default: the headline B=64 K=8 V=128256 bf16)")
+    ap.add_argument("--buffers", type=int, default=0, help="distinct logit buffers to rotate (0: >= 1 GB)")
+    ap.add_argument("--C", type=float, default=None)
+    ap.add_argument("--target-sigma", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain device copy of 1 GiB (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the round of this library runs on a single MI355X "
+              "(batch sharding across GPUs is described in DESIGN.md); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lossless_rejection_sampling_ssd_amd as ssd
+    from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_logits
+
+    w = WORKLOADS[args.workload]
+    T = w.temps[-1]
+    C = args.C if args.C is not None else w.Cs[len(w.Cs) // 2]
+    sig = args.target_sigma
+    esize = 2 if w.dtype == "bf16" else 4
+    F = ssd.ssd_fanout(w.K, w.Bf, w.r)
+    B, K, V = w.B, w.K, w.V
+    K1 = K + 1
+    pass1_bytes = 2 * B * K1 * V * esize
+    nbuf = args.buffers or max(1, -(-(1 << 30) // pass1_bytes))
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    # ---- inputs resident in HBM (untimed): logits and draft tokens sampled from q'
+    bufs = []
+    ws = ssd.Workspace()
+    for i in range(nbuf):
+        zq, zp = make_logits(w, buffer=i, target_sigma=sig, device=dev)
+        shape = ssd.shape_of(zq, T)
+        R = B * K1
+        qm = torch.zeros(R, device=dev)
+        qs = torch.zeros(R, dtype=torch.float64, device=dev)
+        qa = torch.zeros(R, dtype=torch.int32, device=dev)
+        ssd.ssd_softmax(shape, zq, qm, qs, qa, ws=ws)
+        ids = torch.zeros((B, w.Bf), dtype=torch.int32, device=dev)
+        mass = torch.zeros(R, dtype=torch.float64, device=dev)
+        ssd.ssd_build_cache(shape, zq, qm, qs, F, ids, mass, ws=ws)
+        Z = torch.zeros(R, dtype=torch.float64, device=dev)
+        d = torch.zeros((B, K), dtype=torch.int32, device=dev)
+        ssd.ssd_saguaro_reweight(shape, mass, C, Z, zq, qm, qs, qa, F, ids, None, w.seed, 10_000 + i, d, ws=ws)
+        bufs.append((zp, zq, d))
+    torch.cuda.synchronize()
+    shape = ssd.shape_of(bufs[0][0], T)
+    fallback = ssd.SSD_FALLBACK_UNIFORM if w.fallback_uniform else ssd.SSD_FALLBACK_NONE
+    outb = ssd.RoundBuffers(B, K, w.Bf, with_stats=False)
+
+    def step(i, events=None):
+        zp, zq, d = bufs[i % nbuf]
+        ssd.ssd_round(shape, zp, zq, d, F, C, w.seed, i, fallback, outb.out, events=events, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K rounds; HIP events around each round's vocabulary pass
+    n = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:  # create the underlying HIP events before the library records them
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    evs = [ssd.ssd_round_events(a.cuda_event, b.cuda_event, None, None) for a, b in ev]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(n):
+        step(args.warmup + i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    pass1_ms = [a.elapsed_time(b) for a, b in ev]
+    pass1_avg_ms = float(np.mean(pass1_ms))
+    ms_per_step = total_ms / n
+    rounds_per_s = 1000.0 / ms_per_step
+
+    # ---- algorithmic bytes of the same rounds (deterministic replay, untimed)
+    ks, hits = [], []
+    for i in range(min(n, 64)):
+        step(args.warmup + i)
+        ks.append(outb["accept_len"].cpu().numpy().copy())
+        hits.append(outb["hit"].cpu().numpy().copy())
+    ks = np.stack(ks)
+    hits = np.stack(hits)
+    rows2 = np.where(ks < K, 2, 1).sum(axis=1).mean() if T > 0 else 0.0
+    pass2_bytes = rows2 * V * esize
+    round_bytes = pass1_bytes + pass2_bytes
+    round_gbps = round_bytes / (ms_per_step * 1e-3) / 1e9
+    pass1_gbps = pass1_bytes / (pass1_avg_ms * 1e-3) / 1e9
+
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy-calib: 3 x device copy of %d bytes" % (src.numel() * 4))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, bufs[0], T, C, F, args.cpu_seconds)
+
+    label = "%s: B=%d K=%d V=%d %s logits, T=%g, B_f=%d, r=%g, C=%g" % (
+        args.workload, B, K, V, w.dtype, T, w.Bf, w.r, C)
+    rec = {
+        "metric": "verify+cache rounds/sec and achieved HBM GB/s (% of peak), B=64 V=128256 K=8",
+        "value": round(rounds_per_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": label,
+            "logits": w.dtype,
+            "fan_out": F,
+            "buffers": nbuf,
+            "round_bytes": int(round_bytes),
+            "round_GBps": round(round_gbps, 1),
+            "round_frac_of_peak": round(round_gbps / PEAK_HBM_GBPS, 4),
+            "pass1_us": round(pass1_avg_ms * 1e3, 2),
+            "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
+            "mean_accept_len": round(float(ks.mean()), 3),
+            "hit_rate": round(float(hits.mean()), 4),
+            "wall_s": round(wall, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(pass1_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(pass1_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "kernel": "pass1_kernel (vocabulary pass over all 2*B*(K+1) rows)",
+            "bytes_per_launch": int(pass1_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, buf, T, C, F, seconds):
+    """The fp64 oracle, as it stands, on whole rounds of the same workload (first
+    logit buffer), on this host's cores, for about `seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    from lossless_rejection_sampling_ssd_amd.workloads import to_oracle_array
+
+    zp, zq, _ = buf
+    zp_np, zq_np = to_oracle_array(zp.cpu()), to_oracle_array(zq.cpu())
+    Fa = np.asarray(F, np.int32)
+    ids, mass = oracle.build_cache(zq_np, T, Fa)
+    Z, _ = oracle.saguaro(zq_np, T, Fa, ids, mass, C)
+    draft, _ = oracle.draft_sample(zq_np, T, Fa, ids, Z, C, w.seed, 0)
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.round_(zp_np, zq_np, T, Fa, C, draft, w.seed, rounds, w.fallback_uniform)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or rounds >= 50:
+            break
+    log("cpu baseline: %d oracle rounds in %.2f s" % (rounds, el))
+    return {"value": round(rounds / el, 4), "unit": "rounds/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d whole rounds (B=%d sequences each) of the timed workload's first logit buffer" % (
+                rounds, w.B)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) verify-and-pre-speculate round of
+ * Speculative Speculative Decoding (SSD) with the Saguaro algorithm.
+ *
+ * The round runs on logits the draft and target models have already produced.
+ * Sources (two summaries of the paper "Speculative Speculative Decoding" by Kumar,
+ * Dao and May):
+ *   [zh] gist.science/zh/paper/2603.03251, technical part: section 1 (lossless SD),
+ *        section 2 Methodology (basic flow; Challenge 1 geometric fan-out; Challenge 2
+ *        Saguaro sampling; Challenge 3 fallback), section 4 (temperature, batch size);
+ *   [nl] gist.science/nl/paper/2603.03251, technical part: section 2 (Kernprincipes),
+ *        section 3 A (geometric fan-out), 3 B (Saguaro sampling), 3 C (fallback).
+ * The pages name the parts and assert that the round is lossless; the formulas are
+ * the standard lossless speculative-sampling construction, stated at each call.
+ *
+ * Conventions for every call
+ *  - Logits are [B, K+1, V] row-major with row r = b*(K+1) + i and row stride `ld`
+ *    elements (ld >= V).  Row i < K is draft position i; row K is the position after
+ *    the last draft token.  fp32 or bf16 (bf16 is widened to fp32 in registers).
+ *    Logits must be finite or -inf; a row needs at least one finite value.
+ *  - Every pointer except those named *_host is device memory owned by the caller.
+ *    The library allocates nothing, keeps no state between calls and never
+ *    synchronises: every call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *    is the default stream) and returns.  Outputs must not alias inputs.
+ *  - Argument errors are found on the host before any launch and return
+ *    SSD_ERR_ARG with no side effect.  Shapes the kernels do not support return
+ *    SSD_ERR_UNSUPPORTED; launch failures SSD_ERR_HIP (text in ssd_last_error()).
+ *  - Data-dependent errors never trap: they OR bits into the optional per-sequence
+ *    `dev_err[B]` (caller zeroes it): SSD_DEVERR_*.
+ *  - `ws` is a workspace of at least ssd_workspace_bytes() bytes, 256-byte aligned,
+ *    ZERO-FILLED BY THE CALLER BEFORE ITS FIRST USE.  Each call leaves the counters it
+ *    uses back at zero when it completes, so one workspace serves any number of calls
+ *    on one stream.  Two calls that overlap in time must not share a workspace.
+ *  - Uniforms are counter-based: Philox4x64-10 (Salmon et al., SC'11) with key
+ *    (seed, purpose) and counter (round, b, i, 0); u = (word0 >> 40) * 2^-24 and
+ *    u32 = word0 >> 32.  Purposes: SSD_PURPOSE_*.  Results are reproducible from
+ *    (seed, round).
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_ARG = 1,
+    SSD_ERR_UNSUPPORTED = 2,
+    SSD_ERR_HIP = 3,
+    SSD_ERR_WORKSPACE = 4
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum { SSD_FALLBACK_NONE = 0, SSD_FALLBACK_UNIFORM = 1 } ssd_fallback;
+
+enum { SSD_PURPOSE_ACCEPT = 0, SSD_PURPOSE_BONUS = 1, SSD_PURPOSE_DRAFT = 2, SSD_PURPOSE_FALLBACK = 3 };
+
+enum {
+    SSD_DEVERR_TOKEN_RANGE = 1,  /* a draft token outside [0, V): treated as rejected */
+    SSD_DEVERR_QPRIME_ZERO = 2,  /* q'(d) == 0 in fp32 for a tested draft token: rejected */
+    SSD_DEVERR_LEN_RANGE = 4     /* accept_len outside [0, K]: bonus -1, miss */
+};
+
+/* Limits of this build. */
+enum { SSD_MAX_K = 16, SSD_MAX_F = 64 };
+
+typedef struct {
+    int32_t B;      /* sequences, >= 1 */
+    int32_t K;      /* draft tokens per sequence, 1..SSD_MAX_K */
+    int32_t V;      /* vocabulary, >= 2 */
+    int64_t ld;     /* row stride in elements, >= V */
+    int32_t dtype;  /* ssd_dtype */
+    float T;        /* temperature >= 0; 0 selects the greedy (argmax) limit */
+} ssd_shape;
+
+typedef struct {
+    uint64_t seed;
+    uint64_t round;
+} ssd_rng;
+
+/* ssd_fanout -- geometric fan-out ([zh] section 2 Challenge 1; [nl] section 3 A):
+ * splits the cache budget Bf over acceptance lengths k = 0..K in proportion to
+ * r^k, integer shares by largest remainder (ties to the lower k), so that
+ * sum F = Bf.  Host only; F_host has K+1 entries.  0 < r <= 1, Bf >= 0. */
+ssd_status ssd_fanout(int32_t K, int32_t Bf, double r, int32_t* F_host);
+
+/* Bytes of workspace the calls below need for this shape and budget. */
+size_t ssd_workspace_bytes(const ssd_shape* shape, int32_t Bf);
+
+/* ssd_softmax -- temperature softmax of every row ([zh] sections 2 and 4 use
+ * temperature as an axis of the method):  m = max_x z(x),
+ * s = sum_x exp((z(x) - m) / T), p(x) = exp((z(x) - m) / T) / s.  At T = 0:
+ * s = 1 and p is one-hot on argmax (lowest id among the maxima).
+ * Outputs [B*(K+1)]: row_max (fp32, an input value), row_sum (fp64); row_argmax
+ * (int32, nullable) is the lowest id of the maximum; probs (nullable, [B, K+1, V]
+ * fp32, dense) receives p. */
+ssd_status ssd_softmax(const ssd_shape* shape, const void* logits, float* row_max, double* row_sum,
+                       int32_t* row_argmax, float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* ssd_build_cache -- the speculation cache keys ([zh] section 2 flow steps 2-3 and
+ * Challenge 1; [nl] section 2 and 3 A).  For each sequence b and acceptance length
+ * k = 0..K the cache holds F_k candidate bonus tokens: the F_k ids with the largest
+ * draft logit z_q[b, k, .], ties to the lower id, stored in that order at
+ * cache_ids[b, O_k + j] with O_k = F_0 + ... + F_{k-1} (cache_ids is [B, Bf]).
+ * cache_mass[b*(K+1)+k] (fp64) = M_k = sum over those ids of q_k(x), with q from the
+ * given draft row statistics (q_max, q_sum of ssd_softmax).  F_host [K+1] must
+ * satisfy sum F = Bf and 0 <= F_k <= min(V, SSD_MAX_F). */
+ssd_status ssd_build_cache(const ssd_shape* shape, const void* q_logits, const float* q_max,
+                           const double* q_sum, const int32_t* F_host, int32_t Bf, int32_t* cache_ids,
+                           double* cache_mass, void* ws, size_t ws_bytes, void* stream);
+
+/* ssd_saguaro_reweight -- Saguaro sampling ([zh] section 2 Challenge 2; [nl] section
+ * 3 B): the draft law is scaled by C in (0, 1] on the cached tokens S_k and
+ * renormalised:  Z_k = 1 - (1 - C) M_k,  q'_k(x) = q_k(x) (C if x in S_k else 1) / Z_k.
+ * Z [B*(K+1)] (fp64) is always written.  The rest is optional (pass NULL to skip):
+ *  - q_prime [B, K+1, V] fp32 dense receives q';
+ *  - draft [B, K] receives draft tokens sampled from q'_i by inverse CDF with
+ *    u = U(seed, round, b, i, DRAFT) (the smallest id whose running sum of q'_i
+ *    exceeds u times the total), or argmax z_q at T = 0.
+ * Both optional outputs need q_logits, q_max, q_sum, q_argmax (T = 0), F_host, Bf,
+ * cache_ids; draft also needs ws. */
+ssd_status ssd_saguaro_reweight(const ssd_shape* shape, const double* cache_mass, float C, double* Z,
+                                const void* q_logits, const float* q_max, const double* q_sum,
+                                const int32_t* q_argmax, const int32_t* F_host, int32_t Bf,
+                                const int32_t* cache_ids, float* q_prime, ssd_rng rng, int32_t* draft,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ssd_verify -- lossless verification ([zh] section 1 and section 2 flow steps 2 and
+ * 4; [nl] section 2): for i = 0..K-1 in order, ratio_i = p_i(d_i) / q'_i(d_i) and
+ * draft token d_i is accepted iff U(seed, round, b, i, ACCEPT) < ratio_i; the
+ * accepted length k is the first rejected position, or K.  At T = 0, d_i is
+ * accepted iff d_i = argmax p_i (p_argmax required).  accept_len [B] int32;
+ * accept_prob (nullable [B, K] fp32) = min(1, ratio_i) for every i. */
+ssd_status ssd_verify(const ssd_shape* shape, const void* p_logits, const void* q_logits,
+                      const int32_t* draft, const float* p_max, const double* p_sum,
+                      const int32_t* p_argmax, const float* q_max, const double* q_sum,
+                      const int32_t* F_host, int32_t Bf, const int32_t* cache_ids, const double* Z,
+                      float C, ssd_rng rng, int32_t* accept_len, float* accept_prob, int32_t* dev_err,
+                      void* stream);
+
+/* ssd_residual_sample -- the bonus token ([zh] section 2 flow step 2 and Challenge 2:
+ * the bonus comes from the residual distribution; [nl] section 3 B).  With
+ * k = accept_len[b]:  k < K: w(x) = max(p_k(x) - q'_k(x), 0) (w = p_k if that sums to
+ * 0 in fp32);  k = K: w = p_K.  bonus[b] = the smallest id whose running sum of w
+ * exceeds u * sum(w), u = U(seed, round, b, k, BONUS).  At T = 0 the bonus is
+ * argmax p_k (p_argmax required).  resid_mass (nullable [B], fp64) receives sum(w).
+ * The running sums that locate the bonus are kept in fp64. */
+ssd_status ssd_residual_sample(const ssd_shape* shape, const void* p_logits, const void* q_logits,
+                               const float* p_max, const double* p_sum, const int32_t* p_argmax,
+                               const float* q_max, const double* q_sum, const int32_t* F_host,
+                               int32_t Bf, const int32_t* cache_ids, const double* Z, float C,
+                               const int32_t* accept_len, ssd_rng rng, int32_t* bonus,
+                               double* resid_mass, int32_t* dev_err, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ssd_cache_lookup -- cache hit on the verified outcome (k, bonus) ([zh] section 2
+ * flow step 4 and Challenge 3; [nl] section 2 and 3 C).  hit[b] = 1 iff bonus is
+ * one of the F_k cached ids of length k; slot[b] = O_k + its position, else -1.  On
+ * a miss with SSD_FALLBACK_UNIFORM the next draft is K uniform random tokens
+ * fallback_tokens[b, j] = (U32(seed, round, b, j, FALLBACK) * V) >> 32; every other
+ * fallback entry is -1. */
+ssd_status ssd_cache_lookup(int32_t B, int32_t K, int32_t V, const int32_t* F_host, int32_t Bf,
+                            const int32_t* cache_ids, const int32_t* accept_len, const int32_t* bonus,
+                            int32_t fallback, ssd_rng rng, uint8_t* hit, int32_t* slot,
+                            int32_t* fallback_tokens, int32_t* dev_err, void* stream);
+
+/* Outputs of the fused round.  Required: cache_ids [B, Bf], accept_len [B], bonus
+ * [B], hit [B], slot [B], fallback_tokens [B, K].  The rest are nullable. */
+typedef struct {
+    float* p_max;       /* [B*(K+1)] */
+    double* p_sum;
+    int32_t* p_argmax;
+    float* q_max;
+    double* q_sum;
+    int32_t* q_argmax;
+    int32_t* cache_ids;
+    double* cache_mass; /* [B*(K+1)] */
+    double* Z;          /* [B*(K+1)] */
+    int32_t* accept_len;
+    float* accept_prob; /* [B, K] */
+    int32_t* bonus;
+    double* resid_mass; /* [B] */
+    uint8_t* hit;
+    int32_t* slot;
+    int32_t* fallback_tokens;
+    int32_t* dev_err;   /* [B], OR-accumulated */
+} ssd_round_out;
+
+/* Optional HIP events (hipEvent_t, may be NULL) recorded around the two streaming
+ * passes of ssd_round: the vocabulary pass over every row of both models
+ * (softmax statistics, top-F cache, Saguaro and verification) and the bonus pass
+ * over the verified rows (residual sampling and lookup). */
+typedef struct {
+    void* pass1_start;
+    void* pass1_stop;
+    void* pass2_start;
+    void* pass2_stop;
+} ssd_round_events;
+
+/* ssd_round -- one whole verify-and-pre-speculate round in the method's order:
+ * softmax of both models, cache build, Saguaro reweight, verification, bonus and
+ * lookup, with the same arithmetic as the six separate calls (results are
+ * bit-identical to chaining them).  Two streaming kernels: one over all
+ * 2 B (K+1) rows, one over the <= 2 rows per sequence the bonus needs. */
+ssd_status ssd_round(const ssd_shape* shape, const void* p_logits, const void* q_logits,
+                     const int32_t* draft, const int32_t* F_host, int32_t Bf, float C, ssd_rng rng,
+                     int32_t fallback, const ssd_round_out* out, const ssd_round_events* events,
+                     void* ws, size_t ws_bytes, void* stream);
+
+const char* ssd_status_string(ssd_status s);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char* ssd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

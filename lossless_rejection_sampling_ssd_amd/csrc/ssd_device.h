@@ -1,0 +1,393 @@
+// ssd_device.h -- device helpers for the gfx950 kernels of the SSD / Saguaro round:
+// wave64 reductions, the Philox4x64-10 generator, order-preserving keys, bf16 / fp32
+// vector loads, a wave-level radix select and a wave-level bitonic sort.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kWave = 64;        // CDNA wavefront
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kVecPerLane = 8;   // 16-byte vectors each lane keeps in flight per tile
+constexpr int kMaxK = 16;
+constexpr int kMaxF = 64;
+constexpr int kCandCap = 128;    // top-F candidates one wave may stage in LDS
+
+template <int DT> struct ElemTraits;
+template <> struct ElemTraits<0> {  // fp32
+    static constexpr int kPerVec = 4;
+    static constexpr int kBytes = 4;
+};
+template <> struct ElemTraits<1> {  // bf16
+    static constexpr int kPerVec = 8;
+    static constexpr int kBytes = 2;
+};
+template <int DT> constexpr int kTile = kVecPerLane * kWave * ElemTraits<DT>::kPerVec;  // per wave
+template <int DT> constexpr int kChunk = kWavesPerBlock * kTile<DT>;                     // per block
+
+// ---------------------------------------------------------------------------- loads
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Loads the vector of elements [e0, e0 + kPerVec) of a row into x[], elements at or
+// past V set to -inf.  Vector path when the whole vector is in range and aligned.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_vec(const char* row, int64_t e0, int V, float* x) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    if (VEC && e0 + N <= V) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + e0 * ElemTraits<DT>::kBytes);
+        if (DT == 1) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[2 * q] = __uint_as_float(w[q] << 16);
+                x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+            }
+        } else {
+            x[0] = __uint_as_float(v.x);
+            x[1] = __uint_as_float(v.y);
+            x[2] = __uint_as_float(v.z);
+            x[3] = __uint_as_float(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const int64_t id = e0 + e;
+            if (id < V) {
+                if (DT == 1)
+                    x[e] = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[id]);
+                else
+                    x[e] = reinterpret_cast<const float*>(row)[id];
+            } else {
+                x[e] = -INFINITY;
+            }
+        }
+    }
+}
+
+// Raw 16-byte vector of elements [e0, e0 + kPerVec) of a row, elements at or past V
+// replaced by the -inf pattern; unpack_vec widens it to fp32.
+template <int DT, bool VEC>
+__device__ __forceinline__ u32x4 load_raw(const char* row, int64_t e0, int V) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    if (VEC && e0 + N <= V) return *reinterpret_cast<const u32x4*>(row + e0 * ElemTraits<DT>::kBytes);
+    u32x4 v;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const int64_t id = e0 + e;
+        if (id < V) {
+            if (DT == 1) {
+                const uint32_t h = reinterpret_cast<const uint16_t*>(row)[id];
+                w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (h << 16)) : ((w[e >> 1] & 0xFFFF0000u) | h);
+            } else {
+                w[e] = reinterpret_cast<const uint32_t*>(row)[id];
+            }
+        }
+    }
+    v.x = w[0];
+    v.y = w[1];
+    v.z = w[2];
+    v.w = w[3];
+    return v;
+}
+template <int DT>
+__device__ __forceinline__ void unpack_vec(u32x4 v, float* x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (DT == 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[2 * q] = __uint_as_float(w[q] << 16);
+            x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+    }
+}
+
+// The kVecPerLane raw vectors one lane owns in a wave tile starting at element t0
+// (vector j covers [t0 + (j*64 + lane)*kPerVec, +kPerVec)).  When the whole tile is in
+// range and aligned (a wave-uniform test) the loads are unconditional and issued
+// back to back; only a ragged or unaligned tile takes the guarded element path.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, int lane, u32x4 (&raw)[kVecPerLane]) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    constexpr int TILE = kVecPerLane * kWave * N;
+    if (VEC && t0 + TILE <= V) {
+        const u32x4* base = reinterpret_cast<const u32x4*>(row + t0 * ElemTraits<DT>::kBytes) + lane;
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) raw[j] = base[j * kWave];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) raw[j] = load_raw<DT, false>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
+    }
+}
+
+
+template <int DT>
+__device__ __forceinline__ float load_one(const char* row, int64_t id) {
+    if (DT == 1) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[id]);
+    return reinterpret_cast<const float*>(row)[id];
+}
+
+// ---------------------------------------------------------------------------- keys
+// Order-preserving map of a float to uint32 (larger float -> larger key), with -0
+// mapped like +0 so that equal values compare equal.  Finite and -inf inputs only.
+__device__ __forceinline__ uint32_t ord32(float v) {
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unord32(uint32_t k) {
+    uint32_t b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(b);
+}
+// 64-bit candidate key: larger value first, then lower id.  Never 0 for a real
+// element (ord32(-inf) > 0), so 0 marks an empty slot.
+__device__ __forceinline__ uint64_t cand_key(float v, uint32_t id) {
+    return ((uint64_t)ord32(v) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu); }
+__device__ __forceinline__ float key_val(uint64_t k) { return unord32((uint32_t)(k >> 32)); }
+
+// ---------------------------------------------------------------------------- wave ops
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v &= __shfl_xor(v, m, kWave);
+    return v;
+}
+__device__ __forceinline__ int wave_popc(bool p) { return __popcll(__ballot(p)); }
+// Number of lanes below this one with p set.
+__device__ __forceinline__ int lanes_below(bool p) {
+    const uint64_t m = __ballot(p);
+    return __popcll(m & ((1ull << lane_id()) - 1ull));
+}
+
+// (max value, lowest id) reduction.
+__device__ __forceinline__ void arg_merge(float& m, int& a, float m2, int a2) {
+    if (m2 > m || (m2 == m && a2 < a)) {
+        m = m2;
+        a = a2;
+    }
+}
+
+// ---------------------------------------------------------------------------- cross-block data
+// Blocks hand partial results to the last block of their group through memory that
+// may sit in another XCD's L2.  Published values are written and read with
+// agent-scope relaxed atomics (sc1 accesses, coherent across XCDs without the
+// whole-L2 write-back / invalidate an agent-scope fence costs); a writer waits for
+// its stores to complete before it bumps the group's counter.  Every group's
+// published region is padded to whole cache lines and read by one block only.
+template <typename T>
+__device__ __forceinline__ void publish(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T observe(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ unsigned arrive(unsigned* counter) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------- softmax terms
+// With c = log2(e)/T every term of a row is 2^{z c - o} for an integer-valued offset
+// o = rint(m c) taken from a maximum m, so the exponent is formed by one fma with a
+// single rounding and partial sums under different offsets merge exactly by
+// ldexp.  o(-inf) = 0 (such a partial has no mass).
+__device__ __forceinline__ float offset_of(float m, float c) { return m == -INFINITY ? 0.f : rintf(m * c); }
+__device__ __forceinline__ float term(float z, float c, float o) { return __builtin_amdgcn_exp2f(fmaf(z, c, -o)); }
+
+// Sum of 2^{z c - o(M)} for the union of two partials (m1, s1), (m2, s2) whose sums are
+// relative to o(m1), o(m2).
+__device__ __forceinline__ void merge_partial(float& m, double& s, float m2, double s2, float c) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) {
+        m = M;
+        s = 0.0;
+        return;
+    }
+    const float oM = offset_of(M, c);
+    const double a = (m == -INFINITY) ? 0.0 : ldexp(s, (int)(offset_of(m, c) - oM));
+    const double b = (m2 == -INFINITY) ? 0.0 : ldexp(s2, (int)(offset_of(m2, c) - oM));
+    s = a + b;
+    m = M;
+}
+
+// ---------------------------------------------------------------------------- Philox
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round two 64x64->128
+// products with the published multipliers, key bumped by the published Weyl
+// constants; returns the first output word.
+__device__ __forceinline__ uint64_t philox_word0(uint64_t seed, uint64_t round, uint32_t purpose,
+                                                 uint64_t b, uint64_t i) {
+    uint64_t c0 = round, c1 = b, c2 = i, c3 = 0;
+    uint64_t k0 = seed, k1 = purpose;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t lo0 = 0xD2E7470EE14C6C93ull * c0;
+        const uint64_t hi0 = __umul64hi(0xD2E7470EE14C6C93ull, c0);
+        const uint64_t lo1 = 0xCA5A826395121157ull * c2;
+        const uint64_t hi1 = __umul64hi(0xCA5A826395121157ull, c2);
+        const uint64_t n0 = hi1 ^ c1 ^ k0;
+        const uint64_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+    return c0;
+}
+// u in [0, 1) with 24 random bits, exact in fp32.
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t round, uint32_t purpose, uint64_t b,
+                                                uint64_t i) {
+    return (float)(uint32_t)(philox_word0(seed, round, purpose, b, i) >> 40) * (1.0f / 16777216.0f);
+}
+__device__ __forceinline__ uint32_t philox_u32(uint64_t seed, uint64_t round, uint32_t purpose, uint64_t b,
+                                               uint64_t i) {
+    return (uint32_t)(philox_word0(seed, round, purpose, b, i) >> 32);
+}
+
+// ---------------------------------------------------------------------------- select
+// The F-th largest of the distinct nonzero 64-bit keys held by a whole wave in
+// KREG register slots per lane (0 = empty slot), by a most-significant-bit-first
+// radix select that only tests bits where the keys differ.  Returns 0 when there
+// are at most F keys (every key is in).
+template <int KREG>
+__device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
+    int n = 0;
+    uint64_t orv = 0ull, andv = ~0ull;
+#pragma unroll
+    for (int s = 0; s < KREG; ++s) {
+        n += wave_popc(k[s] != 0ull);
+        if (k[s] != 0ull) {
+            orv |= k[s];
+            andv &= k[s];
+        }
+    }
+    if (n <= F) return 0ull;
+    orv = wave_or64(orv);
+    andv = wave_and64(andv);
+    uint64_t diff = orv ^ andv;
+    uint64_t T = andv & ~diff;
+    while (diff) {
+        const int bit = 63 - __clzll(diff);
+        diff &= ~(1ull << bit);
+        const uint64_t cand = T | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int s = 0; s < KREG; ++s) cnt += wave_popc(k[s] >= cand);
+        if (cnt >= F) T = cand;
+    }
+    return T;
+}
+
+// Same selection over n keys in LDS (zeros are ignored), read afresh per tested bit
+// so that no register array is needed.
+__device__ inline uint64_t wave_select_lds(const uint64_t* keys, int n, int F) {
+    const int lane = lane_id();
+    int cnt0 = 0;
+    uint64_t orv = 0ull, andv = ~0ull;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + lane;
+        const uint64_t k = j < n ? keys[j] : 0ull;
+        cnt0 += wave_popc(k != 0ull);
+        if (k != 0ull) {
+            orv |= k;
+            andv &= k;
+        }
+    }
+    if (cnt0 <= F) return 0ull;
+    orv = wave_or64(orv);
+    andv = wave_and64(andv);
+    uint64_t diff = orv ^ andv;
+    uint64_t T = andv & ~diff;
+    while (diff) {
+        const int bit = 63 - __clzll(diff);
+        diff &= ~(1ull << bit);
+        const uint64_t cand = T | (1ull << bit);
+        int cnt = 0;
+        for (int j0 = 0; j0 < n; j0 += kWave) {
+            const int j = j0 + lane;
+            cnt += wave_popc(j < n && keys[j] >= cand);
+        }
+        if (cnt >= F) T = cand;
+    }
+    return T;
+}
+
+// Same for one nonzero 32-bit key per lane (0 = no key).
+__device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
+    const int n = wave_popc(k != 0u);
+    if (n <= F) return 0u;
+    uint32_t orv = k, andv = k ? k : ~0u;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
+        andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
+    }
+    uint32_t diff = orv ^ andv;
+    uint32_t T = andv & ~diff;
+    while (diff) {
+        const int bit = 31 - __clz(diff);
+        diff &= ~(1u << bit);
+        const uint32_t cand = T | (1u << bit);
+        if (wave_popc(k >= cand) >= F) T = cand;
+    }
+    return T;
+}
+
+// Sorts one 64-bit key per lane in descending order across the wave (bitonic).
+__device__ inline uint64_t wave_sort_desc(uint64_t key) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t other = __shfl_xor(key, j, kWave);
+            const bool desc = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            const uint64_t hi = key > other ? key : other;
+            const uint64_t lo = key > other ? other : key;
+            key = (desc == lower) ? hi : lo;
+        }
+    }
+    return key;
+}
+
+}  // namespace ssd

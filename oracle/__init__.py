@@ -30,6 +30,8 @@ PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
 ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE = 1, 2, 4
 E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
 FANOUT_EPS = 1e-9
+# Half-width of the inverse-CDF near-tie band (E2) on the normalised CDF.
+CDF_TIE_EPS = 1e-8
 
 
 def build(force: bool = False) -> str:
@@ -52,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         i32, i64, u64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
         L.orc_philox4x64_10.argtypes = [P, P, P]
         L.orc_uniform.argtypes = [u64, u64, i32, i64, i64]
         L.orc_uniform.restype = dbl
@@ -62,14 +66,14 @@ def lib() -> ctypes.CDLL:
         L.orc_softmax.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, P, P, P]
         L.orc_build_cache.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P]
         L.orc_saguaro.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P, dbl, P, P]
-        L.orc_draft_sample.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P, dbl, u64, u64, P, P]
+        L.orc_draft_sample.argtypes = [i32, i32, i32, i64, i32, P, dbl, P, i32, P, P, dbl, u64, u64, i64, dbl, P, P, P]
         L.orc_verify.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, P, P, P, P, P, P, P, i32, P, P,
-                                 dbl, u64, u64, P, P, P, P]
+                                 dbl, u64, u64, i64, P, P, P, P]
         L.orc_residual_sample.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, P, P, P, P, P, P, i32, P,
-                                          P, dbl, P, u64, u64, P, P, P, P, P]
-        L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, P, P, P, P]
-        L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i32,
-                                P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+                                          P, dbl, P, u64, u64, i64, dbl, P, P, P, P, P, P]
+        L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, i64, P, P, P, P]
+        L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i64, dbl, i32,
+                                P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -100,6 +104,10 @@ def _base(z):
 
 
 # ---------------------------------------------------------------------------
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
 def philox4x64_10(ctr, key):
     c = np.ascontiguousarray(ctr, dtype=np.uint64)
     k = np.ascontiguousarray(key, dtype=np.uint64)
@@ -160,20 +168,24 @@ def saguaro(zq, T: float, F, cache_ids, cache_mass, C: float, want_qprime: bool 
     return Z, qp
 
 
-def draft_sample(zq, T: float, F, cache_ids, Z, C: float, seed: int, round_: int):
-    """Harness step: draft tokens sampled from the reweighted draft law q'."""
+def draft_sample(zq, T: float, F, cache_ids, Z, C: float, seed: int, round_: int, b_base: int = 0,
+                 cdf_eps: float = None, want_gaps: bool = False):
+    """Harness step: draft tokens sampled from the reweighted draft law q'.  Returns
+    (draft, E2 flags) or, with want_gaps, (draft, flags, gaps)."""
     code, B, K, V, ld = _logit_info(zq)
     F = np.ascontiguousarray(F, dtype=np.int32)
     cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
     Z = np.ascontiguousarray(Z, dtype=np.float64)
     d = np.zeros((B, K), dtype=np.int32)
     flags = np.zeros((B, K), dtype=np.uint8)
+    gaps = np.zeros((B, K))
+    eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_draft_sample(B, K, V, ld, code, _base(zq), T, _ptr(F), int(F.sum()), _ptr(cache_ids),
-                           _ptr(Z), C, seed, round_, _ptr(d), _ptr(flags))
-    return d, flags
+                           _ptr(Z), C, seed, round_, b_base, eps, _ptr(d), _ptr(flags), _ptr(gaps))
+    return (d, flags, gaps) if want_gaps else (d, flags)
 
 
-def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_):
+def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_, b_base: int = 0):
     code, B, K, V, ld = _logit_info(zp)
     F = np.ascontiguousarray(F, dtype=np.int32)
     pm, ps, pa = (np.ascontiguousarray(x) for x in pstats[:3])
@@ -187,12 +199,12 @@ def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_):
     exc = np.zeros(B, dtype=np.uint8)
     lib().orc_verify(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(draft), _ptr(pm), _ptr(ps), _ptr(pa),
                      _ptr(qm), _ptr(qs), _ptr(qa), _ptr(F), int(F.sum()), _ptr(cache_ids), _ptr(Z), C,
-                     seed, round_, _ptr(acc), _ptr(aprob), _ptr(err), _ptr(exc))
+                     seed, round_, b_base, _ptr(acc), _ptr(aprob), _ptr(err), _ptr(exc))
     return acc, aprob, err, exc
 
 
 def residual_sample(zp, zq, T, pstats, qstats, F, cache_ids, Z, C, accept_len, seed, round_,
-                    want_resid: bool = False):
+                    want_resid: bool = False, b_base: int = 0, cdf_eps: float = None):
     code, B, K, V, ld = _logit_info(zp)
     F = np.ascontiguousarray(F, dtype=np.int32)
     pm, ps, pa = (np.ascontiguousarray(x) for x in pstats[:3])
@@ -205,14 +217,15 @@ def residual_sample(zp, zq, T, pstats, qstats, F, cache_ids, Z, C, accept_len, s
     resid = np.zeros((B, V)) if want_resid else None
     err = np.zeros(B, dtype=np.int32)
     exc = np.zeros(B, dtype=np.uint8)
+    eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_residual_sample(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(pm), _ptr(ps), _ptr(pa),
                               _ptr(qm), _ptr(qs), _ptr(qa), _ptr(F), int(F.sum()), _ptr(cache_ids),
-                              _ptr(Z), C, _ptr(accept_len), seed, round_, _ptr(bonus), _ptr(zr),
-                              _ptr(resid), _ptr(err), _ptr(exc))
+                              _ptr(Z), C, _ptr(accept_len), seed, round_, b_base, eps, _ptr(bonus), _ptr(zr),
+                              _ptr(resid), _ptr(err), _ptr(exc), None)
     return bonus, zr, resid, err, exc
 
 
-def cache_lookup(K, V, F, cache_ids, accept_len, bonus, fallback_uniform, seed, round_):
+def cache_lookup(K, V, F, cache_ids, accept_len, bonus, fallback_uniform, seed, round_, b_base: int = 0):
     F = np.ascontiguousarray(F, dtype=np.int32)
     cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
     accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
@@ -223,7 +236,8 @@ def cache_lookup(K, V, F, cache_ids, accept_len, bonus, fallback_uniform, seed, 
     fb = np.zeros((B, K), dtype=np.int32)
     err = np.zeros(B, dtype=np.int32)
     lib().orc_cache_lookup(B, K, V, _ptr(F), int(F.sum()), _ptr(cache_ids), _ptr(accept_len), _ptr(bonus),
-                           int(bool(fallback_uniform)), seed, round_, _ptr(hit), _ptr(slot), _ptr(fb), _ptr(err))
+                           int(bool(fallback_uniform)), seed, round_, b_base, _ptr(hit), _ptr(slot), _ptr(fb),
+                           _ptr(err))
     return hit, slot, fb, err
 
 
@@ -247,9 +261,11 @@ class RoundResult:
     fallback_tokens: np.ndarray
     err: np.ndarray
     exc: np.ndarray
+    cdf_gap: np.ndarray
 
 
-def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap=None) -> RoundResult:
+def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap=None,
+           b_base: int = 0, cdf_eps: float = None) -> RoundResult:
     """One whole round in the method's order.  ``exc`` holds the per-sequence
     exception bits E1..E5 decided from the oracle's own fp64 values."""
     code, B, K, V, ld = _logit_info(zp)
@@ -266,13 +282,16 @@ def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap
         cache_ids=np.zeros((B, Bf), np.int32), cache_mass=np.zeros(R), Z=np.zeros(R),
         accept_len=np.zeros(B, np.int32), accept_prob=np.zeros((B, K)), bonus=np.zeros(B, np.int32),
         resid_mass=np.zeros(B), hit=np.zeros(B, np.uint8), slot=np.zeros(B, np.int32),
-        fallback_tokens=np.zeros((B, K), np.int32), err=np.zeros(B, np.int32), exc=np.zeros(B, np.uint8))
+        fallback_tokens=np.zeros((B, K), np.int32), err=np.zeros(B, np.int32), exc=np.zeros(B, np.uint8),
+        cdf_gap=np.zeros(B))
     o = out
+    eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_round(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(F), Bf, C, _ptr(draft), seed,
-                    round_idx, int(bool(fallback_uniform)), _ptr(o.p_max), _ptr(o.p_sum), _ptr(o.p_arg),
+                    round_idx, b_base, eps, int(bool(fallback_uniform)), _ptr(o.p_max), _ptr(o.p_sum), _ptr(o.p_arg),
                     _ptr(o.q_max), _ptr(o.q_sum), _ptr(o.q_arg), _ptr(o.cache_ids), _ptr(o.cache_mass),
                     _ptr(o.Z), _ptr(o.accept_len), _ptr(o.accept_prob), _ptr(o.bonus), _ptr(o.resid_mass),
-                    _ptr(o.hit), _ptr(o.slot), _ptr(o.fallback_tokens), _ptr(o.err), _ptr(o.exc))
+                    _ptr(o.hit), _ptr(o.slot), _ptr(o.fallback_tokens), _ptr(o.err), _ptr(o.exc),
+                    _ptr(o.cdf_gap))
     if fanout_gap is not None and fanout_gap < FANOUT_EPS:
         o.exc |= E4_FANOUT_TIE
     return out

@@ -28,6 +28,10 @@
  * with one plain loop per definition; the only library routines used are qsort
  * (sorting candidate ids) and exp/pow/floor from libm.
  *
+ * The functions that draw uniforms take b_base, the global index of the first
+ * sequence passed in, so that a sub-batch of a larger batch draws the same uniforms
+ * as it would inside the whole batch.
+ *
  * Pins: the Python tests check these functions against closed forms, numpy
  * library routines, exact enumeration on tiny vocabularies and numpy's own
  * Philox4x64 generator.  No function here is "parity unpinned".
@@ -36,6 +40,9 @@
 #include <stdlib.h>
 #include <string.h>
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_F32 0
 #define ORC_BF16 1
@@ -58,10 +65,19 @@
 #define ORC_E4_FANOUT_TIE 8
 #define ORC_E5_TINY_PROB 16
 
-#define ORC_TIE_EPS 1e-5
+#define ORC_TIE_EPS 1e-5   /* accept near-tie |u - p/q'|, as the method's parity rule states */
 #define ORC_RESID_EPS 1e-5
 #define ORC_FANOUT_EPS 1e-9
 #define ORC_TINY 1e-30
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------- */
 /* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
@@ -298,6 +314,11 @@ void orc_saguaro(int B, int K, int V, int64_t ld, int dtype, const void* q_logit
 }
 
 /* ------------------------------------------------------------------------- */
+/* Inverse-CDF near-tie (E2).  The decision "smallest j with running sum > u * total"
+ * flips only when u lies within the arithmetic error of the sums from a step of the
+ * normalised CDF; cdf_eps is the half-width of that band, a parameter of the parity
+ * rule (the oracle itself is exact up to fp64 rounding). */
+
 /* Inverse-CDF selection: the smallest j whose running sum of w exceeds u * total,
  * ids scanned in ascending order; if rounding leaves no such j, the largest j with
  * w_j > 0.  *gap (nullable) receives min(|C(j*) - u|, |C(j*-1) - u|) with
@@ -330,7 +351,8 @@ static int inverse_cdf(const double* w, int V, double total, double u, double* g
  * with u = U(seed, round, b, i, DRAFT).  At T = 0 the draft is greedy. */
 void orc_draft_sample(int B, int K, int V, int64_t ld, int dtype, const void* q_logits, double T,
                       const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
-                      uint64_t seed, uint64_t round, int32_t* draft, uint8_t* tie_flags /* [B,K] */) {
+                      uint64_t seed, uint64_t round, int64_t b_base, double cdf_eps, int32_t* draft,
+                      uint8_t* tie_flags /* [B,K] */, double* gaps /* nullable [B,K] */) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t bi = 0; bi < (int64_t)B * K; ++bi) {
         int b = (int)(bi / K), i = (int)(bi % K);
@@ -351,11 +373,13 @@ void orc_draft_sample(int B, int K, int V, int64_t ld, int dtype, const void* q_
                 w[x] = row_prob(z[x], x, m, s, arg, T) * (in_cache(S, F[i], x) ? C : 1.0) / Z[r];
                 tot += w[x];
             }
-            double u = orc_uniform(seed, round, ORC_PURPOSE_DRAFT, b, i), gap;
+            double u = orc_uniform(seed, round, ORC_PURPOSE_DRAFT, b_base + b, i), gap;
             draft[bi] = inverse_cdf(w, V, tot, u, &gap);
-            if (gap < ORC_TIE_EPS) flag = ORC_E2_CDF_TIE;
+            if (gap < cdf_eps) flag = ORC_E2_CDF_TIE;
+            if (gaps) gaps[bi] = gap;
         } else {
             draft[bi] = arg;
+            if (gaps) gaps[bi] = INFINITY;
         }
         if (tie_flags) tie_flags[bi] = flag;
         free(w);
@@ -377,8 +401,8 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
                 const double* p_max, const double* p_sum, const int32_t* p_arg,
                 const double* q_max, const double* q_sum, const int32_t* q_arg,
                 const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
-                uint64_t seed, uint64_t round, int32_t* accept_len, double* accept_prob,
-                int32_t* err, uint8_t* exc) {
+                uint64_t seed, uint64_t round, int64_t b_base, int32_t* accept_len,
+                double* accept_prob, int32_t* err, uint8_t* exc) {
     for (int b = 0; b < B; ++b) {
         int k = K, e = 0, x_flags = 0;
         int Oi = 0;
@@ -406,7 +430,7 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
                 }
                 if (k == K) {
                     /* no earlier rejection: this position is tested */
-                    double u = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b, i);
+                    double u = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b_base + b, i);
                     if (fabs(u - ratio) < ORC_TIE_EPS) x_flags |= ORC_E1_ACCEPT_TIE;
                     if (p < ORC_TINY || qp < ORC_TINY) x_flags |= ORC_E5_TINY_PROB;
                 }
@@ -417,7 +441,7 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
             if (k == K) {
                 int acc;
                 if (!ok) acc = 0;
-                else if (T > 0.0) acc = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b, i) < ratio;
+                else if (T > 0.0) acc = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b_base + b, i) < ratio;
                 else acc = (d == p_arg[r]);
                 if (!acc) k = i;
             }
@@ -442,11 +466,13 @@ void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void*
                          const double* p_max, const double* p_sum, const int32_t* p_arg,
                          const double* q_max, const double* q_sum, const int32_t* q_arg,
                          const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
-                         const int32_t* accept_len, uint64_t seed, uint64_t round, int32_t* bonus,
-                         double* resid_mass, double* resid, int32_t* err, uint8_t* exc) {
+                         const int32_t* accept_len, uint64_t seed, uint64_t round, int64_t b_base,
+                         double cdf_eps, int32_t* bonus, double* resid_mass, double* resid, int32_t* err,
+                         uint8_t* exc, double* cdf_gap /* nullable [B] */) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         int k = accept_len[b];
+        if (cdf_gap) cdf_gap[b] = INFINITY;
         if (k < 0 || k > K) {
             bonus[b] = -1;
             if (resid_mass) resid_mass[b] = 0.0;
@@ -486,9 +512,10 @@ void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void*
                 Zr += w[x];
             }
         }
-        double u = orc_uniform(seed, round, ORC_PURPOSE_BONUS, b, k), gap;
+        double u = orc_uniform(seed, round, ORC_PURPOSE_BONUS, b_base + b, k), gap;
         bonus[b] = inverse_cdf(w, V, Zr, u, &gap);
-        if (gap < ORC_TIE_EPS) x_flags |= ORC_E2_CDF_TIE;
+        if (gap < cdf_eps) x_flags |= ORC_E2_CDF_TIE;
+        if (cdf_gap) cdf_gap[b] = gap;
         if (resid_mass) resid_mass[b] = Zr;
         if (resid)
             for (int x = 0; x < V; ++x) resid[(int64_t)b * V + x] = w[x];
@@ -506,7 +533,7 @@ void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void*
  * FALLBACK); otherwise the fallback tokens are -1. */
 void orc_cache_lookup(int B, int K, int V, const int32_t* F, int Bf, const int32_t* cache_ids,
                       const int32_t* accept_len, const int32_t* bonus, int fallback_uniform,
-                      uint64_t seed, uint64_t round, uint8_t* hit, int32_t* slot,
+                      uint64_t seed, uint64_t round, int64_t b_base, uint8_t* hit, int32_t* slot,
                       int32_t* fallback_tokens, int32_t* err) {
     for (int b = 0; b < B; ++b) {
         int k = accept_len[b];
@@ -524,7 +551,7 @@ void orc_cache_lookup(int B, int K, int V, const int32_t* F, int Bf, const int32
         for (int j = 0; j < K; ++j) {
             int32_t t = -1;
             if (!h && fallback_uniform) {
-                uint64_t x = orc_uniform_u32(seed, round, ORC_PURPOSE_FALLBACK, b, j);
+                uint64_t x = orc_uniform_u32(seed, round, ORC_PURPOSE_FALLBACK, b_base + b, j);
                 t = (int32_t)((x * (uint64_t)V) >> 32);
             }
             fallback_tokens[(int64_t)b * K + j] = t;
@@ -537,21 +564,23 @@ void orc_cache_lookup(int B, int K, int V, const int32_t* F, int Bf, const int32
  * Saguaro reweight, verify, bonus, lookup.  All outputs in double / int. */
 void orc_round(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
                const void* q_logits, double T, const int32_t* F, int Bf, double C,
-               const int32_t* draft, uint64_t seed, uint64_t round, int fallback_uniform,
+               const int32_t* draft, uint64_t seed, uint64_t round, int64_t b_base, double cdf_eps,
+               int fallback_uniform,
                double* p_max, double* p_sum, int32_t* p_arg, double* q_max, double* q_sum,
                int32_t* q_arg, int32_t* cache_ids, double* cache_mass, double* Z,
                int32_t* accept_len, double* accept_prob, int32_t* bonus, double* resid_mass,
-               uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* err, uint8_t* exc) {
+               uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* err, uint8_t* exc,
+               double* cdf_gap) {
     orc_softmax(B, K, V, ld, dtype, p_logits, T, p_max, p_sum, p_arg, NULL);
     orc_softmax(B, K, V, ld, dtype, q_logits, T, q_max, q_sum, q_arg, NULL);
     orc_build_cache(B, K, V, ld, dtype, q_logits, T, F, Bf, cache_ids, cache_mass);
     orc_saguaro(B, K, V, ld, dtype, q_logits, T, F, Bf, cache_ids, cache_mass, C, Z, NULL);
     for (int b = 0; b < B; ++b) { err[b] = 0; exc[b] = 0; }
     orc_verify(B, K, V, ld, dtype, p_logits, q_logits, T, draft, p_max, p_sum, p_arg, q_max, q_sum,
-               q_arg, F, Bf, cache_ids, Z, C, seed, round, accept_len, accept_prob, err, exc);
+               q_arg, F, Bf, cache_ids, Z, C, seed, round, b_base, accept_len, accept_prob, err, exc);
     orc_residual_sample(B, K, V, ld, dtype, p_logits, q_logits, T, p_max, p_sum, p_arg, q_max, q_sum,
-                        q_arg, F, Bf, cache_ids, Z, C, accept_len, seed, round, bonus, resid_mass,
-                        NULL, err, exc);
+                        q_arg, F, Bf, cache_ids, Z, C, accept_len, seed, round, b_base, cdf_eps,
+                        bonus, resid_mass, NULL, err, exc, cdf_gap);
     orc_cache_lookup(B, K, V, F, Bf, cache_ids, accept_len, bonus, fallback_uniform, seed, round,
-                     hit, slot, fallback_tokens, err);
+                     b_base, hit, slot, fallback_tokens, err);
 }

@@ -1,0 +1,73 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI, run
+the fp64 oracle on the same bits, and compare under the parity rules:
+ - integer outputs bit-exact, except on sequences the oracle flags with its own fp64
+   values: E1 (|u - p/q'| < 1e-5 at a tested position) and E5 (a tested p or q'
+   below 1e-30) exclude everything from the accepted length on; E2 (u within 1e-5 of
+   a CDF step around the sampled id) and E3 (residual mass below 1e-5) exclude the
+   bonus, hit, slot and fallback tokens;
+ - probabilities within 1e-5 absolute; row sums within 1e-5 relative; row maxima
+   exact (they are input values)."""
+import numpy as np
+import torch
+
+import oracle
+import lossless_rejection_sampling_ssd_amd as ssd
+from lossless_rejection_sampling_ssd_amd.workloads import to_oracle_array
+
+PROB_ATOL = 1e-5
+SUM_RTOL = 1e-5
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def oracle_draft(zp_np, zq_np, T, F, C, seed, rnd, b_base=0):
+    """Draft tokens sampled by the oracle from its own q' (harness step)."""
+    ids, mass = oracle.build_cache(zq_np, T, F)
+    Z, _ = oracle.saguaro(zq_np, T, F, ids, mass, C)
+    d, flags = oracle.draft_sample(zq_np, T, F, ids, Z, C, seed, rnd, b_base)
+    return d, flags
+
+
+def gpu_round(zp, zq, T, F, C, draft, seed, rnd, fallback, ws=None):
+    shape = ssd.shape_of(zp, T)
+    B, K = shape.B, shape.K
+    buf = ssd.RoundBuffers(B, K, int(sum(F)))
+    d = torch.as_tensor(np.ascontiguousarray(draft), dtype=torch.int32, device="cuda")
+    ssd.ssd_round(shape, zp, zq, d, list(F), C, seed, rnd, fallback, buf.out, ws=ws)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in buf.t.items()}
+
+
+def compare_round(g, o, K, Bf, check_stats=True, label=""):
+    """Asserts parity of a GPU fused round g (dict of numpy) with an oracle round o
+    (oracle.RoundResult).  Returns the number of flagged sequences."""
+    B = o.accept_len.shape[0]
+    R = B * (K + 1)
+    if check_stats:
+        assert np.array_equal(g["p_max"], o.p_max.reshape(R).astype(np.float32)), label
+        assert np.array_equal(g["q_max"], o.q_max.reshape(R).astype(np.float32)), label
+        np.testing.assert_allclose(g["p_sum"], o.p_sum.reshape(R), rtol=SUM_RTOL, err_msg=label)
+        np.testing.assert_allclose(g["q_sum"], o.q_sum.reshape(R), rtol=SUM_RTOL, err_msg=label)
+        assert np.array_equal(g["p_argmax"], o.p_arg.reshape(R)), label
+        assert np.array_equal(g["q_argmax"], o.q_arg.reshape(R)), label
+    if Bf > 0:
+        assert np.array_equal(g["cache_ids"][:, :Bf], o.cache_ids), label
+    np.testing.assert_allclose(g["cache_mass"], o.cache_mass.reshape(R), atol=PROB_ATOL, rtol=0, err_msg=label)
+    np.testing.assert_allclose(g["Z"], o.Z.reshape(R), atol=PROB_ATOL, rtol=0, err_msg=label)
+    np.testing.assert_allclose(g["accept_prob"], o.accept_prob, atol=PROB_ATOL, rtol=0, err_msg=label)
+    assert np.array_equal(g["dev_err"], o.err), label
+    e_len = (o.exc & (oracle.E1_ACCEPT_TIE | oracle.E5_TINY_PROB)) != 0
+    e_any = o.exc != 0
+    ok = ~e_len
+    assert np.array_equal(g["accept_len"][ok], o.accept_len[ok]), (label, np.nonzero(g["accept_len"] != o.accept_len))
+    same_k = g["accept_len"] == o.accept_len
+    np.testing.assert_allclose(g["resid_mass"][same_k], o.resid_mass[same_k], atol=PROB_ATOL, rtol=0, err_msg=label)
+    ok2 = ~e_any
+    bad = np.nonzero((g["bonus"] != o.bonus) & ok2)[0]
+    assert bad.size == 0, (label, "bonus", bad[:10], g["bonus"][bad[:10]], o.bonus[bad[:10]])
+    assert np.array_equal(g["hit"][ok2], o.hit[ok2]), label
+    assert np.array_equal(g["slot"][ok2], o.slot[ok2]), label
+    assert np.array_equal(g["fallback_tokens"][ok2], o.fallback_tokens[ok2]), label
+    return int(e_any.sum())

@@ -1,0 +1,370 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle on seeded
+synthetic inputs.  Each test prints what names its case before the GPU step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import lossless_rejection_sampling_ssd_amd as ssd
+from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_logits, scaled, to_oracle_array
+
+from gpu_helpers import PROB_ATOL, SUM_RTOL, compare_round, gpu_round, oracle_draft
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def _case(msg):
+    print("\n[case] " + msg, flush=True)
+
+
+def _rand(B, K, V, dtype, seed, scale=2.0, noise=0.8, ld=None):
+    g = torch.Generator().manual_seed(seed)
+    zq = torch.randn((B, K + 1, V), generator=g) * scale
+    zp = zq + torch.randn((B, K + 1, V), generator=g) * noise
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    zq, zp = zq.to(dt), zp.to(dt)
+    if ld is not None and ld > V:
+        def pad(z):
+            o = torch.full((B, K + 1, ld), float("nan"), dtype=dt)
+            o[:, :, :V] = z
+            return o[:, :, :V]
+        zq, zp = pad(zq), pad(zp)
+    return zq, zp
+
+
+def _to_dev(z):
+    """Device copy keeping the row stride of a padded view."""
+    if z.is_contiguous():
+        return z.cuda()
+    B, K1, V = z.shape
+    ld = z.stride(1)
+    base = torch.empty((B, K1, ld), dtype=z.dtype)
+    base[:, :, :V] = z
+    base[:, :, V:] = float("nan")
+    return base.cuda()[:, :, :V]
+
+
+# ----------------------------------------------------------------------------- softmax
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,pad", [(7, 0), (1000, 0), (4099, 0), (20011, 0), (33000, 8), (5003, 3)])
+@pytest.mark.parametrize("T", [0.0, 0.7, 1.0])
+def test_softmax(dtype, V, pad, T):
+    _case("softmax dtype=%s V=%d pad=%d T=%g" % (dtype, V, pad, T))
+    B, K = 3, 2
+    zq, zp = _rand(B, K, V, dtype, 11 + V, ld=V + pad if pad else None)
+    z = _to_dev(zp)
+    shape = ssd.shape_of(z, T)
+    R = B * (K + 1)
+    m = torch.zeros(R, device="cuda")
+    s = torch.zeros(R, dtype=torch.float64, device="cuda")
+    a = torch.zeros(R, dtype=torch.int32, device="cuda")
+    probs = torch.zeros((B, K + 1, V), device="cuda")
+    ssd.ssd_softmax(shape, z, m, s, a, probs)
+    torch.cuda.synchronize()
+    om, os_, oa, op = oracle.softmax(to_oracle_array(zp), T, want_probs=True)
+    assert np.array_equal(m.cpu().numpy(), om.reshape(R).astype(np.float32))
+    np.testing.assert_allclose(s.cpu().numpy(), os_.reshape(R), rtol=SUM_RTOL)
+    assert np.array_equal(a.cpu().numpy(), oa.reshape(R))
+    np.testing.assert_allclose(probs.cpu().numpy(), op, atol=PROB_ATOL, rtol=0)
+
+
+# ----------------------------------------------------------------------------- cache
+def _gpu_stats(z, T):
+    shape = ssd.shape_of(z, T)
+    R = shape.B * (shape.K + 1)
+    m = torch.zeros(R, device="cuda")
+    s = torch.zeros(R, dtype=torch.float64, device="cuda")
+    a = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ssd.ssd_softmax(shape, z, m, s, a)
+    return m, s, a
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,F,kind", [
+    (5000, [20, 14, 10, 7, 5], "gauss"),
+    (5000, [64, 0, 3, 1, 0], "gauss"),
+    (128256, [24, 19, 16, 13, 10], "quantised"),
+    (3000, [40, 30, 20, 10, 5], "constant"),
+    (9, [9, 4, 1, 0, 2], "gauss"),
+    (20011, [1, 1, 1, 1, 1], "neginf"),
+])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_build_cache(dtype, V, F, kind, T):
+    _case("build_cache dtype=%s V=%d F=%s kind=%s T=%g" % (dtype, V, F, kind, T))
+    B, K = 2, len(F) - 1
+    zq, _ = _rand(B, K, V, dtype, 5 + V)
+    if kind == "quantised":
+        zq = (zq * 2).round() / 2          # many equal values: ties broken by id
+    elif kind == "constant":
+        zq = torch.full_like(zq, 1.25)     # every id ties: exact slow path
+    elif kind == "neginf":
+        zq[:, :, ::3] = float("-inf")
+    z = zq.cuda()
+    m, s, a = _gpu_stats(z, T)
+    Bf = sum(F)
+    ids = torch.zeros((B, Bf), dtype=torch.int32, device="cuda")
+    mass = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
+    ssd.ssd_build_cache(ssd.shape_of(z, T), z, m, s, F, ids, mass)
+    torch.cuda.synchronize()
+    oids, omass = oracle.build_cache(to_oracle_array(zq), T, np.array(F, np.int32))
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(mass.cpu().numpy(), omass.reshape(-1), atol=PROB_ATOL, rtol=0)
+
+
+# ----------------------------------------------------------------------------- Saguaro + draft
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,C", [(1.0, 0.5), (0.7, 0.2), (1.0, 1.0), (0.0, 0.5)])
+def test_saguaro_and_draft(dtype, T, C):
+    V, B, K = 6007, 8, 3
+    _case("saguaro dtype=%s T=%g C=%g" % (dtype, T, C))
+    zq, _ = _rand(B, K, V, dtype, 21)
+    F = [6, 3, 2, 1]
+    z = zq.cuda()
+    m, s, a = _gpu_stats(z, T)
+    ids = torch.zeros((B, sum(F)), dtype=torch.int32, device="cuda")
+    mass = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
+    ssd.ssd_build_cache(ssd.shape_of(z, T), z, m, s, F, ids, mass)
+    Z = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
+    qp = torch.zeros((B, K + 1, V), device="cuda")
+    d = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+    ssd.ssd_saguaro_reweight(ssd.shape_of(z, T), mass, C, Z, z, m, s, a, F, ids, qp, seed=77, round_=5, draft=d)
+    torch.cuda.synchronize()
+    zq_np = to_oracle_array(zq)
+    oids, omass = oracle.build_cache(zq_np, T, np.array(F, np.int32))
+    oZ, oqp = oracle.saguaro(zq_np, T, np.array(F, np.int32), oids, omass, C, want_qprime=True)
+    np.testing.assert_allclose(Z.cpu().numpy(), oZ.reshape(-1), atol=PROB_ATOL, rtol=0)
+    np.testing.assert_allclose(qp.cpu().numpy(), oqp, atol=PROB_ATOL, rtol=0)
+    od, flags = oracle.draft_sample(zq_np, T, np.array(F, np.int32), oids, oZ, C, 77, 5)
+    ok = flags == 0
+    assert np.array_equal(d.cpu().numpy()[ok], od[ok])
+
+
+# ----------------------------------------------------------------------------- chain of the six calls
+def _chain(zp, zq, T, F, C, draft, seed, rnd, fallback):
+    """The six separate calls in the method's order (GPU)."""
+    shape = ssd.shape_of(zp, T)
+    B, K = shape.B, shape.K
+    R = B * (K + 1)
+    Bf = sum(F)
+    pm, ps, pa = _gpu_stats(zp, T)
+    qm, qs, qa = _gpu_stats(zq, T)
+    ids = torch.zeros((B, max(Bf, 1)), dtype=torch.int32, device="cuda")
+    mass = torch.zeros(R, dtype=torch.float64, device="cuda")
+    ssd.ssd_build_cache(shape, zq, qm, qs, F, ids, mass)
+    Z = torch.zeros(R, dtype=torch.float64, device="cuda")
+    ssd.ssd_saguaro_reweight(shape, mass, C, Z)
+    d = torch.as_tensor(np.ascontiguousarray(draft), dtype=torch.int32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    aprob = torch.zeros((B, K), device="cuda")
+    err = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ssd.ssd_verify(shape, zp, zq, d, pm, ps, pa, qm, qs, F, ids, Z, C, seed, rnd, acc, aprob, err)
+    bonus = torch.zeros(B, dtype=torch.int32, device="cuda")
+    zr = torch.zeros(B, dtype=torch.float64, device="cuda")
+    ssd.ssd_residual_sample(shape, zp, zq, pm, ps, pa, qm, qs, F, ids, Z, C, acc, seed, rnd, bonus, zr, err)
+    hit = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    slot = torch.zeros(B, dtype=torch.int32, device="cuda")
+    fb = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+    ssd.ssd_cache_lookup(B, K, shape.V, F, ids, acc, bonus, fallback, seed, rnd, hit, slot, fb, err)
+    torch.cuda.synchronize()
+    out = {"p_max": pm, "p_sum": ps, "p_argmax": pa, "q_max": qm, "q_sum": qs, "q_argmax": qa, "cache_ids": ids,
+           "cache_mass": mass, "Z": Z, "accept_len": acc, "accept_prob": aprob, "bonus": bonus, "resid_mass": zr,
+           "hit": hit, "slot": slot, "fallback_tokens": fb, "dev_err": err}
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+ROUND_CASES = [
+    # (label, dtype, B, K, V, T, F, C, fallback, scale, noise)
+    ("c1-like", "f32", 1, 4, 32000, 1.0, [6, 4, 3, 2, 1], 0.5, 0, 2.0, 0.7),
+    ("c2-greedy", "f32", 16, 5, 32000, 0.0, [13, 8, 5, 3, 2, 1], 0.3, 0, 2.5, 0.8),
+    ("c2-T0.7", "f32", 16, 5, 32000, 0.7, [13, 8, 5, 3, 2, 1], 0.3, 0, 2.5, 0.8),
+    ("c3-small", "bf16", 12, 8, 40000, 1.0, [20, 14, 10, 7, 5, 3, 2, 2, 1], 0.5, 0, 3.0, 1.0),
+    ("c5-small", "bf16", 24, 4, 151936, 1.0, [17, 8, 4, 2, 1], 0.5, 1, 2.0, 1.5),
+    ("ragged", "bf16", 5, 2, 4101, 1.3, [9, 0, 4], 0.8, 1, 2.0, 0.6),
+    ("tiny-V", "f32", 7, 3, 5, 1.0, [2, 1, 1, 1], 0.4, 1, 1.0, 0.5),
+    ("K=1", "f32", 9, 1, 777, 0.9, [3, 2], 0.5, 1, 2.0, 0.5),
+    ("Bf=0", "bf16", 4, 3, 3000, 1.0, [0, 0, 0, 0], 1.0, 1, 2.0, 0.8),
+    ("K=16", "f32", 3, 16, 2000, 1.0, [4] * 17, 0.6, 0, 2.0, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", ROUND_CASES, ids=[c[0] for c in ROUND_CASES])
+def test_round_vs_oracle_and_chain(case):
+    label, dtype, B, K, V, T, F, C, fb, scale, noise = case
+    _case("round " + label)
+    zq, zp = _rand(B, K, V, dtype, sum(map(ord, label)), scale, noise)
+    seed, rnd = 0x1234 + B, 9
+    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, fb)
+    zpd, zqd = zp.cuda(), zq.cuda()
+    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    compare_round(g, o, K, sum(F), label=label)
+    ch = _chain(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    for k in ch:
+        a, b = g[k], ch[k]
+        if k == "cache_ids":
+            a, b = a[:, :sum(F)], b[:, :sum(F)]
+        assert np.array_equal(a, b), (label, k)
+    g2 = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    for k in g:
+        assert np.array_equal(g[k], g2[k]), ("determinism", label, k)
+
+
+def test_forced_paths():
+    """All accepted (p = q, C = 1); rejection at position 0 (z_p(d_0) = -inf);
+    invalid draft tokens; a bonus that cannot be cached (F = 0) misses."""
+    B, K, V, T = 6, 4, 3001, 1.0
+    zq, zp = _rand(B, K, V, "f32", 3)
+    F = [5, 4, 3, 2, 1]
+    zp_same = zq.clone()
+    zp_np, zq_np = to_oracle_array(zp_same), to_oracle_array(zq)
+    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), 1.0, 1, 1)
+    _case("forced all-accept")
+    g = gpu_round(zp_same.cuda(), zq.cuda(), T, F, 1.0, draft, 1, 1, 1)
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), 1.0, draft, 1, 1, 1)
+    compare_round(g, o, K, sum(F), label="all-accept")
+    assert np.all(g["accept_len"] == K)
+    _case("forced reject at 0")
+    zp_rej = zp.clone()
+    for b in range(B):
+        zp_rej[b, 0, draft[b, 0]] = float("-inf")
+    zp_np = to_oracle_array(zp_rej)
+    g = gpu_round(zp_rej.cuda(), zq.cuda(), T, F, 0.5, draft, 1, 1, 1)
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), 0.5, draft, 1, 1, 1)
+    compare_round(g, o, K, sum(F), label="reject0")
+    assert np.all(g["accept_len"] == 0)
+    assert np.all(g["bonus"] != draft[:, 0])
+    _case("forced invalid tokens")
+    bad = draft.copy()
+    bad[1, 0] = -3
+    bad[2, 2] = V
+    bad[3, 3] = V + 100
+    g = gpu_round(zp.cuda(), zq.cuda(), T, F, 0.5, bad, 1, 1, 1)
+    o = oracle.round_(to_oracle_array(zp), zq_np, T, np.array(F, np.int32), 0.5, bad, 1, 1, 1)
+    compare_round(g, o, K, sum(F), label="invalid")
+    assert g["dev_err"][1] & ssd.SSD_DEVERR_TOKEN_RANGE and g["accept_len"][1] == 0
+
+
+def test_lookup_oracle_fed():
+    """ssd_cache_lookup on oracle-made inputs: random caches, lengths (including out
+    of range) and bonus tokens."""
+    _case("lookup oracle-fed")
+    rng = np.random.default_rng(3)
+    B, K, V = 300, 4, 50
+    F = [6, 4, 3, 0, 2]
+    Bf = sum(F)
+    ids = np.stack([rng.permutation(V)[:Bf] for _ in range(B)]).astype(np.int32)
+    acc = rng.integers(-1, K + 2, B).astype(np.int32)
+    bonus = rng.integers(0, V, B).astype(np.int32)
+    for mode in (0, 1):
+        oh, osl, ofb, oerr = oracle.cache_lookup(K, V, np.array(F, np.int32), ids, acc, bonus, mode, 5, 6)
+        t = lambda x: torch.as_tensor(x, device="cuda")  # noqa: E731
+        hit = torch.zeros(B, dtype=torch.uint8, device="cuda")
+        slot = torch.zeros(B, dtype=torch.int32, device="cuda")
+        fb = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+        err = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ssd.ssd_cache_lookup(B, K, V, F, t(ids), t(acc), t(bonus), mode, 5, 6, hit, slot, fb, err)
+        torch.cuda.synchronize()
+        assert np.array_equal(hit.cpu().numpy(), oh)
+        assert np.array_equal(slot.cpu().numpy(), osl)
+        assert np.array_equal(fb.cpu().numpy(), ofb)
+        assert np.array_equal(err.cpu().numpy(), oerr)
+
+
+def test_residual_bad_len_and_greedy():
+    """ssd_residual_sample with accepted lengths outside [0, K] reports the error and
+    returns -1; at T = 0 it returns argmax p_k."""
+    B, K, V = 4, 3, 999
+    zq, zp = _rand(B, K, V, "f32", 8)
+    F = [3, 2, 1, 1]
+    for T in (1.0, 0.0):
+        _case("residual bad len T=%g" % T)
+        zpd, zqd = zp.cuda(), zq.cuda()
+        pm, ps, pa = _gpu_stats(zpd, T)
+        qm, qs, qa = _gpu_stats(zqd, T)
+        ids = torch.zeros((B, sum(F)), dtype=torch.int32, device="cuda")
+        mass = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
+        shape = ssd.shape_of(zpd, T)
+        ssd.ssd_build_cache(shape, zqd, qm, qs, F, ids, mass)
+        Z = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
+        ssd.ssd_saguaro_reweight(shape, mass, 0.5, Z)
+        acc = torch.tensor([0, 3, -1, 4], dtype=torch.int32, device="cuda")
+        bonus = torch.zeros(B, dtype=torch.int32, device="cuda")
+        err = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ssd.ssd_residual_sample(shape, zpd, zqd, pm, ps, pa, qm, qs, F, ids, Z, 0.5, acc, 1, 2, bonus, None, err)
+        torch.cuda.synchronize()
+        bo = bonus.cpu().numpy()
+        eo = err.cpu().numpy()
+        assert bo[2] == -1 and bo[3] == -1
+        assert eo[2] == ssd.SSD_DEVERR_LEN_RANGE and eo[3] == ssd.SSD_DEVERR_LEN_RANGE
+        assert eo[0] == 0 and eo[1] == 0
+        if T == 0.0:
+            ap = np.argmax(zp.numpy(), -1)
+            assert bo[0] == ap[0, 0] and bo[1] == ap[1, 3]
+
+
+# ----------------------------------------------------------------------------- workloads
+def test_c1_rounds():
+    """The single-sequence workload: every round with its own logits and counter."""
+    w = WORKLOADS["c1"]
+    F, gap = oracle.fanout(w.K, w.Bf, w.r)
+    flagged = 0
+    n = 300
+    ws = ssd.Workspace()
+    for rnd in range(n):
+        if rnd % 100 == 0:
+            _case("c1 round %d" % rnd)
+        zq, zp = make_logits(w, buffer=rnd)
+        zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+        draft, _ = oracle_draft(zp_np, zq_np, 1.0, F, 0.5, w.seed, rnd)
+        o = oracle.round_(zp_np, zq_np, 1.0, F, 0.5, draft, w.seed, rnd, False, gap)
+        g = gpu_round(zp.cuda(), zq.cuda(), 1.0, F.tolist(), 0.5, draft, w.seed, rnd, 0, ws=ws)
+        flagged += compare_round(g, o, w.K, w.Bf, label="c1 round %d" % rnd)
+    assert flagged <= max(1, n // 100)
+
+
+@pytest.mark.parametrize("name,C,sig", [("c3", 0.5, None), ("c4", 0.2, 1.65), ("c4", 0.8, 0.3), ("c5", 0.5, None)])
+def test_full_size_sampled(name, C, sig):
+    """The workload at its full size in the launch configuration the benchmark
+    times; the oracle recomputes a sample of sequences one by one (their uniforms
+    keep the global sequence index)."""
+    w = WORKLOADS[name]
+    T = w.temps[0]
+    _case("full-size %s C=%g sigma=%s: generate" % (name, C, sig))
+    zq, zp = make_logits(w, target_sigma=sig, device="cuda")
+    F, gap = oracle.fanout(w.K, w.Bf, w.r)
+    rng = np.random.default_rng(w.seed)
+    sample = np.sort(rng.choice(w.B, size=6, replace=False))
+    seed, rnd = w.seed, 1
+    draft = rng.integers(0, w.V, size=(w.B, w.K)).astype(np.int32)
+    zp_h, zq_h = zp.cpu(), zq.cpu()
+    per = {}
+    for b in sample:
+        zp_np = to_oracle_array(zp_h[b:b + 1])
+        zq_np = to_oracle_array(zq_h[b:b + 1])
+        d, _ = oracle_draft(zp_np, zq_np, T, F, C, seed, rnd, b_base=int(b))
+        draft[b] = d[0]
+        per[int(b)] = (zp_np, zq_np)
+    _case("full-size %s: GPU round" % name)
+    g = gpu_round(zp, zq, T, F.tolist(), C, draft, seed, rnd, int(w.fallback_uniform))
+    _case("full-size %s: oracle on %s" % (name, sample.tolist()))
+    for b in sample:
+        zp_np, zq_np = per[int(b)]
+        o = oracle.round_(zp_np, zq_np, T, F, C, draft[b:b + 1], seed, rnd, w.fallback_uniform, gap, int(b))
+        K1 = w.K + 1
+        gb = {k: (v[b * K1:(b + 1) * K1] if v.ndim == 1 and v.shape[0] == w.B * K1 else v[b:b + 1])
+              for k, v in g.items()}
+        compare_round(gb, o, w.K, w.Bf, label="%s b=%d" % (name, b))
+    # properties that hold for every sequence
+    assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= w.K))
+    assert np.all((g["bonus"] >= 0) & (g["bonus"] < w.V))
+    O = np.concatenate([[0], np.cumsum(F)])
+    for b in range(w.B):
+        k = g["accept_len"][b]
+        S = g["cache_ids"][b, O[k]:O[k + 1]]
+        h = g["bonus"][b] in S
+        assert g["hit"][b] == h
+        if not h and w.fallback_uniform:
+            assert np.all((g["fallback_tokens"][b] >= 0) & (g["fallback_tokens"][b] < w.V))
+    assert np.all(g["dev_err"] == 0)
