@@ -28,9 +28,10 @@
  *  - Data-dependent errors never trap: they OR bits into the optional per-sequence
  *    `dev_err[B]` (caller zeroes it): SSD_DEVERR_*.
  *  - `ws` is a workspace of at least ssd_workspace_bytes() bytes, 256-byte aligned,
- *    ZERO-FILLED BY THE CALLER BEFORE ITS FIRST USE.  Each call leaves the counters it
- *    uses back at zero when it completes, so one workspace serves any number of calls
- *    on one stream.  Two calls that overlap in time must not share a workspace.
+ *    owned by the caller.  Its contents need no initialisation: every call writes
+ *    the scratch it reads (per-tile partials, candidate keys, segment sums) before
+ *    reading it, in a later kernel of the same call.  One workspace serves any
+ *    number of calls on one stream; two calls that overlap in time must not share it.
  *  - Uniforms are counter-based: Philox4x64-10 (Salmon et al., SC'11) with key
  *    (seed, purpose) and counter (round, b, i, 0); u = (word0 >> 40) * 2^-24 and
  *    u32 = word0 >> 32.  Purposes: SSD_PURPOSE_*.  Results are reproducible from
@@ -191,10 +192,13 @@ typedef struct {
     int32_t* dev_err;   /* [B], OR-accumulated */
 } ssd_round_out;
 
-/* Optional HIP events (hipEvent_t, may be NULL) recorded around the two streaming
- * passes of ssd_round: the vocabulary pass over every row of both models
- * (softmax statistics, top-F cache, Saguaro and verification) and the bonus pass
- * over the verified rows (residual sampling and lookup). */
+/* Optional HIP events (hipEvent_t, may be NULL) recorded on `stream` around the
+ * two streaming kernels of ssd_round: pass 1 over every row of both models (tile
+ * partials of the softmax statistics and top-F candidates) and pass 2 over the rows
+ * the bonus needs (residual tile sums).  The per-sequence finalisation (cache,
+ * Saguaro, verification) runs between pass1_stop and pass2_start, the bonus
+ * search and lookup after pass2_stop.  At T = 0 pass 2 does not run and its
+ * events are not recorded. */
 typedef struct {
     void* pass1_start;
     void* pass1_stop;
@@ -206,7 +210,8 @@ typedef struct {
  * softmax of both models, cache build, Saguaro reweight, verification, bonus and
  * lookup, with the same arithmetic as the six separate calls (results are
  * bit-identical to chaining them).  Two streaming kernels: one over all
- * 2 B (K+1) rows, one over the <= 2 rows per sequence the bonus needs. */
+ * 2 B (K+1) rows, one over the <= 2 rows per sequence the bonus needs; each is
+ * followed by a small per-sequence kernel. */
 ssd_status ssd_round(const ssd_shape* shape, const void* p_logits, const void* q_logits,
                      const int32_t* draft, const int32_t* F_host, int32_t Bf, float C, ssd_rng rng,
                      int32_t fallback, const ssd_round_out* out, const ssd_round_events* events,

@@ -15,49 +15,41 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Fixed counter region at the start of every workspace, shared by all shapes so that
-// counters left at zero by one call are zero for the next call of any shape.
-constexpr int64_t kCounterWords = 65536;
-constexpr int64_t kCounterHalf = kCounterWords / 2;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace regions (byte offsets).  Every region is written by one kernel of a call
+// and read by a later kernel of the same call; nothing persists between calls.
+//   part   [B][2][K+1][nt]        WavePartial, one per wave tile
+//   cand   [B][K+1][nt][cap]      top-F candidate keys of the draft rows' tiles
+//   seg    [max(B, B K)][nt]      (weight sum, target-law sum) per pass-2 tile
+//   stats  [B (K+1)]              fp64 p_sum q_sum cache_mass Z, fp32 p_max q_max,
+//                                 int32 p_arg (for outputs the caller leaves NULL)
 struct Layout {
-    size_t cnt1, cnt2, part, topk, seg, stats, total;
-    int nb, Fmax;
-    int64_t part_stride, topk_stride, seg_stride;  // per sequence, in elements
+    size_t part, cand, seg, stats, total;
+    int nt, cap;
 };
 
-int64_t round_elems(int64_t bytes, int64_t elem) { return (int64_t)align_up((size_t)bytes) / elem; }
-
-// Per-sequence regions are padded to whole 256-byte lines: the last block of a
-// sequence reads them, and no cache line is shared between two sequences.
-bool layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
+void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     const int64_t K1 = s->K + 1;
     const int64_t R = (int64_t)s->B * K1;
-    const int nb = ssd::blocks_per_row(s->dtype, s->V);
+    const int nt = ssd::tiles_per_row(s->dtype, s->V);
     const int Fmax = Bf < 1 ? 1 : (Bf > SSD_MAX_F ? SSD_MAX_F : Bf);
-    const int64_t nseq2 = std::max<int64_t>(s->B, (int64_t)s->B * s->K);
-    L->part_stride = round_elems(2 * K1 * nb * (int64_t)sizeof(ssd::RowPartial), sizeof(ssd::RowPartial));
-    L->topk_stride = round_elems(K1 * nb * Fmax * 8, 8);
-    L->seg_stride = round_elems((int64_t)nb * 4 * 16, 16);
+    const int cap = ssd::cand_cap(Fmax);
+    const int64_t groups = std::max<int64_t>(s->B, (int64_t)s->B * s->K);
     size_t off = 0;
-    L->cnt1 = off;
-    L->cnt2 = off + kCounterHalf * 4;
-    off = align_up(kCounterWords * 4);
     L->part = off;
-    off = align_up(off + (size_t)s->B * L->part_stride * sizeof(ssd::RowPartial));
-    L->topk = off;
-    off = align_up(off + (size_t)s->B * L->topk_stride * 8);
+    off = align_up(off + (size_t)R * 2 * nt * sizeof(ssd::WavePartial));
+    L->cand = off;
+    off = align_up(off + (size_t)R * nt * cap * sizeof(uint64_t));
     L->seg = off;
-    off = align_up(off + (size_t)nseq2 * L->seg_stride * 16);
+    off = align_up(off + (size_t)groups * nt * 16);
     L->stats = off;
-    off = align_up(off + (size_t)R * 40);  // p_sum q_sum cache_mass Z (fp64), p_max q_max (fp32), p_arg q_arg
+    off = align_up(off + (size_t)R * (4 * 8 + 2 * 4 + 4));
     L->total = off;
-    L->nb = nb;
-    L->Fmax = Fmax;
-    return true;
+    L->nt = nt;
+    L->cap = cap;
 }
 
 ssd_status fail_hip(hipError_t e, const char* where) {
@@ -70,9 +62,9 @@ ssd_status check_shape(const ssd_shape* s) {
     if (s->B < 1 || s->K < 1 || s->K > SSD_MAX_K || s->V < 2 || s->ld < s->V) return SSD_ERR_ARG;
     if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_ARG;
     if (!std::isfinite(s->T) || s->T < 0.f) return SSD_ERR_ARG;
-    if (s->B > kCounterHalf || (int64_t)s->B * s->K > kCounterHalf) return SSD_ERR_UNSUPPORTED;
-    const int64_t grid = (int64_t)s->B * 2 * (s->K + 1) * ssd::blocks_per_row(s->dtype, s->V);
-    if (grid > 0x7FFFFFFF) return SSD_ERR_UNSUPPORTED;
+    const int64_t nt = ssd::tiles_per_row(s->dtype, s->V);
+    const int64_t grid = (int64_t)s->B * 2 * (s->K + 1) * ((nt + 3) / 4);
+    if (grid > 0x7FFFFFFF || (int64_t)s->B * s->K * ((nt + 3) / 4) > 0x7FFFFFFF) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -124,10 +116,10 @@ void fill_fo(ssd::Pass2Args& a, const int32_t* F, const int* O, int K1) {
 int zeros_F[SSD_MAX_K + 1] = {0};
 
 void set_ws(ssd::Pass1Args& a, void* ws, const Layout& L) {
-    a.part = at<ssd::RowPartial>(ws, L.part);
-    a.part_stride = L.part_stride;
-    a.topk = at<uint64_t>(ws, L.topk);
-    a.topk_stride = L.topk_stride;
+    a.nt = L.nt;
+    a.cap = L.cap;
+    a.part = at<ssd::WavePartial>(ws, L.part);
+    a.cand = at<uint64_t>(ws, L.cand);
 }
 
 }  // namespace
@@ -205,12 +197,9 @@ ssd_status ssd_softmax(const ssd_shape* s, const void* logits, float* row_max, d
     a.c = temp_scale(s->T);
     a.greedy = greedy;
     a.want_arg = greedy || row_argmax != nullptr || probs != nullptr;
-    a.nb = L.nb;
-    a.Fmax = L.Fmax;
     int O[SSD_MAX_K + 2] = {0};
     fill_fo(a, zeros_F, O, K1);
     set_ws(a, ws, L);
-    a.seq_counter = nullptr;
     hipError_t e = ssd::launch_pass1(s->dtype, vec_ok(s, logits), a, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_softmax pass");
     int32_t* argp = row_argmax ? row_argmax : at<int32_t>(ws, L.stats);
@@ -249,8 +238,6 @@ ssd_status ssd_build_cache(const ssd_shape* s, const void* q_logits, const float
     a.c = temp_scale(s->T);
     a.greedy = greedy;
     a.want_arg = 0;
-    a.nb = L.nb;
-    a.Fmax = L.Fmax;
     fill_fo(a, F_host, O, K1);
     set_ws(a, ws, L);
     hipError_t e = ssd::launch_pass1(s->dtype, vec_ok(s, q_logits), a, hs);
@@ -302,7 +289,7 @@ ssd_status ssd_saguaro_reweight(const ssd_shape* s, const double* cache_mass, fl
             a.c = c;
             a.C = C;
             a.mode = 1;
-            a.nb = L.nb;
+            a.nt = L.nt;
             fill_fo(a, F_host, O, K1);
             a.Bf = Bf;
             a.q_max = q_max;
@@ -312,10 +299,10 @@ ssd_status ssd_saguaro_reweight(const ssd_shape* s, const double* cache_mass, fl
             a.seed = rng.seed;
             a.round = rng.round;
             a.seg = at<double2>(ws, L.seg);
-            a.seg_stride = L.seg_stride;
-            a.counter = at<unsigned>(ws, L.cnt2);
             a.out_tok = draft;
-            e = ssd::launch_pass2(s->dtype, vec_ok(s, q_logits), a, s->B * s->K, hs);
+            const bool vec = vec_ok(s, q_logits);
+            e = ssd::launch_pass2(s->dtype, vec, a, s->B * s->K, hs);
+            if (e == hipSuccess) e = ssd::launch_finalize_bonus(s->dtype, vec, a, s->B * s->K, hs);
         }
         if (e != hipSuccess) return fail_hip(e, "ssd_saguaro_reweight draft");
     }
@@ -377,7 +364,7 @@ ssd_status ssd_residual_sample(const ssd_shape* s, const void* p_logits, const v
     a.c = temp_scale(s->T);
     a.C = C;
     a.mode = 0;
-    a.nb = L.nb;
+    a.nt = L.nt;
     fill_fo(a, F_host, O, s->K + 1);
     a.Bf = Bf;
     a.p_max = p_max;
@@ -390,13 +377,13 @@ ssd_status ssd_residual_sample(const ssd_shape* s, const void* p_logits, const v
     a.seed = rng.seed;
     a.round = rng.round;
     a.seg = at<double2>(ws, L.seg);
-    a.seg_stride = L.seg_stride;
-    a.counter = at<unsigned>(ws, L.cnt2);
     a.out_tok = bonus;
     a.resid_mass = resid_mass;
     a.dev_err = dev_err;
     a.do_lookup = 0;
-    e = ssd::launch_pass2(s->dtype, vec_ok(s, p_logits) && vec_ok(s, q_logits), a, s->B, hs);
+    const bool vec = vec_ok(s, p_logits) && vec_ok(s, q_logits);
+    e = ssd::launch_pass2(s->dtype, vec, a, s->B, hs);
+    if (e == hipSuccess) e = ssd::launch_finalize_bonus(s->dtype, vec, a, s->B, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_residual_sample");
     return SSD_OK;
 }
@@ -450,12 +437,24 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     a.c = temp_scale(s->T);
     a.greedy = greedy;
     a.want_arg = greedy || out->p_argmax || out->q_argmax;
-    a.nb = L.nb;
-    a.Fmax = L.Fmax;
     fill_fo(a, F_host, O, K1);
     set_ws(a, ws, L);
-    a.seq_counter = at<unsigned>(ws, L.cnt1);
-    ssd::SeqFinal& f = a.fin;
+
+    ssd::SeqFinal f{};
+    f.part = a.part;
+    f.cand = a.cand;
+    f.p_logits = a.logits[0];
+    f.q_logits = a.logits[1];
+    f.B = s->B;
+    f.K = s->K;
+    f.V = s->V;
+    f.nt = a.nt;
+    f.cap = a.cap;
+    f.ld_bytes = a.ld_bytes;
+    f.c = a.c;
+    f.greedy = greedy;
+    for (int i = 0; i <= ssd::kMaxKc; ++i) f.F[i] = a.F[i];
+    for (int i = 0; i <= ssd::kMaxKc + 1; ++i) f.O[i] = a.O[i];
     f.draft = draft;
     f.C = C;
     f.seed = rng.seed;
@@ -479,6 +478,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     f.slot = out->slot;
     f.fallback_tokens = out->fallback_tokens;
     f.dev_err = out->dev_err;
+
     const bool vec = vec_ok(s, p_logits) && vec_ok(s, q_logits);
     hipError_t e;
     if (ev && ev->pass1_start && (e = hipEventRecord((hipEvent_t)ev->pass1_start, hs)) != hipSuccess)
@@ -487,7 +487,10 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     if (e != hipSuccess) return fail_hip(e, "ssd_round pass 1");
     if (ev && ev->pass1_stop && (e = hipEventRecord((hipEvent_t)ev->pass1_stop, hs)) != hipSuccess)
         return fail_hip(e, "ssd_round event");
+    e = ssd::launch_finalize_seq(s->dtype, f, hs);
+    if (e != hipSuccess) return fail_hip(e, "ssd_round finalise");
     if (greedy) return SSD_OK;
+
     ssd::Pass2Args b{};
     b.p_logits = (const char*)p_logits;
     b.q_logits = (const char*)q_logits;
@@ -498,7 +501,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.c = a.c;
     b.C = C;
     b.mode = 0;
-    b.nb = L.nb;
+    b.nt = L.nt;
     fill_fo(b, F_host, O, K1);
     b.Bf = Bf;
     b.p_max = f.p_max;
@@ -511,8 +514,6 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.seed = rng.seed;
     b.round = rng.round;
     b.seg = at<double2>(ws, L.seg);
-    b.seg_stride = L.seg_stride;
-    b.counter = at<unsigned>(ws, L.cnt2);
     b.out_tok = out->bonus;
     b.resid_mass = out->resid_mass;
     b.dev_err = out->dev_err;
@@ -527,6 +528,8 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     if (e != hipSuccess) return fail_hip(e, "ssd_round pass 2");
     if (ev && ev->pass2_stop && (e = hipEventRecord((hipEvent_t)ev->pass2_stop, hs)) != hipSuccess)
         return fail_hip(e, "ssd_round event");
+    e = ssd::launch_finalize_bonus(s->dtype, vec, b, s->B, hs);
+    if (e != hipSuccess) return fail_hip(e, "ssd_round bonus");
     return SSD_OK;
 }
 

@@ -8,16 +8,49 @@ namespace ssd {
 
 constexpr int kMaxKc = 16;
 
-// Softmax partial of one vocabulary chunk of a row: its maximum m, the lowest id
-// attaining it, and s = sum of 2^{z c - o(m)} over the chunk (o(m) = rint(m c)).
-struct RowPartial {
+// Softmax partial of one wave tile of a row: its maximum m, the lowest id attaining
+// it, s = sum of 2^{z c - o(m)} over the tile (o(m) = rint(m c)), and for draft rows
+// of the cache the tile's candidate threshold (an order key; 0 admits every element)
+// and how many candidate keys it stored.
+struct WavePartial {
     float m;
     int arg;
     double s;
+    uint32_t tau;
+    int ncand;
+    int pad0, pad1;
 };
 
-// Everything the sequence finaliser of the fused vocabulary pass needs.
+struct Pass1Args {
+    const char* logits[2];
+    int nmodel;       // 1, or 2 for the fused round (0 = target p, 1 = draft q)
+    int topf_model;   // model whose rows collect top-F candidates, -1 for none
+    int B, K1, V;
+    int64_t ld_bytes;
+    float c;          // log2(e) / T, 0 when greedy
+    int greedy;
+    int want_arg;
+    int nt;           // wave tiles per row
+    int cap;          // candidate slots per tile
+    int F[kMaxKc + 1];
+    int O[kMaxKc + 2];
+    WavePartial* part;  // [B][nmodel][K1][nt]
+    uint64_t* cand;     // [B][K1][nt][cap]
+};
+
+// Per-sequence finalisation of the vocabulary pass: row statistics, speculation
+// cache, Saguaro normalisers and verification (and, at T = 0, bonus and lookup).
 struct SeqFinal {
+    const WavePartial* part;
+    const uint64_t* cand;
+    const char* p_logits;
+    const char* q_logits;
+    int B, K, V, nt, cap;
+    int64_t ld_bytes;
+    float c;
+    int greedy;
+    int F[kMaxKc + 1];
+    int O[kMaxKc + 2];
     const int32_t* draft;  // [B, K]
     float C;
     uint64_t seed, round;
@@ -42,27 +75,6 @@ struct SeqFinal {
     int32_t* dev_err;     // nullable
 };
 
-struct Pass1Args {
-    const char* logits[2];
-    int nmodel;       // 1, or 2 for the fused round (0 = target p, 1 = draft q)
-    int topf_model;   // model whose rows build top-F lists, -1 for none
-    int B, K1, V;
-    int64_t ld_bytes;
-    float c;          // log2(e) / T, 0 when greedy
-    int greedy;
-    int want_arg;
-    int nb;           // blocks per row
-    int F[kMaxKc + 1];
-    int O[kMaxKc + 2];
-    int Fmax;         // slots per block list
-    RowPartial* part;  // per sequence: [nmodel][K1][nb], sequence stride part_stride
-    int64_t part_stride;
-    uint64_t* topk;    // per sequence: [K1][nb][Fmax], sequence stride topk_stride
-    int64_t topk_stride;
-    unsigned* seq_counter;  // non-null: fused round with a per-sequence finaliser
-    SeqFinal fin;
-};
-
 struct Pass2Args {
     const char* p_logits;
     const char* q_logits;
@@ -71,7 +83,7 @@ struct Pass2Args {
     float c;
     float C;
     int mode;         // 0: bonus from the residual (per sequence); 1: draft tokens from q' (per (b, i))
-    int nb;
+    int nt;
     int F[kMaxKc + 1];
     int O[kMaxKc + 2];
     int Bf;
@@ -83,9 +95,7 @@ struct Pass2Args {
     const int32_t* cache_ids;
     const int32_t* accept_len;
     uint64_t seed, round;
-    double2* seg;       // per group: [nb * waves] (weight sum, target-law sum), group stride seg_stride
-    int64_t seg_stride;
-    unsigned* counter;  // [groups]
+    double2* seg;       // [groups][nt] (weight sum, target-law sum) per wave tile
     int32_t* out_tok;   // bonus [B] or draft [B, K]
     double* resid_mass; // nullable
     int32_t* dev_err;   // nullable
@@ -96,11 +106,14 @@ struct Pass2Args {
     int32_t* fallback_tokens;
 };
 
-int chunk_elems(int dtype);
-int blocks_per_row(int dtype, int V);
+int tile_elems(int dtype);
+int tiles_per_row(int dtype, int V);
+int cand_cap(int Fmax);
 
 hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st);
-hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int nseq, hipStream_t st);
+hipError_t launch_finalize_seq(int dtype, const SeqFinal& f, hipStream_t st);
+hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st);
+hipError_t launch_finalize_bonus(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st);
 hipError_t launch_combine_stats(const Pass1Args& a, float* m, double* s, int32_t* arg, hipStream_t st);
 hipError_t launch_combine_topf(const Pass1Args& a, int Bf, const float* q_max, const double* q_sum,
                                int32_t* cache_ids, double* cache_mass, hipStream_t st);

@@ -1,40 +1,44 @@
 // ssd_kernels.hip -- gfx950 kernels of the verify-and-pre-speculate round of
 // Speculative Speculative Decoding with the Saguaro algorithm.
 //
-// Data flow of one round (two streaming kernels):
-//  pass 1  every row of the target and draft logits [B, K+1, V] is read once.  Each
-//          256-thread block (4 wave64s) owns one vocabulary chunk of one row; each
-//          lane keeps 8 x 16-byte vectors in registers.  Per chunk it computes the
-//          softmax partial (max, sum of 2^{z c - o}), the lowest-id argmax, and for
-//          draft rows the chunk's exact top-F keys (wave radix select on lane maxima,
-//          LDS candidate staging, wave radix select of the top F).  The last block of
-//          a sequence (completion counter) merges its rows: softmax statistics, cache
-//          ids S_k (sorted, ties to the lower id), M_k, the Saguaro normaliser Z_k and
-//          the lossless verification of the K draft tokens.
-//  pass 2  only the rows the bonus needs (target row k, plus draft row k when k < K)
-//          are read again.  Each block sums the residual max(p - q', 0) per wave
-//          segment of its chunk; the last block of the sequence locates the segment
-//          where the running sum crosses u * sum, rescans that segment to find the
-//          bonus id, and performs the cache lookup.
+// One round is four kernels; the two streaming ones carry all the bytes:
+//  pass 1      every row of the target and draft logits [B, K+1, V] is read once.  The
+//              unit of work is one wave64 and one tile of 8 x 16-byte vectors per
+//              lane (4096 bf16 / 2048 fp32 elements); waves never wait for each
+//              other.  Per tile: the softmax partial (max, sum of 2^{z c - o}), the
+//              lowest-id argmax and, for draft rows of the cache, every element at
+//              or above the F-th largest lane maximum of the tile (a lower bound of
+//              the tile's F-th largest value) as a candidate key.
+//  finalise    one block per sequence merges its rows: softmax statistics, cache ids
+//              S_k (top F_k draft ids, ties to the lower id), M_k, the Saguaro
+//              normaliser Z_k, and the lossless verification of the K draft tokens.
+//  pass 2      only the rows the bonus needs (target row k, plus draft row k when
+//              k < K) are read again; each wave sums the residual max(p - q', 0) of
+//              its tile.
+//  bonus       one wave per sequence locates the tile where the running sum crosses
+//              u * sum, rescans that tile for the bonus id and does the cache lookup.
 // Normalisers, cached masses, Z and every running sum that decides an integer are
-// kept in fp64; per-element terms are fp32 exp2 of an exactly formed exponent.
-// The separate C-ABI calls reuse the same device code, so their results are
+// kept in fp64; per-element terms are fp32 exp2 of an exactly formed exponent.  The
+// separate C-ABI calls reuse the same device code, so their results are
 // bit-identical to the fused round.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace ssd {
 
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4 };
+constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
 
-int chunk_elems(int dtype) { return dtype == 1 ? kChunk<1> : kChunk<0>; }
-int blocks_per_row(int dtype, int V) {
-    const int c = chunk_elems(dtype);
-    return (V + c - 1) / c;
+int tile_elems(int dtype) { return dtype == 1 ? kTile<1> : kTile<0>; }
+int tiles_per_row(int dtype, int V) {
+    const int t = tile_elems(dtype);
+    return (V + t - 1) / t;
 }
+int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }
 
 // ============================================================================ shared pieces
 // Row normalisation from the exchanged statistics (row max m, row sum
@@ -55,114 +59,8 @@ __device__ __forceinline__ RowNorm row_norm(float m, double s_std, float c) {
     r.inv = offset_factor(m, c, r.o) / s_std;
     return r;
 }
-// Standard row sum from a sum relative to o(m).
 __device__ __forceinline__ double std_sum(float m, double s_rel, float c) {
     return s_rel * offset_factor(m, c, offset_of(m, c));
-}
-
-__device__ __forceinline__ void publish_partial(RowPartial* p, float m, int arg, double s) {
-    const uint64_t w = (uint64_t)__float_as_uint(m) | ((uint64_t)(uint32_t)arg << 32);
-    publish(reinterpret_cast<uint64_t*>(p), w);
-    publish(&p->s, s);
-}
-__device__ __forceinline__ RowPartial observe_partial(const RowPartial* p) {
-    const uint64_t w = observe(reinterpret_cast<const uint64_t*>(p));
-    RowPartial r;
-    r.m = __uint_as_float((uint32_t)w);
-    r.arg = (int)(uint32_t)(w >> 32);
-    r.s = observe(&p->s);
-    return r;
-}
-
-// Softmax statistics of a row from its per-chunk partials, merged in chunk order.
-// Returns the sum relative to o(m).
-__device__ inline void combine_partials(const RowPartial* P, int nb, float c, float& m, double& s, int& arg) {
-    RowPartial q = observe_partial(P);
-    m = q.m;
-    s = q.s;
-    arg = q.arg;
-    for (int j = 1; j < nb; ++j) {
-        q = observe_partial(P + j);
-        if (q.m > m || (q.m == m && q.arg < arg)) arg = q.arg;
-        merge_partial(m, s, q.m, q.s, c);
-    }
-}
-
-// Cache lookup of one verified outcome (k, tok) by one wave, plus the uniform
-// fallback draft on a miss.
-__device__ inline void lookup_wave(int b, int K, int V, int k, int tok, const int* F, const int* O, int Bf,
-                                   const int32_t* cache_ids, int fallback, uint64_t seed, uint64_t round,
-                                   uint8_t* hit, int32_t* slot, int32_t* fb) {
-    const int lane = lane_id();
-    bool match = false;
-    int Ok = 0;
-    if (k >= 0 && k <= K) {
-        Ok = O[k];
-        if (lane < F[k]) match = cache_ids[(int64_t)b * Bf + Ok + lane] == tok;
-    }
-    const uint64_t mk = __ballot(match);
-    const bool h = mk != 0ull;
-    if (lane == 0) {
-        hit[b] = h ? 1 : 0;
-        slot[b] = h ? Ok + (__ffsll((long long)mk) - 1) : -1;
-    }
-    for (int j = lane; j < K; j += kWave) {
-        int32_t t = -1;
-        if (!h && fallback) {
-            const uint64_t u32 = philox_u32(seed, round, kPurposeFallback, (uint64_t)b, (uint64_t)j);
-            t = (int32_t)((u32 * (uint64_t)V) >> 32);
-        }
-        fb[(int64_t)b * K + j] = t;
-    }
-}
-
-// Verification of the K draft tokens of sequence b by one wave: lane i < K tests
-// position i with that position's row statistics.  Returns the accepted length k
-// (same in every lane); writes accept_prob and the OR of the error bits to *errs.
-template <int DT>
-__device__ inline int verify_wave(int b, int K, int V, const char* p_row_i, const char* q_row_i, int d, float mp,
-                                  double sp, int argp, float mq, double sq, double Zi, bool in_cache, float C, float c,
-                                  int greedy, uint64_t seed, uint64_t round, float* accept_prob, int* errs) {
-    const int i = lane_id();
-    const bool act = i < K;
-    int err = 0;
-    bool ok = act;
-    double ratio = 0.0;
-    if (act && (d < 0 || d >= V)) {
-        err |= kErrTokenRange;
-        ok = false;
-    }
-    if (ok) {
-        if (greedy) {
-            ratio = (d == argp) ? 1.0 : 0.0;
-        } else {
-            const RowNorm np = row_norm(mp, sp, c), nq = row_norm(mq, sq, c);
-            const double p = (double)term(load_one<DT>(p_row_i, d), c, np.o) * np.inv;
-            const double q = (double)term(load_one<DT>(q_row_i, d), c, nq.o) * nq.inv;
-            const double qp = q * (in_cache ? (double)C : 1.0) / Zi;
-            if (!(qp > 0.0)) {
-                err |= kErrQprimeZero;
-                ok = false;
-            } else {
-                ratio = p / qp;
-            }
-        }
-    }
-    bool acc = false;
-    if (ok) {
-        if (greedy)
-            acc = ratio == 1.0;
-        else
-            acc = (double)philox_uniform(seed, round, kPurposeAccept, (uint64_t)b, (uint64_t)i) < ratio;
-    }
-    const uint64_t rej = __ballot(act && !acc);
-    const int k = rej ? (__ffsll((long long)rej) - 1) : K;
-    if (act && accept_prob) accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
-    int e = err;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) e |= __shfl_xor(e, m, kWave);
-    *errs = e;
-    return k;
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -171,47 +69,231 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Merges nb per-chunk lists of F keys (Fmax slots each, 0 = empty) into the row's
-// top F, returned sorted: lane j holds the j-th largest key (0 past the end).
-// xchg: 64 uint64 of LDS private to the calling wave.
-__device__ inline uint64_t merge_topf(const uint64_t* lists, int nb, int Fmax, int F, uint64_t* xchg) {
-    const int lane = lane_id();
-    constexpr int KR = 4;
-    uint64_t keep = 0ull;
-    const int per_batch = ((KR - 1) * kWave) / F;
-    for (int l0 = 0; l0 < nb; l0 += per_batch) {
-        const int l1 = min(nb, l0 + per_batch);
-        const int n = (l1 - l0) * F;
-        uint64_t k[KR];
-        k[0] = keep;
-#pragma unroll
-        for (int s = 1; s < KR; ++s) {
-            const int idx = (s - 1) * kWave + lane;
-            k[s] = idx < n ? observe(lists + (int64_t)(l0 + idx / F) * Fmax + idx % F) : 0ull;
-        }
-        const uint64_t T = wave_select_regs<KR>(k, F);
-        int written = 0;
-#pragma unroll
-        for (int s = 0; s < KR; ++s) {
-            const bool take = k[s] != 0ull && k[s] >= T;
-            const int pos = written + lanes_below(take);
-            if (take && pos < kWave) xchg[pos] = k[s];
-            written += wave_popc(take);
-        }
-        wave_sync_lds();
-        keep = lane < min(written, F) ? xchg[lane] : 0ull;
-        wave_sync_lds();
-    }
-    return wave_sort_desc(keep);
+// (max, lowest-id argmax, sum relative to o(max)) merge; symmetric bit for bit.
+__device__ __forceinline__ void merge_stats(float& m, double& s, int& arg, float m2, double s2, int a2, float c) {
+    if (m2 > m || (m2 == m && a2 < arg)) arg = a2;
+    merge_partial(m, s, m2, s2, c);
 }
 
-// Cache keys, cached mass M = sum q(x) over them of one draft row, by one wave.
-// Writes the sorted ids to ids_out[0..F) (and ids_lds if given).
-__device__ inline double cache_row(const uint64_t* lists, int nb, int Fmax, int F, float mq, double sq, float c,
-                                   int greedy, int32_t* ids_out, int* ids_lds, uint64_t* xchg) {
+// Softmax statistics of one row from its nt tile partials, by one wave in a fixed
+// order (lane-sequential, then a butterfly); every lane returns the same values.
+__device__ inline void row_stats_wave(const WavePartial* P, int nt, float c, float& m, double& s, int& arg) {
+    const int lane = lane_id();
+    m = -INFINITY;
+    s = 0.0;
+    arg = INT_MAX;
+    for (int t = lane; t < nt; t += kWave) {
+        const WavePartial q = P[t];
+        merge_stats(m, s, arg, q.m, q.s, q.arg, c);
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m, off, kWave);
+        const double s2 = __shfl_xor(s, off, kWave);
+        const int a2 = __shfl_xor(arg, off, kWave);
+        merge_stats(m, s, arg, m2, s2, a2, c);
+    }
+}
+
+// Merge of the candidates of one draft row by one wave.  Candidate (tile t, slot s)
+// is gathered by lane (s*nt + t) mod 64 into register u = (s*nt + t) / 64, so every
+// load address is known up front and all loads of a row are in flight together.
+constexpr int kCandRegs = 24;    // register slots per lane: up to 1536 candidates per row
+constexpr int kMaxMergeTiles = 512;
+
+struct TopfScratch {
+    uint64_t surv[kSurvivorCap];  // keys at or above the value threshold
+    uint64_t rank[kWave];         // the top F, placed by rank
+    uint8_t nc[kMaxMergeTiles];   // candidates per tile
+};
+
+// The largest 32-bit value part T such that at least F of the nonzero keys have a
+// value part >= T (the F-th largest value, ties counted), by the same radix select as
+// wave_select_regs restricted to the value bits; 0 when there are at most F keys.
+template <int KREG>
+__device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int F) {
+    int n = 0;
+    uint32_t orv = 0u, andv = ~0u;
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) {
+        n += wave_popc(k[u] != 0ull);
+        if (k[u] != 0ull) {
+            orv |= (uint32_t)(k[u] >> 32);
+            andv &= (uint32_t)(k[u] >> 32);
+        }
+    }
+    if (n <= F) return 0u;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
+        andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
+    }
+    uint32_t diff = orv ^ andv;
+    uint32_t T = andv & ~diff;
+    while (diff) {
+        const int bit = 31 - __clz(diff);
+        diff &= ~(1u << bit);
+        const uint64_t cand = (uint64_t)(T | (1u << bit)) << 32;
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < KREG; ++u) cnt += wave_popc(k[u] >= cand);
+        if (cnt >= F) T |= 1u << bit;
+    }
+    return T;
+}
+
+// Sorts the n <= kSurvivorCap distinct keys in sc.surv by rank and returns lane j =
+// the j-th largest (0 past min(n, F)).
+__device__ inline uint64_t rank_sort_lds(TopfScratch& sc, int n, int F) {
+    const int lane = lane_id();
+    uint64_t k[4];
+    int rank[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = u * kWave + lane;
+        k[u] = j < n ? sc.surv[j] : 0ull;
+        rank[u] = 0;
+    }
+    if (n <= kWave) {
+        for (int v = 0; v < n; ++v) rank[0] += sc.surv[v] > k[0];
+    } else {
+        for (int v = 0; v < n; ++v) {
+            const uint64_t x = sc.surv[v];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rank[u] += x > k[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        if (k[u] != 0ull && rank[u] < F) sc.rank[rank[u]] = k[u];
+    wave_sync_lds();
+    const uint64_t key = lane < min(n, F) ? sc.rank[lane] : 0ull;
+    wave_sync_lds();
+    return key;
+}
+
+// Appends the keys of k[] that satisfy keep (in register, then lane order) to sc.surv;
+// returns the count (keys past kSurvivorCap are counted, not stored).
+template <int KREG>
+__device__ inline int compact_keys(TopfScratch& sc, const uint64_t (&k)[KREG], uint64_t lo) {
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) {
+        const bool keep = k[u] != 0ull && k[u] >= lo;
+        const int pos = n + lanes_below(keep);
+        if (keep && pos < kSurvivorCap) sc.surv[pos] = k[u];
+        n += wave_popc(keep);
+    }
+    wave_sync_lds();
+    return n;
+}
+
+// Candidate key number j of a 64-tile chunk (flattened in tile order) of a row: the
+// tile is the last one whose first slot is <= j.  start: the chunk's first slots, in
+// sc.surv reinterpreted (slow path only).
+__device__ __forceinline__ uint64_t chunk_key(const uint64_t* cand, int cap, int c0, const int* start, int j) {
+    int lo = 0;
+#pragma unroll
+    for (int step = 32; step >= 1; step >>= 1)
+        if (start[lo + step] <= j) lo += step;
+    return cand[(int64_t)(c0 + lo) * cap + (j - start[lo])];
+}
+
+// Top F of one draft row from its tiles' candidate keys, by one wave.  The largest
+// tile threshold bounds the row's F-th largest value from below (that tile alone has
+// F elements at or above it), so only keys at or above it can be in the row's top F,
+// and every such key is in its tile's list.  Keys are distinct (they carry the id).
+// Returns lane j = the j-th largest key (0 past F).
+__device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F,
+                                         TopfScratch& sc) {
+    const int lane = lane_id();
+    uint32_t tr = 0u;
+    int max_nc = 0;
+    for (int t = lane; t < nt; t += kWave) {
+        const WavePartial q = P[t];
+        tr = max(tr, q.tau);
+        max_nc = max(max_nc, q.ncand);
+        if (t < kMaxMergeTiles) sc.nc[t] = (uint8_t)q.ncand;
+    }
+    tr = wave_max_u32(tr);
+    max_nc = (int)wave_max_u32((uint32_t)max_nc);
+    const uint64_t floor_key = (uint64_t)tr << 32;
+    wave_sync_lds();
+    const int U = (int)(((int64_t)nt * max_nc + kWave - 1) / kWave);
+
+    if (nt <= kMaxMergeTiles && U <= kCandRegs) {
+        uint64_t k[kCandRegs];
+        int t = lane % nt, sl = lane / nt;
+        // opaque to the optimiser: keeps the 24 slot addresses from being hoisted out of
+        // a caller's loop over rows (they would stay live in registers across it)
+        __asm__ volatile("" : "+v"(t), "+v"(sl));
+        const int dt = kWave % nt, ds = kWave / nt;
+#pragma unroll
+        for (int u = 0; u < kCandRegs; ++u) {
+            uint64_t x = 0ull;
+            if (u < U && sl < (int)sc.nc[t]) x = cand[(int64_t)t * cap + sl];
+            k[u] = x >= floor_key ? x : 0ull;
+            t += dt;
+            sl += ds;
+            if (t >= nt) {
+                t -= nt;
+                ++sl;
+            }
+        }
+        const uint32_t T = wave_select_value<kCandRegs>(k, F);
+        const uint64_t lo = (uint64_t)T << 32;
+        int n = compact_keys<kCandRegs>(sc, k, lo);
+        if (n > kSurvivorCap) {
+            // many keys tie at the threshold value: select on the whole key
+#pragma unroll
+            for (int u = 0; u < kCandRegs; ++u) k[u] = k[u] >= lo ? k[u] : 0ull;
+            const uint64_t T64 = wave_select_regs<kCandRegs>(k, F);
+            n = compact_keys<kCandRegs>(sc, k, T64);
+        }
+        return rank_sort_lds(sc, n, F);
+    }
+
+    // Rows with more candidates than register slots: exact selection by F rounds of a
+    // wave maximum below the previous key.
+    int* start = reinterpret_cast<int*>(sc.surv);
+    uint64_t key = 0ull, prev = ~0ull;
+    for (int r = 0; r < F; ++r) {
+        uint64_t best = 0ull;
+        for (int c0 = 0; c0 < nt; c0 += kWave) {
+            const int nc = c0 + lane < nt ? P[c0 + lane].ncand : 0;
+            int incl = nc;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int y = __shfl_up(incl, off, kWave);
+                if (lane >= off) incl += y;
+            }
+            const int tot = __shfl(incl, kWave - 1, kWave);
+            start[lane] = incl - nc;
+            wave_sync_lds();
+            for (int j = lane; j < tot; j += kWave) {
+                const uint64_t x = chunk_key(cand, cap, c0, start, j);
+                if (x >= floor_key && x < prev && x > best) best = x;
+            }
+            wave_sync_lds();
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = __shfl_xor(best, off, kWave);
+            best = o > best ? o : best;
+        }
+        if (lane == r) key = best;
+        prev = best;
+    }
+    return key;
+}
+
+// Cache ids (sorted) and cached mass M = sum of q(x) over them, of one draft row.
+__device__ __forceinline__ double cache_row_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F, float mq,
+                                        double sq, float c, int greedy, int32_t* ids_out, int* ids_lds,
+                                        TopfScratch& sc) {
     const int lane = lane_id();
     if (F <= 0) return 0.0;
-    const uint64_t key = merge_topf(lists, nb, Fmax, F, xchg);
+    const uint64_t key = row_topf_wave(P, cand, nt, cap, F, sc);
     const int id = key ? (int)key_id(key) : -1;
     if (lane < F) {
         ids_out[lane] = id;
@@ -231,120 +313,126 @@ __device__ inline double cache_row(const uint64_t* lists, int nb, int Fmax, int 
     return t;
 }
 
-// ============================================================================ pass 1
-struct FinShared {
-    float m[2][kMaxK + 1];
-    double s[2][kMaxK + 1];
-    int arg[2][kMaxK + 1];
-    double Z[kMaxK + 1];
-    int ids[kMaxK + 1][kMaxF];
-    uint64_t xchg[kWavesPerBlock][kWave];
-};
-
-template <int DT>
-__device__ void finalize_sequence(const Pass1Args& a, int b, FinShared& fs) {
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int K1 = a.K1, K = K1 - 1;
-    const SeqFinal& f = a.fin;
-    const RowPartial* part = a.part + (int64_t)b * a.part_stride;
-    const uint64_t* topk = a.topk + (int64_t)b * a.topk_stride;
-
-    // row statistics of both models
-    if (tid < 2 * K1) {
-        const int model = tid / K1, i = tid % K1;
-        const int64_t r = (int64_t)b * K1 + i;
-        float m;
-        double s;
-        int arg;
-        combine_partials(part + (int64_t)(model * K1 + i) * a.nb, a.nb, a.c, m, s, arg);
-        s = a.greedy ? 1.0 : std_sum(m, s, a.c);
-        fs.m[model][i] = m;
-        fs.s[model][i] = s;
-        fs.arg[model][i] = arg;
-        if (model) {
-            f.q_max[r] = m;
-            f.q_sum[r] = s;
-            if (f.q_arg) f.q_arg[r] = arg;
-        } else {
-            f.p_max[r] = m;
-            f.p_sum[r] = s;
-            if (f.p_arg) f.p_arg[r] = arg;
-        }
-    }
-    __syncthreads();
-
-    // speculation cache per acceptance length, cached mass and Saguaro normaliser
-    for (int i = wave; i < K1; i += kWavesPerBlock) {
-        const int64_t r = (int64_t)b * K1 + i;
-        const double M = cache_row(topk + (int64_t)i * a.nb * a.Fmax, a.nb, a.Fmax, a.F[i], fs.m[1][i], fs.s[1][i],
-                                   a.c, a.greedy, f.cache_ids + (int64_t)b * f.Bf + a.O[i], fs.ids[i], fs.xchg[wave]);
-        const double Z = 1.0 - (1.0 - (double)f.C) * M;
-        if (lane == 0) {
-            f.cache_mass[r] = M;
-            f.Z[r] = Z;
-            fs.Z[i] = Z;
-        }
-    }
-    __syncthreads();
-
-    if (wave != 0) return;
-    const int i = lane;
-    const bool act = i < K;
-    const int ic = act ? i : 0;
-    const int64_t ri = (int64_t)b * K1 + ic;
-    const int d = act ? f.draft[(int64_t)b * K + i] : 0;
-    bool in_cache = false;
-    for (int j = 0; j < a.F[ic]; ++j) in_cache |= fs.ids[ic][j] == d;
-    int errs;
-    const int k = verify_wave<DT>(b, K, a.V, a.logits[0] + ri * a.ld_bytes, a.logits[1] + ri * a.ld_bytes, d,
-                                  fs.m[0][ic], fs.s[0][ic], fs.arg[0][ic], fs.m[1][ic], fs.s[1][ic], fs.Z[ic],
-                                  in_cache, f.C, a.c, a.greedy, f.seed, f.round, f.accept_prob, &errs);
+// Cache lookup of one verified outcome (k, tok) by one wave, plus the uniform
+// fallback draft on a miss.  my_id: lane j < F_k holds the j-th cached id of outcome
+// k (slot O_k + j); other lanes, and every lane when k is invalid (k < 0), hold -1.
+__device__ inline void lookup_wave(int b, int K, int V, int k, int Ok, int my_id, int tok, int fallback,
+                                   uint64_t seed, uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fb) {
+    const int lane = lane_id();
+    const uint64_t mk = __ballot(k >= 0 && my_id >= 0 && my_id == tok);
+    const bool h = mk != 0ull;
     if (lane == 0) {
-        f.accept_len[b] = k;
-        if (f.dev_err && errs) f.dev_err[b] |= errs;
+        hit[b] = h ? 1 : 0;
+        slot[b] = h ? Ok + (__ffsll((long long)mk) - 1) : -1;
     }
-    if (a.greedy) {
-        const int tok = fs.arg[0][k];
-        if (lane == 0) {
-            f.bonus[b] = tok;
-            if (f.resid_mass) f.resid_mass[b] = 1.0;
+    for (int j = lane; j < K; j += kWave) {
+        int32_t t = -1;
+        if (!h && fallback) {
+            const uint64_t u32 = philox_u32(seed, round, kPurposeFallback, (uint64_t)b, (uint64_t)j);
+            t = (int32_t)((u32 * (uint64_t)V) >> 32);
         }
-        lookup_wave(b, K, a.V, k, tok, a.F, a.O, f.Bf, f.cache_ids, f.fallback, f.seed, f.round, f.hit, f.slot,
-                    f.fallback_tokens);
+        fb[(int64_t)b * K + j] = t;
     }
 }
 
+// The cached id of lane j of outcome k of sequence b (-1 past F_k or for k invalid).
+__device__ __forceinline__ int cached_id(const int32_t* cache_ids, int b, int Bf, int k, int K, const int* F,
+                                         const int* O) {
+    const int lane = lane_id();
+    if (k < 0 || k > K || lane >= F[k]) return -1;
+    return cache_ids[(int64_t)b * Bf + O[k] + lane];
+}
+
+// What lane i < K needs to test draft token d_i, loaded ahead of the row statistics:
+// the token, both models' logits at it (when d_i is in range and T > 0) and the
+// acceptance uniform.
+struct DraftProbe {
+    int d;
+    float zp, zq;
+    float u;
+};
+
+template <int DT>
+__device__ inline DraftProbe probe_draft(const int32_t* draft, const char* p_logits, const char* q_logits,
+                                         int64_t ld_bytes, int b, int K, int V, int greedy, uint64_t seed,
+                                         uint64_t round) {
+    const int i = lane_id();
+    DraftProbe pr;
+    pr.d = i < K ? draft[(int64_t)b * K + i] : 0;
+    pr.zp = pr.zq = 0.f;
+    if (i < K && !greedy && pr.d >= 0 && pr.d < V) {
+        const int64_t r = (int64_t)b * (K + 1) + i;
+        pr.zp = load_one<DT>(p_logits + r * ld_bytes, pr.d);
+        pr.zq = load_one<DT>(q_logits + r * ld_bytes, pr.d);
+    }
+    pr.u = (i < K && !greedy) ? philox_uniform(seed, round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
+    return pr;
+}
+
+// Verification of the K draft tokens of sequence b by one wave: lane i < K tests
+// position i with that position's row statistics.  Returns the accepted length k
+// (same in every lane); writes accept_prob and the OR of the error bits to *errs.
+__device__ inline int verify_wave(int b, int K, int V, const DraftProbe& pr, float mp, double sp, int argp, float mq,
+                                  double sq, double Zi, bool in_cache, float C, float c, int greedy,
+                                  float* accept_prob, int* errs) {
+    const int i = lane_id();
+    const bool act = i < K;
+    const int d = pr.d;
+    int err = 0;
+    bool ok = act;
+    double ratio = 0.0;
+    if (act && (d < 0 || d >= V)) {
+        err |= kErrTokenRange;
+        ok = false;
+    }
+    if (ok) {
+        if (greedy) {
+            ratio = (d == argp) ? 1.0 : 0.0;
+        } else {
+            const RowNorm np = row_norm(mp, sp, c), nq = row_norm(mq, sq, c);
+            const double p = (double)term(pr.zp, c, np.o) * np.inv;
+            const double q = (double)term(pr.zq, c, nq.o) * nq.inv;
+            const double qp = q * (in_cache ? (double)C : 1.0) / Zi;
+            if (!(qp > 0.0)) {
+                err |= kErrQprimeZero;
+                ok = false;
+            } else {
+                ratio = p / qp;
+            }
+        }
+    }
+    bool acc = false;
+    if (ok) acc = greedy ? ratio == 1.0 : (double)pr.u < ratio;
+    const uint64_t rej = __ballot(act && !acc);
+    const int k = rej ? (__ffsll((long long)rej) - 1) : K;
+    if (act && accept_prob) accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
+    int e = err;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) e |= __shfl_xor(e, m, kWave);
+    *errs = e;
+    return k;
+}
+
+// ============================================================================ pass 1
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     constexpr int N = ElemTraits<DT>::kPerVec;
-    __shared__ float sh_m[kWavesPerBlock];
-    __shared__ double sh_s[kWavesPerBlock];
-    __shared__ int sh_a[kWavesPerBlock];
-    __shared__ uint64_t sh_best[kWavesPerBlock];
-    __shared__ uint64_t sh_cand[kWavesPerBlock * kCandCap];
-    __shared__ int sh_ncand;
-    __shared__ int sh_overflow;
-    __shared__ int sh_last;
-    __shared__ FinShared fs;
-
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
     int bid = blockIdx.x;
-    const int blk = bid % a.nb;
-    bid /= a.nb;
+    const int blk = bid % nblk;
+    bid /= nblk;
     const int i = bid % a.K1;
     bid /= a.K1;
     const int model = bid % a.nmodel;
     const int b = bid / a.nmodel;
+    const int t = blk * kWavesPerBlock + wave;
+    if (t >= a.nt) return;
     const int64_t r = (int64_t)b * a.K1 + i;
     const char* row = a.logits[model] + r * a.ld_bytes;
-    const int64_t tile0 = (int64_t)blk * kChunk<DT> + (int64_t)wave * kTile<DT>;
+    const int64_t tile0 = (int64_t)t * kTile<DT>;
     const int V = a.V;
     const float c = a.c;
-
-    if (tid == 0) {
-        sh_ncand = 0;
-        sh_overflow = 0;
-    }
 
     float x[kVecPerLane][N];
     {
@@ -354,11 +442,12 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         for (int j = 0; j < kVecPerLane; ++j) unpack_vec<DT>(raw[j], x[j]);
     }
 
-    float m_lane = -INFINITY;
+    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kVecPerLane; ++j)
 #pragma unroll
-        for (int e = 0; e < N; ++e) m_lane = fmaxf(m_lane, x[j][e]);
+        for (int e = 0; e < N; ++e) m = fmaxf(m, x[j][e]);
+    const float m_lane = m;
 
     int arg = INT_MAX;
     if (a.want_arg) {
@@ -377,14 +466,14 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         float vs[kVecPerLane];
 #pragma unroll
         for (int j = 0; j < kVecPerLane; ++j) {
-            float t[N];
+            float tt[N];
 #pragma unroll
-            for (int e = 0; e < N; ++e) t[e] = term(x[j][e], c, o);
+            for (int e = 0; e < N; ++e) tt[e] = term(x[j][e], c, o);
 #pragma unroll
             for (int w = N / 2; w >= 1; w >>= 1)
 #pragma unroll
-                for (int e = 0; e < w; ++e) t[e] += t[e + w];
-            vs[j] = t[0];
+                for (int e = 0; e < w; ++e) tt[e] += tt[e + w];
+            vs[j] = tt[0];
         }
 #pragma unroll
         for (int w = kVecPerLane / 2; w >= 1; w >>= 1)
@@ -393,22 +482,25 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         s = (double)vs[0];
     }
 
-    // ---- top-F candidates of this wave's tile (draft rows of the cache): the F-th
-    // largest lane maximum bounds the tile's top F from below.
+    // ---- candidate keys of this tile (draft rows of the cache): every element at or
+    // above the F-th largest lane maximum.
     const int F = a.F[i];
-    const bool do_topf = (model == a.topf_model) && F > 0;
-    if (do_topf) {
+    uint32_t tau = 0u;
+    int ncand = 0;
+    if (model == a.topf_model && F > 0) {
         const bool lane_valid = tile0 + (int64_t)lane * N < V;
-        const uint32_t tau = wave_select_u32(lane_valid ? ord32(m_lane) : 0u, F);
+        tau = wave_select_u32(lane_valid ? ord32(m_lane) : 0u, F);
         const float tauf = tau ? unord32(tau) : -INFINITY;
         const int id0 = (int)tile0 + lane * N;
+        const bool full = tile0 + kTile<DT> <= V;
         uint32_t mask[kVecPerLane];
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < kVecPerLane; ++j) {
             uint32_t mk = 0u;
 #pragma unroll
-            for (int e = 0; e < N; ++e) mk |= (x[j][e] >= tauf && id0 + j * kWave * N + e < V) ? (1u << e) : 0u;
+            for (int e = 0; e < N; ++e)
+                mk |= (x[j][e] >= tauf && (full || id0 + j * kWave * N + e < V)) ? (1u << e) : 0u;
             mask[j] = mk;
             cnt += __popc(mk);
         }
@@ -419,13 +511,9 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             if (lane >= off) incl += y;
         }
         const int tot = __shfl(incl, kWave - 1, kWave);
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&sh_ncand, tot);
-        base = __shfl(base, 0, kWave);
-        if (base + tot > kWavesPerBlock * kCandCap) {
-            if (lane == 0) sh_overflow = 1;
-        } else if (cnt) {
-            int pos = base + incl - cnt;
+        uint64_t* out = a.cand + ((r * a.nt) + t) * a.cap;
+        if (tot <= a.cap) {
+            int pos = incl - cnt;
 #pragma unroll
             for (int j = 0; j < kVecPerLane; ++j) {
                 uint32_t mk = mask[j];
@@ -435,52 +523,16 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                     float v = x[j][0];
 #pragma unroll
                     for (int q = 1; q < N; ++q) v = (e == q) ? x[j][q] : v;
-                    sh_cand[pos++] = cand_key(v, (uint32_t)(id0 + j * kWave * N + e));
+                    out[pos++] = cand_key(v, (uint32_t)(id0 + j * kWave * N + e));
                 }
             }
-        }
-    }
-
-    // ---- wave partial
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m_lane, off, kWave);
-        const double s2 = __shfl_xor(s, off, kWave);
-        const int a2 = __shfl_xor(arg, off, kWave);
-        if (m2 > m_lane || (m2 == m_lane && a2 < arg)) arg = a2;
-        merge_partial(m_lane, s, m2, s2, c);
-    }
-    if (lane == 0) {
-        sh_m[wave] = m_lane;
-        sh_s[wave] = s;
-        sh_a[wave] = arg;
-    }
-    __syncthreads();
-
-    uint64_t* out_list = a.topk + (int64_t)b * a.topk_stride + ((int64_t)i * a.nb + blk) * a.Fmax;
-    if (do_topf) {
-        if (!sh_overflow) {
-            if (wave == 0) {
-                const int n = sh_ncand;
-                const uint64_t T = wave_select_lds(sh_cand, n, F);
-                int written = 0;
-                for (int j0 = 0; j0 < n; j0 += kWave) {
-                    const int j = j0 + lane;
-                    const uint64_t kk = j < n ? sh_cand[j] : 0ull;
-                    const bool take = kk != 0ull && kk >= T;
-                    const int pos = written + lanes_below(take);
-                    if (take && pos < F) publish(out_list + pos, kk);
-                    written += wave_popc(take);
-                }
-                for (int j = written + lane; j < F; j += kWave) publish(out_list + j, (uint64_t)0);
-            }
+            ncand = tot;
         } else {
-            // Too many tied candidates for LDS (e.g. near-constant logits): exact
-            // selection by F rounds of a block-wide maximum below the previous key,
-            // re-reading the chunk.
+            // More tied candidates than slots: store this tile's exact top F, found by
+            // F rounds of a wave maximum below the previous key (re-reading the tile).
             uint64_t prev = ~0ull;
 #pragma unroll 1
-            for (int t = 0; t < F; ++t) {
+            for (int q = 0; q < F; ++q) {
                 uint64_t best = 0ull;
 #pragma unroll 1
                 for (int j = 0; j < kVecPerLane; ++j) {
@@ -498,44 +550,119 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                     const uint64_t o = __shfl_xor(best, off, kWave);
                     best = o > best ? o : best;
                 }
-                if (lane == 0) sh_best[wave] = best;
-                __syncthreads();
-                best = sh_best[0];
-#pragma unroll
-                for (int w = 1; w < kWavesPerBlock; ++w) best = sh_best[w] > best ? sh_best[w] : best;
-                __syncthreads();
-                if (tid == 0) publish(out_list + t, best);
+                if (lane == 0) out[q] = best;
                 prev = best;
+            }
+            ncand = F;
+        }
+    }
+
+    // ---- tile partial
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m, off, kWave);
+        const double s2 = __shfl_xor(s, off, kWave);
+        const int a2 = __shfl_xor(arg, off, kWave);
+        merge_stats(m, s, arg, m2, s2, a2, c);
+    }
+    if (lane == 0) {
+        WavePartial P;
+        P.m = m;
+        P.arg = arg;
+        P.s = s;
+        P.tau = tau;
+        P.ncand = ncand;
+        P.pad0 = P.pad1 = 0;
+        a.part[(((int64_t)b * a.nmodel + model) * a.K1 + i) * a.nt + t] = P;
+    }
+}
+
+// ============================================================================ finalise
+constexpr int kFinWaves = 8;
+constexpr int kFinBlock = kFinWaves * kWave;
+
+struct FinShared {
+    float m[2][kMaxK + 1];
+    double s[2][kMaxK + 1];
+    int arg[2][kMaxK + 1];
+    double Z[kMaxK + 1];
+    int ids[kMaxK + 1][kMaxF];
+    TopfScratch tf[kFinWaves];
+};
+
+// One block of 8 waves per sequence.  Wave w < K+1 takes draft row w (statistics,
+// cache ids, cached mass M, Saguaro Z = 1 - (1 - C) M), the next K+1 waves the target
+// rows; the last wave loads what verification needs first and verifies once every
+// row is done.
+template <int DT>
+__global__ __launch_bounds__(kFinBlock) void finalize_seq_kernel(const SeqFinal f) {
+    __shared__ FinShared fs;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int b = blockIdx.x;
+    const int K = f.K, K1 = K + 1;
+    const WavePartial* part = f.part + (int64_t)b * 2 * K1 * f.nt;
+    const bool verifier = wave == kFinWaves - 1;
+    DraftProbe pr{};
+    if (verifier)
+        pr = probe_draft<DT>(f.draft, f.p_logits, f.q_logits, f.ld_bytes, b, K, f.V, f.greedy, f.seed, f.round);
+
+    for (int rr = wave; rr < 2 * K1; rr += kFinWaves) {
+        const int model = rr < K1 ? 1 : 0, i = rr < K1 ? rr : rr - K1;
+        const int64_t r = (int64_t)b * K1 + i;
+        float m;
+        double s;
+        int arg;
+        row_stats_wave(part + (int64_t)(model * K1 + i) * f.nt, f.nt, f.c, m, s, arg);
+        s = f.greedy ? 1.0 : std_sum(m, s, f.c);
+        if (lane == 0) {
+            fs.m[model][i] = m;
+            fs.s[model][i] = s;
+            fs.arg[model][i] = arg;
+            if (model) {
+                f.q_max[r] = m;
+                f.q_sum[r] = s;
+                if (f.q_arg) f.q_arg[r] = arg;
+            } else {
+                f.p_max[r] = m;
+                f.p_sum[r] = s;
+                if (f.p_arg) f.p_arg[r] = arg;
+            }
+        }
+        if (model) {
+            const double M = cache_row_wave(part + (int64_t)(K1 + i) * f.nt, f.cand + r * f.nt * f.cap, f.nt, f.cap,
+                                            f.F[i], m, s, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i],
+                                            fs.ids[i], fs.tf[wave]);
+            const double Z = 1.0 - (1.0 - (double)f.C) * M;
+            if (lane == 0) {
+                f.cache_mass[r] = M;
+                f.Z[r] = Z;
+                fs.Z[i] = Z;
             }
         }
     }
+    __syncthreads();
 
-    // ---- block partial
-    if (tid == 0) {
-        float bm = sh_m[0];
-        double bs = sh_s[0];
-        int ba = sh_a[0];
-#pragma unroll
-        for (int w = 1; w < kWavesPerBlock; ++w) {
-            if (sh_m[w] > bm || (sh_m[w] == bm && sh_a[w] < ba)) ba = sh_a[w];
-            merge_partial(bm, bs, sh_m[w], sh_s[w], c);
+    if (!verifier) return;
+    const int i = lane;
+    const int ic = i < K ? i : 0;
+    bool in_cache = false;
+    for (int j = 0; j < f.F[ic]; ++j) in_cache |= fs.ids[ic][j] == pr.d;
+    int errs;
+    const int k = verify_wave(b, K, f.V, pr, fs.m[0][ic], fs.s[0][ic], fs.arg[0][ic], fs.m[1][ic], fs.s[1][ic],
+                              fs.Z[ic], in_cache, f.C, f.c, f.greedy, f.accept_prob, &errs);
+    if (lane == 0) {
+        f.accept_len[b] = k;
+        if (f.dev_err && errs) f.dev_err[b] |= errs;
+    }
+    if (f.greedy) {
+        const int tok = fs.arg[0][k];
+        if (lane == 0) {
+            f.bonus[b] = tok;
+            if (f.resid_mass) f.resid_mass[b] = 1.0;
         }
-        publish_partial(a.part + (int64_t)b * a.part_stride + (int64_t)(model * a.K1 + i) * a.nb + blk, bm, ba, bs);
+        const int my_id = lane < f.F[k] ? fs.ids[k][lane] : -1;
+        lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens);
     }
-    if (!a.seq_counter) return;
-
-    // ---- fused round: the last block of sequence b finishes the sequence
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned total = (unsigned)(a.nmodel * a.K1 * a.nb);
-        const unsigned old = arrive(&a.seq_counter[b]);
-        sh_last = (old == total - 1u);
-        if (sh_last) publish(&a.seq_counter[b], 0u);
-    }
-    __syncthreads();
-    if (!sh_last) return;
-    finalize_sequence<DT>(a, b, fs);
 }
 
 // ============================================================================ pass 2
@@ -548,21 +675,39 @@ struct WParams {
     double sc_q, sc_qC; // q'(x) = term(z_q, c, oq) * (sc_qC if cached else sc_q)
 };
 
-__device__ inline WParams make_wparams(const Pass2Args& a, int64_t r) {
+// Row statistics of one (b, position), loaded together with no branch in between so
+// that they travel with the tile loads.  Without a target law (draft sampling) the
+// draft statistics stand in for it and are not used.
+struct LawIn {
+    float pm, qm;
+    double ps, qs, Z;
+};
+__device__ __forceinline__ LawIn load_law(const Pass2Args& a, int64_t r) {
+    const float* pmx = a.p_max ? a.p_max : a.q_max;
+    const double* psx = a.p_sum ? a.p_sum : a.q_sum;
+    LawIn L;
+    L.pm = pmx[r];
+    L.ps = psx[r];
+    L.qm = a.q_max[r];
+    L.qs = a.q_sum[r];
+    L.Z = a.Z[r];
+    return L;
+}
+
+__device__ __forceinline__ WParams make_wparams(float c, float C, bool with_p, const LawIn& L) {
     WParams w;
-    w.c = a.c;
-    if (a.mode == 0) {
-        const RowNorm np = row_norm(a.p_max[r], a.p_sum[r], a.c);
+    w.c = c;
+    w.op = 0.f;
+    w.inv_p = 0.0;
+    if (with_p) {
+        const RowNorm np = row_norm(L.pm, L.ps, c);
         w.op = np.o;
         w.inv_p = np.inv;
-    } else {
-        w.op = 0.f;
-        w.inv_p = 0.0;
     }
-    const RowNorm nq = row_norm(a.q_max[r], a.q_sum[r], a.c);
+    const RowNorm nq = row_norm(L.qm, L.qs, c);
     w.oq = nq.o;
-    w.sc_q = nq.inv / a.Z[r];
-    w.sc_qC = w.sc_q * (double)a.C;
+    w.sc_q = nq.inv / L.Z;
+    w.sc_qC = w.sc_q * (double)C;
     return w;
 }
 
@@ -578,41 +723,34 @@ __device__ __forceinline__ double elem_weight_t(const WParams& w, float zp, floa
     const double d = p - q;
     return d > 0.0 ? d : 0.0;
 }
-__device__ __forceinline__ double elem_weight(int mode, const WParams& w, float zp, float zq, bool in_cache,
-                                              double* pw) {
-    if (mode == kWResid) return elem_weight_t<kWResid>(w, zp, zq, in_cache, pw);
-    if (mode == kWP) return elem_weight_t<kWP>(w, zp, zq, in_cache, pw);
-    return elem_weight_t<kWQprime>(w, zp, zq, in_cache, pw);
+
+// Wave-private membership bitmap (kTile/32 words) of the cached ids of a row that
+// fall in the tile [t0, t0 + kTile); lane j holds cached id j (or -1) in my_id.
+template <int DT>
+__device__ inline void tile_bitmap(uint32_t* bits, int64_t t0, int my_id) {
+    const int lane = lane_id();
+    for (int w = lane; w < kTile<DT> / 32; w += kWave) bits[w] = 0u;
+    wave_sync_lds();
+    if (my_id >= t0 && my_id < t0 + kTile<DT>)
+        atomicOr(&bits[(my_id - t0) >> 5], 1u << ((my_id - t0) & 31));
+    wave_sync_lds();
 }
 
-// Membership bitmap (LDS, kChunk/32 words) of the cached ids of a row that fall in
-// [c0, c0 + chunk).
-template <int DT>
-__device__ inline void clear_bitmap(uint32_t* bits, int t, int nthreads) {
-    for (int w = t; w < kChunk<DT> / 32; w += nthreads) bits[w] = 0u;
-}
-template <int DT>
-__device__ inline void set_bitmap(uint32_t* bits, int64_t c0, const int32_t* ids, int F, int t, int nthreads) {
-    for (int j = t; j < F; j += nthreads) {
-        const int64_t id = ids[j];
-        if (id >= c0 && id < c0 + kChunk<DT>) atomicOr(&bits[(id - c0) >> 5], 1u << ((id - c0) & 31));
-    }
-}
-
-// Weights of one lane's vector (N elements starting at e0) of a tile, from the
-// raw vectors of the target (rp) and draft (rq) rows.
-template <int DT>
-__device__ __forceinline__ void vec_weights(int mode, const WParams& wp, u32x4 rp, u32x4 rq, int64_t e0, int V,
-                                            const uint32_t* bits, int64_t c0, double* w, double* p) {
+// Weights of one lane's vector j of a tile from the raw vectors of the target and
+// draft rows; elements past V weigh 0.
+template <int DT, int MODE>
+__device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 rq, int64_t e0, int V,
+                                            const uint32_t* bits, int64_t t0, double* w, double* p) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     float zp[N], zq[N];
-    unpack_vec<DT>(rp, zp);
-    unpack_vec<DT>(rq, zq);
+    if (MODE != kWQprime) unpack_vec<DT>(rp, zp);
+    if (MODE != kWP) unpack_vec<DT>(rq, zq);
     uint32_t cbits = 0u;
-    if (mode != kWP) cbits = bits[(e0 - c0) >> 5] >> ((e0 - c0) & 31);
+    if (MODE != kWP) cbits = bits[(e0 - t0) >> 5] >> ((e0 - t0) & 31);
 #pragma unroll
     for (int e = 0; e < N; ++e) {
-        w[e] = elem_weight(mode, wp, zp[e], zq[e], (cbits >> e) & 1u, &p[e]);
+        w[e] = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f, (cbits >> e) & 1u,
+                                   &p[e]);
         if (e0 + e >= V) {
             w[e] = 0.0;
             p[e] = 0.0;
@@ -620,118 +758,204 @@ __device__ __forceinline__ void vec_weights(int mode, const WParams& wp, u32x4 r
     }
 }
 
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_pair(int mode, const char* prow, const char* qrow, int64_t e0, int V, u32x4& rp,
-                                          u32x4& rq) {
-    const u32x4 ninf = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
-    rp = mode != kWQprime ? load_raw<DT, VEC>(prow, e0, V) : ninf;
-    rq = mode != kWP ? load_raw<DT, VEC>(qrow, e0, V) : ninf;
-}
-
-// Sums over one lane's part of a wave tile: sw of the weights, sp of p(x).
+// Sums over one lane's part of a wave tile: sw of the weights, sp of p(x).  The tile
+// and the row statistics are requested before any of them is used.
 template <int DT, bool VEC, int MODE>
-__device__ __forceinline__ void tile_sums(const WParams& wp, const char* prow, const char* qrow, int64_t tile0, int V,
-                                          const uint32_t* bits, int64_t c0, double& sw, double& sp) {
+__device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const char* prow, const char* qrow, int64_t t0,
+                                          const int32_t* ids, int Fk, uint32_t* bits, double& sw, double& sp) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int lane = lane_id();
     u32x4 rp[kVecPerLane], rq[kVecPerLane];
-    if (MODE != kWQprime) load_tile<DT, VEC>(prow, tile0, V, lane, rp);
-    if (MODE != kWP) load_tile<DT, VEC>(qrow, tile0, V, lane, rq);
+    if (MODE != kWQprime) load_tile<DT, VEC>(prow, t0, a.V, lane, rp);
+    if (MODE != kWP) load_tile<DT, VEC>(qrow, t0, a.V, lane, rq);
+    int my_id = -1;
+    if (MODE != kWP && lane < Fk) my_id = ids[lane];
+    const LawIn L = load_law(a, r);
+    const WParams wp = make_wparams(a.c, a.C, MODE != kWQprime, L);
+    if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
 #pragma unroll
     for (int j = 0; j < kVecPerLane; ++j) {
-        const int64_t e0 = tile0 + (int64_t)(j * kWave + lane) * N;
-        float zp[N], zq[N];
-        if (MODE != kWQprime) unpack_vec<DT>(rp[j], zp);
-        if (MODE != kWP) unpack_vec<DT>(rq[j], zq);
-        uint32_t cbits = 0u;
-        if (MODE != kWP) cbits = bits[(e0 - c0) >> 5] >> ((e0 - c0) & 31);
+        const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+        double w[N], p[N];
+        vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, a.V, bits, t0, w, p);
         double vw = 0.0, vp = 0.0;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            double p;
-            const double w = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f,
-                                                 (cbits >> e) & 1u, &p);
-            if (e0 + e < V) {
-                vw += w;
-                vp += p;
-            }
+            vw += w[e];
+            vp += p[e];
         }
         sw += vw;
         sp += vp;
     }
 }
 
-struct P2Shared {
-    uint32_t bits[kChunk<1> / 32];
-    int last;
-};
+__device__ inline void pass2_group(const Pass2Args& a, int g, int& b, int& pos, bool& valid) {
+    if (a.mode == 0) {
+        b = g;
+        pos = a.accept_len[b];
+        valid = pos >= 0 && pos <= a.K;
+    } else {
+        b = g / a.K;
+        pos = g % a.K;
+        valid = true;
+    }
+    if (!valid) pos = 0;
+}
+
+__device__ __forceinline__ int pass2_mode(const Pass2Args& a, int pos) {
+    return a.mode == 1 ? kWQprime : (pos < a.K ? kWResid : kWP);
+}
 
 template <int DT, bool VEC>
-__device__ void finalize_pass2(const Pass2Args& a, int sidx, int b, int pos, bool valid, int64_t r, int mode,
-                               const WParams& wp, P2Shared& sh) {
+__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
+    __shared__ uint32_t bits[kWavesPerBlock][kTile<1> / 32];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int g = blockIdx.x / nblk;
+    const int t = (blockIdx.x % nblk) * kWavesPerBlock + wave;
+    if (t >= a.nt) return;
+    int b, pos;
+    bool valid;
+    pass2_group(a, g, b, pos, valid);
+    double sw = 0.0, sp = 0.0;
+    if (valid) {
+        const int64_t r = (int64_t)b * (a.K + 1) + pos;
+        const int mode = pass2_mode(a, pos);
+        const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
+        const char* qrow = a.q_logits + r * a.ld_bytes;
+        const int64_t t0 = (int64_t)t * kTile<DT>;
+        const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
+        const int Fk = a.F[pos];
+        if (mode == kWResid)
+            tile_sums<DT, VEC, kWResid>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+        else if (mode == kWP)
+            tile_sums<DT, VEC, kWP>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+        else
+            tile_sums<DT, VEC, kWQprime>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        sw += __shfl_xor(sw, m, kWave);
+        sp += __shfl_xor(sp, m, kWave);
+    }
+    if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
+}
+
+// Rescan of one tile element by element in id order: the first id whose running sum
+// (starting at base) exceeds thr, or with pick_last the last id of positive weight.
+// The caller has issued the tile loads (rp, rq).
+template <int DT, int MODE>
+__device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPerLane], const u32x4 (&rq)[kVecPerLane],
+                                  int64_t t0, int V, int my_id, uint32_t* bits, double base, double thr,
+                                  bool pick_last) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int lane = lane_id();
-    const int nseg = a.nb * kWavesPerBlock;
-    const double2* seg = a.seg + (int64_t)sidx * a.seg_stride;
+    if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
+    double run = base;
+    int found = -1, last_pos = -1;
+#pragma unroll
+    for (int j = 0; j < kVecPerLane; ++j) {
+        const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+        double w[N], p[N];
+        vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, V, bits, t0, w, p);
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < N; ++e) ls += w[e];
+        double incl = ls;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        double cum = run + (incl - ls);
+        int hitpos = -1, lastp = -1;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            cum += w[e];
+            if (hitpos < 0 && cum > thr) hitpos = (int)(e0 + e);
+            if (w[e] > 0.0) lastp = (int)(e0 + e);
+        }
+        if (!pick_last && found < 0) {
+            const uint64_t hm = __ballot(hitpos >= 0);
+            if (hm) found = __shfl(hitpos, __ffsll((long long)hm) - 1, kWave);
+        }
+        const uint64_t lm = __ballot(lastp >= 0);
+        if (lm) last_pos = __shfl(lastp, 63 - __clzll(lm), kWave);
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    return found >= 0 ? found : (last_pos >= 0 ? last_pos : (int)min<int64_t>(t0, V - 1));
+}
+
+// Inclusive wave scan of x (fp64, lane order).
+__device__ __forceinline__ double wave_scan_incl(double x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// One wave per group: totals over the tiles in tile order, the tile where the running
+// sum crosses u * total, the id inside it, and the cache lookup.  The tile sums of the
+// first 64 tiles, the row statistics and the cached ids are requested together.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args a, int ngroups) {
+    __shared__ uint32_t bits[kWavesPerBlock][kTile<1> / 32];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int g = blockIdx.x * kWavesPerBlock + wave;
+    if (g >= ngroups) return;
+    int b, pos;
+    bool valid;
+    pass2_group(a, g, b, pos, valid);
     const int K = a.K;
+    const int nt = a.nt;
+    const double2* seg = a.seg + (int64_t)g * nt;
     int tok = -1;
     double Zused = 0.0;
+    const int my_id = valid ? cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O) : -1;
     if (valid) {
-        // totals over segments in segment order (fixed-shape wave scans)
+        const int64_t r = (int64_t)b * (K + 1) + pos;
+        const double2 v0 = lane < nt ? seg[lane] : make_double2(0.0, 0.0);
+        const LawIn L = load_law(a, r);
+        const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
+        const double u = (double)philox_uniform(a.seed, a.round, purpose, (uint64_t)b, (uint64_t)pos);
         double tot_w = 0.0, tot_p = 0.0;
-        for (int g0 = 0; g0 < nseg; g0 += kWave) {
-            const int g = g0 + lane;
-            double iw = 0.0, ip = 0.0;
-            if (g < nseg) {
-                iw = observe(&seg[g].x);
-                ip = observe(&seg[g].y);
-            }
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const double yw = __shfl_up(iw, off, kWave);
-                const double yp = __shfl_up(ip, off, kWave);
-                if (lane >= off) {
-                    iw += yw;
-                    ip += yp;
-                }
-            }
-            tot_w += __shfl(iw, kWave - 1, kWave);
-            tot_p += __shfl(ip, kWave - 1, kWave);
+        for (int g0 = 0; g0 < nt; g0 += kWave) {
+            const int j = g0 + lane;
+            double2 v = v0;
+            if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+            tot_w += __shfl(wave_scan_incl(v.x), kWave - 1, kWave);
+            tot_p += __shfl(wave_scan_incl(v.y), kWave - 1, kWave);
         }
-        int wmode = mode;
+        int mode = pass2_mode(a, pos);
         double Z = tot_w;
-        if (mode == kWResid && !(Z > 0.0)) {
-            wmode = kWP;
+        const bool use_p = mode == kWResid && !(Z > 0.0);
+        if (use_p) {
+            mode = kWP;
             Z = tot_p;
         }
         Zused = Z;
-        const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
-        const double u = (double)philox_uniform(a.seed, a.round, purpose, (uint64_t)b, (uint64_t)pos);
-        const double t = u * Z;
-        // first segment whose inclusive running sum exceeds t
+        const double thr = u * Z;
         int gsel = -1, glast = -1;
         double gbase = 0.0, lastbase = 0.0, carry = 0.0;
-        for (int g0 = 0; g0 < nseg; g0 += kWave) {
-            const int g = g0 + lane;
-            double x = 0.0;
-            if (g < nseg) x = (wmode == kWP && mode == kWResid) ? observe(&seg[g].y) : observe(&seg[g].x);
-            double incl = x;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const double y = __shfl_up(incl, off, kWave);
-                if (lane >= off) incl += y;
-            }
-            incl += carry;
+        for (int g0 = 0; g0 < nt; g0 += kWave) {
+            const int j = g0 + lane;
+            double2 v = v0;
+            if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+            const double x = use_p ? v.y : v.x;
+            const double incl = wave_scan_incl(x) + carry;
             const double excl = incl - x;
-            const uint64_t cross = __ballot(g < nseg && incl > t);
-            const uint64_t pos_m = __ballot(g < nseg && x > 0.0);
+            const uint64_t cross = __ballot(j < nt && incl > thr);
+            const uint64_t posm = __ballot(j < nt && x > 0.0);
             if (gsel < 0 && cross) {
                 const int l = __ffsll((long long)cross) - 1;
                 gsel = g0 + l;
                 gbase = __shfl(excl, l, kWave);
             }
-            if (pos_m) {
-                const int l = 63 - __clzll(pos_m);
+            if (posm) {
+                const int l = 63 - __clzll(posm);
                 glast = g0 + l;
                 lastbase = __shfl(excl, l, kWave);
             }
@@ -743,53 +967,19 @@ __device__ void finalize_pass2(const Pass2Args& a, int sidx, int b, int pos, boo
             gbase = lastbase;
             pick_last = true;
         }
-        // rescan the selected segment (one wave tile) element by element in id order
-        const int64_t c0 = (int64_t)(gsel / kWavesPerBlock) * kChunk<DT>;
-        const int64_t tile0 = c0 + (int64_t)(gsel % kWavesPerBlock) * kTile<DT>;
-        const int F = a.F[pos];
-        const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
-        if (wmode != kWP) {
-            clear_bitmap<DT>(sh.bits, lane, kWave);
-            wave_sync_lds();
-            set_bitmap<DT>(sh.bits, c0, ids, F, lane, kWave);
-            wave_sync_lds();
-        }
+        const int64_t t0 = (int64_t)gsel * kTile<DT>;
         const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
         const char* qrow = a.q_logits + r * a.ld_bytes;
-        double run = gbase;
-        int found = -1, last_pos = -1;
-        for (int j = 0; j < kVecPerLane && found < 0; ++j) {
-            const int64_t e0 = tile0 + (int64_t)(j * kWave + lane) * N;
-            double w[N], p[N];
-            u32x4 rp, rq;
-            load_pair<DT, VEC>(wmode, prow, qrow, e0, a.V, rp, rq);
-            vec_weights<DT>(wmode, wp, rp, rq, e0, a.V, sh.bits, c0, w, p);
-            double ls = 0.0;
-#pragma unroll
-            for (int e = 0; e < N; ++e) ls += w[e];
-            double incl = ls;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const double y = __shfl_up(incl, off, kWave);
-                if (lane >= off) incl += y;
-            }
-            double cum = run + (incl - ls);
-            int hitpos = -1, lastp = -1;
-#pragma unroll
-            for (int e = 0; e < N; ++e) {
-                cum += w[e];
-                if (hitpos < 0 && cum > t) hitpos = (int)(e0 + e);
-                if (w[e] > 0.0) lastp = (int)(e0 + e);
-            }
-            if (!pick_last) {
-                const uint64_t hm = __ballot(hitpos >= 0);
-                if (hm) found = __shfl(hitpos, __ffsll((long long)hm) - 1, kWave);
-            }
-            const uint64_t lm = __ballot(lastp >= 0);
-            if (lm) last_pos = __shfl(lastp, 63 - __clzll(lm), kWave);
-            run += __shfl(incl, kWave - 1, kWave);
-        }
-        tok = found >= 0 ? found : (last_pos >= 0 ? last_pos : (int)min<int64_t>(tile0, a.V - 1));
+        u32x4 rp[kVecPerLane], rq[kVecPerLane];
+        if (mode != kWQprime) load_tile<DT, VEC>(prow, t0, a.V, lane, rp);
+        if (mode != kWP) load_tile<DT, VEC>(qrow, t0, a.V, lane, rq);
+        const WParams wp = make_wparams(a.c, a.C, mode != kWQprime, L);
+        if (mode == kWResid)
+            tok = rescan_tile<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
+        else if (mode == kWP)
+            tok = rescan_tile<DT, kWP>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
+        else
+            tok = rescan_tile<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
     }
     if (lane == 0) {
         if (a.mode == 0) {
@@ -801,103 +991,38 @@ __device__ void finalize_pass2(const Pass2Args& a, int sidx, int b, int pos, boo
         }
     }
     if (a.mode == 0 && a.do_lookup)
-        lookup_wave(b, K, a.V, valid ? pos : -1, tok, a.F, a.O, a.Bf, a.cache_ids, a.fallback, a.seed, a.round,
-                    a.hit, a.slot, a.fallback_tokens);
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
-    constexpr int N = ElemTraits<DT>::kPerVec;
-    __shared__ P2Shared sh;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int sidx = blockIdx.x / a.nb, blk = blockIdx.x % a.nb;
-    const int K = a.K, K1 = K + 1;
-    int b, pos;
-    bool valid;
-    if (a.mode == 0) {
-        b = sidx;
-        pos = a.accept_len[b];
-        valid = pos >= 0 && pos <= K;
-    } else {
-        b = sidx / K;
-        pos = sidx % K;
-        valid = true;
-    }
-    if (!valid) pos = 0;
-    const int64_t r = (int64_t)b * K1 + pos;
-    const int mode = a.mode == 1 ? kWQprime : (pos < K ? kWResid : kWP);
-    const WParams wp = make_wparams(a, r);
-    const int64_t c0 = (int64_t)blk * kChunk<DT>;
-    const int F = a.F[pos];
-    const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
-    if (mode != kWP) {
-        clear_bitmap<DT>(sh.bits, tid, kBlock);
-        __syncthreads();
-        set_bitmap<DT>(sh.bits, c0, ids, F, tid, kBlock);
-    }
-    __syncthreads();
-
-    const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
-    const char* qrow = a.q_logits + r * a.ld_bytes;
-    const int64_t tile0 = c0 + (int64_t)wave * kTile<DT>;
-    double sw = 0.0, sp = 0.0;
-    if (valid) {
-        if (mode == kWResid)
-            tile_sums<DT, VEC, kWResid>(wp, prow, qrow, tile0, a.V, sh.bits, c0, sw, sp);
-        else if (mode == kWP)
-            tile_sums<DT, VEC, kWP>(wp, prow, qrow, tile0, a.V, sh.bits, c0, sw, sp);
-        else
-            tile_sums<DT, VEC, kWQprime>(wp, prow, qrow, tile0, a.V, sh.bits, c0, sw, sp);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        sw += __shfl_xor(sw, m, kWave);
-        sp += __shfl_xor(sp, m, kWave);
-    }
-    if (lane == 0) {
-        double2* g = a.seg + (int64_t)sidx * a.seg_stride + blk * kWavesPerBlock + wave;
-        publish(&g->x, sw);
-        publish(&g->y, sp);
-    }
-
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = arrive(&a.counter[sidx]);
-        sh.last = (old == (unsigned)a.nb - 1u);
-        if (sh.last) publish(&a.counter[sidx], 0u);
-    }
-    __syncthreads();
-    if (!sh.last) return;
-    if (wave != 0) return;
-    finalize_pass2<DT, VEC>(a, sidx, b, pos, valid, r, mode, wp, sh);
+        lookup_wave(b, K, a.V, valid ? pos : -1, valid ? a.O[pos] : 0, my_id, tok, a.fallback, a.seed, a.round, a.hit,
+                    a.slot, a.fallback_tokens);
 }
 
 // ============================================================================ small kernels
-__global__ void combine_stats_kernel(const Pass1Args a, float* m_out, double* s_out, int32_t* arg_out) {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= a.B * a.K1) return;
-    const int b = r / a.K1, i = r % a.K1;
+// Per-row merges for the separate calls: one wave per row (same code as the round).
+__global__ __launch_bounds__(kBlock) void combine_stats_kernel(const Pass1Args a, float* m_out, double* s_out,
+                                                               int32_t* arg_out) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (r >= (int64_t)a.B * a.K1) return;
     float m;
     double s;
     int arg;
-    combine_partials(a.part + (int64_t)b * a.part_stride + (int64_t)i * a.nb, a.nb, a.c, m, s, arg);
-    m_out[r] = m;
-    s_out[r] = a.greedy ? 1.0 : std_sum(m, s, a.c);
-    if (arg_out) arg_out[r] = arg;
+    row_stats_wave(a.part + r * a.nt, a.nt, a.c, m, s, arg);
+    if (lane == 0) {
+        m_out[r] = m;
+        s_out[r] = a.greedy ? 1.0 : std_sum(m, s, a.c);
+        if (arg_out) arg_out[r] = arg;
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void combine_topf_kernel(const Pass1Args a, int Bf, const float* q_max,
                                                               const double* q_sum, int32_t* cache_ids,
                                                               double* cache_mass) {
-    __shared__ uint64_t xchg[kWavesPerBlock][kWave];
+    __shared__ TopfScratch sc[kWavesPerBlock];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (r >= (int64_t)a.B * a.K1) return;
     const int b = (int)(r / a.K1), i = (int)(r % a.K1);
-    const double M = cache_row(a.topk + (int64_t)b * a.topk_stride + (int64_t)i * a.nb * a.Fmax, a.nb, a.Fmax, a.F[i],
-                               q_max[r], q_sum[r], a.c, a.greedy, cache_ids + (int64_t)b * Bf + a.O[i], nullptr,
-                               xchg[wave]);
+    const double M = cache_row_wave(a.part + r * a.nt, a.cand + r * a.nt * a.cap, a.nt, a.cap, a.F[i], q_max[r],
+                                    q_sum[r], a.c, a.greedy, cache_ids + (int64_t)b * Bf + a.O[i], nullptr, sc[wave]);
     if (lane == 0) cache_mass[r] = M;
 }
 
@@ -945,20 +1070,18 @@ __global__ void verify_kernel(const char* p_logits, const char* q_logits, int B,
     if (b >= B) return;
     const int lane = lane_id();
     const int K1 = K + 1;
-    const bool act = lane < K;
-    const int ic = act ? lane : 0;
+    const int ic = lane < K ? lane : 0;
     const int64_t r = (int64_t)b * K1 + ic;
-    const int d = act ? draft[(int64_t)b * K + lane] : 0;
+    const DraftProbe pr = probe_draft<DT>(draft, p_logits, q_logits, ld_bytes, b, K, V, greedy, seed, round);
     bool in_cache = false;
     const int32_t* ids = cache_ids + (int64_t)b * Bf + fo.O[ic];
-    for (int j = 0; j < fo.F[ic]; ++j) in_cache |= ids[j] == d;
+    for (int j = 0; j < fo.F[ic]; ++j) in_cache |= ids[j] == pr.d;
     const float mp = greedy ? 0.f : p_max[r], mq = greedy ? 0.f : q_max[r];
     const double sp = greedy ? 1.0 : p_sum[r], sq = greedy ? 1.0 : q_sum[r];
     const int argp = greedy ? p_arg[r] : 0;
     const double Zi = greedy ? 1.0 : Z[r];
     int errs;
-    const int k = verify_wave<DT>(b, K, V, p_logits + r * ld_bytes, q_logits + r * ld_bytes, d, mp, sp, argp, mq, sq,
-                                  Zi, in_cache, C, c, greedy, seed, round, accept_prob, &errs);
+    const int k = verify_wave(b, K, V, pr, mp, sp, argp, mq, sq, Zi, in_cache, C, c, greedy, accept_prob, &errs);
     if (lane == 0) {
         accept_len[b] = k;
         if (dev_err && errs) dev_err[b] |= errs;
@@ -991,7 +1114,8 @@ __global__ void lookup_kernel(int B, int K, int V, FO fo, int Bf, const int32_t*
     const int k = accept_len[b];
     const bool ok = k >= 0 && k <= K;
     if (!ok && lane_id() == 0 && dev_err) dev_err[b] |= kErrLenRange;
-    lookup_wave(b, K, V, ok ? k : -1, bonus[b], fo.F, fo.O, Bf, cache_ids, fallback, seed, round, hit, slot, fb);
+    const int my_id = cached_id(cache_ids, b, Bf, ok ? k : -1, K, fo.F, fo.O);
+    lookup_wave(b, K, V, ok ? k : -1, ok ? fo.O[k] : 0, my_id, bonus[b], fallback, seed, round, hit, slot, fb);
 }
 
 // ============================================================================ launchers
@@ -1002,43 +1126,58 @@ static FO make_fo(const int* F, const int* O, int K1) {
     return fo;
 }
 
-hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st) {
-    const int64_t grid = (int64_t)a.B * a.nmodel * a.K1 * a.nb;
-    if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
+template <typename Fn>
+static hipError_t by_type(int dtype, bool vec, Fn&& fn) {
     if (dtype == 1) {
         if (vec)
-            pass1_kernel<1, true><<<(unsigned)grid, kBlock, 0, st>>>(a);
+            fn(std::integral_constant<int, 1>{}, std::true_type{});
         else
-            pass1_kernel<1, false><<<(unsigned)grid, kBlock, 0, st>>>(a);
+            fn(std::integral_constant<int, 1>{}, std::false_type{});
     } else {
         if (vec)
-            pass1_kernel<0, true><<<(unsigned)grid, kBlock, 0, st>>>(a);
+            fn(std::integral_constant<int, 0>{}, std::true_type{});
         else
-            pass1_kernel<0, false><<<(unsigned)grid, kBlock, 0, st>>>(a);
+            fn(std::integral_constant<int, 0>{}, std::false_type{});
     }
     return hipGetLastError();
 }
 
-hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int nseq, hipStream_t st) {
-    const int64_t grid = (int64_t)nseq * a.nb;
+hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st) {
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t grid = (int64_t)a.B * a.nmodel * a.K1 * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
-    if (dtype == 1) {
-        if (vec)
-            pass2_kernel<1, true><<<(unsigned)grid, kBlock, 0, st>>>(a);
-        else
-            pass2_kernel<1, false><<<(unsigned)grid, kBlock, 0, st>>>(a);
-    } else {
-        if (vec)
-            pass2_kernel<0, true><<<(unsigned)grid, kBlock, 0, st>>>(a);
-        else
-            pass2_kernel<0, false><<<(unsigned)grid, kBlock, 0, st>>>(a);
-    }
+    return by_type(dtype, vec, [&](auto DT, auto VEC) {
+        pass1_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
+    });
+}
+
+hipError_t launch_finalize_seq(int dtype, const SeqFinal& f, hipStream_t st) {
+    if (dtype == 1)
+        finalize_seq_kernel<1><<<f.B, kFinBlock, 0, st>>>(f);
+    else
+        finalize_seq_kernel<0><<<f.B, kFinBlock, 0, st>>>(f);
     return hipGetLastError();
+}
+
+hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st) {
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t grid = (int64_t)ngroups * nblk;
+    if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
+    return by_type(dtype, vec, [&](auto DT, auto VEC) {
+        pass2_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
+    });
+}
+
+hipError_t launch_finalize_bonus(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st) {
+    const int grid = (ngroups + kWavesPerBlock - 1) / kWavesPerBlock;
+    return by_type(dtype, vec, [&](auto DT, auto VEC) {
+        finalize_bonus_kernel<decltype(DT)::value, decltype(VEC)::value><<<grid, kBlock, 0, st>>>(a, ngroups);
+    });
 }
 
 hipError_t launch_combine_stats(const Pass1Args& a, float* m, double* s, int32_t* arg, hipStream_t st) {
     const int R = a.B * a.K1;
-    combine_stats_kernel<<<(R + 255) / 256, 256, 0, st>>>(a, m, s, arg);
+    combine_stats_kernel<<<(R + kWavesPerBlock - 1) / kWavesPerBlock, kBlock, 0, st>>>(a, m, s, arg);
     return hipGetLastError();
 }
 

@@ -67,8 +67,12 @@ def test_workspace_bytes(ssd):
     for bad in [_shape(ssd, B=0), _shape(ssd, K=0), _shape(ssd, K=17), _shape(ssd, V=1), _shape(ssd, ld=50),
                 _shape(ssd, dtype=3), _shape(ssd, T=-1.0), _shape(ssd, T=float("inf")), _shape(ssd, T=float("nan"))]:
         assert L.ssd_workspace_bytes(ctypes.byref(bad), 8) == 0
-    big = ssd.ssd_shape(40000, 1, 100, 100, 0, 1.0)
+    # one pass-1 block per 4 tiles of each of the 2 B (K+1) rows: above 2^31 - 1 blocks
+    # the shape is unsupported
+    big = ssd.ssd_shape(1 << 30, 1, 100, 100, 0, 1.0)
     assert L.ssd_workspace_bytes(ctypes.byref(big), 8) == 0
+    ok = ssd.ssd_shape(40000, 1, 100, 100, 0, 1.0)
+    assert L.ssd_workspace_bytes(ctypes.byref(ok), 8) > 0
 
 
 def _F(vals):

@@ -86,6 +86,8 @@ def _gpu_stats(z, T):
     (5000, [64, 0, 3, 1, 0], "gauss"),
     (128256, [24, 19, 16, 13, 10], "quantised"),
     (3000, [40, 30, 20, 10, 5], "constant"),
+    (128256, [30, 2, 1, 0, 1], "constant"),   # ties across many tiles: whole-key select
+    (128256, [64, 40, 1, 0, 2], "gauss"),     # more candidates than register slots
     (9, [9, 4, 1, 0, 2], "gauss"),
     (20011, [1, 1, 1, 1, 1], "neginf"),
 ])
