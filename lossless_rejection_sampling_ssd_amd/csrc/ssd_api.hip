@@ -26,8 +26,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //   seg    [max(B, B K)][nt]      (weight sum, target-law sum) per pass-2 tile
 //   stats  [B (K+1)]              fp64 p_sum q_sum cache_mass Z, fp32 p_max q_max,
 //                                 int32 p_arg (for outputs the caller leaves NULL)
+//   vflag  [B K]                  int32 outcome of each draft-token test
 struct Layout {
-    size_t part, cand, seg, stats, total;
+    size_t part, cand, seg, stats, vflag, total;
     int nt, cap;
 };
 
@@ -47,6 +48,8 @@ void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     off = align_up(off + (size_t)groups * nt * 16);
     L->stats = off;
     off = align_up(off + (size_t)R * (4 * 8 + 2 * 4 + 4));
+    L->vflag = off;
+    off = align_up(off + (size_t)s->B * s->K * 4);
     L->total = off;
     L->nt = nt;
     L->cap = cap;
@@ -478,6 +481,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     f.slot = out->slot;
     f.fallback_tokens = out->fallback_tokens;
     f.dev_err = out->dev_err;
+    f.vflag = at<int32_t>(ws, L.vflag);
 
     const bool vec = vec_ok(s, p_logits) && vec_ok(s, q_logits);
     hipError_t e;
@@ -487,9 +491,13 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     if (e != hipSuccess) return fail_hip(e, "ssd_round pass 1");
     if (ev && ev->pass1_stop && (e = hipEventRecord((hipEvent_t)ev->pass1_stop, hs)) != hipSuccess)
         return fail_hip(e, "ssd_round event");
-    e = ssd::launch_finalize_seq(s->dtype, f, hs);
+    e = ssd::launch_finalize_pos(s->dtype, f, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_round finalise");
-    if (greedy) return SSD_OK;
+    if (greedy) {
+        e = ssd::launch_finish_greedy(f, hs);
+        if (e != hipSuccess) return fail_hip(e, "ssd_round greedy bonus");
+        return SSD_OK;
+    }
 
     ssd::Pass2Args b{};
     b.p_logits = (const char*)p_logits;
@@ -510,7 +518,8 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.q_sum = f.q_sum;
     b.Z = f.Z;
     b.cache_ids = f.cache_ids;
-    b.accept_len = f.accept_len;
+    b.vflag = f.vflag;
+    b.accept_len_out = f.accept_len;
     b.seed = rng.seed;
     b.round = rng.round;
     b.seg = at<double2>(ws, L.seg);

@@ -33,64 +33,45 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Loads the vector of elements [e0, e0 + kPerVec) of a row into x[], elements at or
-// past V set to -inf.  Vector path when the whole vector is in range and aligned.
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_vec(const char* row, int64_t e0, int V, float* x) {
+// The raw pattern of a vector of -inf elements.
+template <int DT>
+__device__ __forceinline__ u32x4 neg_inf_vec() {
+    const uint32_t w = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
+    u32x4 v;
+    v.x = v.y = v.z = v.w = w;
+    return v;
+}
+
+// Raw 16-byte vector of elements [e0, e0 + kPerVec) of a row by element loads, the
+// elements at or past V replaced by the -inf pattern.  Every element load reads a
+// clamped, in-range id and is unconditional, so all of them are in flight together.
+template <int DT>
+__device__ __forceinline__ u32x4 load_raw_elems(const char* row, int64_t e0, int V) {
     constexpr int N = ElemTraits<DT>::kPerVec;
-    if (VEC && e0 + N <= V) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + e0 * ElemTraits<DT>::kBytes);
-        if (DT == 1) {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w[4];
+    if (DT == 1) {
+        uint32_t h[N];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                x[2 * q] = __uint_as_float(w[q] << 16);
-                x[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-            }
-        } else {
-            x[0] = __uint_as_float(v.x);
-            x[1] = __uint_as_float(v.y);
-            x[2] = __uint_as_float(v.z);
-            x[3] = __uint_as_float(v.w);
+        for (int e = 0; e < N; ++e) {
+            const int64_t id = e0 + e < V ? e0 + e : V - 1;
+            h[e] = reinterpret_cast<const uint16_t*>(row)[id];
         }
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+            if (e0 + e >= V) h[e] = 0xFF80u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = h[2 * q] | (h[2 * q + 1] << 16);
     } else {
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const int64_t id = e0 + e;
-            if (id < V) {
-                if (DT == 1)
-                    x[e] = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[id]);
-                else
-                    x[e] = reinterpret_cast<const float*>(row)[id];
-            } else {
-                x[e] = -INFINITY;
-            }
+            const int64_t id = e0 + e < V ? e0 + e : V - 1;
+            w[e] = reinterpret_cast<const uint32_t*>(row)[id];
         }
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+            if (e0 + e >= V) w[e] = 0xFF800000u;
     }
-}
-
-// Raw 16-byte vector of elements [e0, e0 + kPerVec) of a row, elements at or past V
-// replaced by the -inf pattern; unpack_vec widens it to fp32.
-template <int DT, bool VEC>
-__device__ __forceinline__ u32x4 load_raw(const char* row, int64_t e0, int V) {
-    constexpr int N = ElemTraits<DT>::kPerVec;
-    if (VEC && e0 + N <= V) return *reinterpret_cast<const u32x4*>(row + e0 * ElemTraits<DT>::kBytes);
     u32x4 v;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-        const int64_t id = e0 + e;
-        if (id < V) {
-            if (DT == 1) {
-                const uint32_t h = reinterpret_cast<const uint16_t*>(row)[id];
-                w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (h << 16)) : ((w[e >> 1] & 0xFFFF0000u) | h);
-            } else {
-                w[e] = reinterpret_cast<const uint32_t*>(row)[id];
-            }
-        }
-    }
     v.x = w[0];
     v.y = w[1];
     v.z = w[2];
@@ -112,10 +93,43 @@ __device__ __forceinline__ void unpack_vec(u32x4 v, float* x) {
     }
 }
 
+// Marks the vectors as rewritten, so that values derived from them before this point
+// are recomputed after it instead of being kept in registers.
+__device__ __forceinline__ void opaque_regs(u32x4 (&raw)[kVecPerLane]) {
+#pragma unroll
+    for (int j = 0; j < kVecPerLane; ++j) __asm__ volatile("" : "+v"(raw[j]));
+}
+
+// Element e (a compile-time constant after unrolling) of a raw vector, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
+    if (DT == 1) {
+        const uint32_t w = v[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    return __uint_as_float(v[e]);
+}
+// The same for an element index known only at run time.
+template <int DT>
+__device__ __forceinline__ float vec_elem_dyn(const u32x4& v, int e) {
+    const int q = DT == 1 ? e >> 1 : e;
+    uint32_t w = v.x;
+    w = q == 1 ? v.y : w;
+    w = q == 2 ? v.z : w;
+    w = q == 3 ? v.w : w;
+    if (DT == 1) w = (e & 1) ? (w & 0xFFFF0000u) : (w << 16);
+    return __uint_as_float(w);
+}
+
 // The kVecPerLane raw vectors one lane owns in a wave tile starting at element t0
-// (vector j covers [t0 + (j*64 + lane)*kPerVec, +kPerVec)).  When the whole tile is in
-// range and aligned (a wave-uniform test) the loads are unconditional and issued
-// back to back; only a ragged or unaligned tile takes the guarded element path.
+// (vector j covers [t0 + (j*64 + lane)*kPerVec, +kPerVec)), elements at or past V
+// replaced by -inf.  VEC: the row is 16-byte aligned.
+//  - whole tile in range: unconditional 16-byte loads, issued back to back,
+//    non-temporal (each logit is read once per pass);
+//  - last tile of an aligned row: vectors wholly in range are loaded as vectors (lanes
+//    past the end load the row's first vector instead and discard it, so the loads
+//    stay unconditional); the one vector that straddles V, if any, by element loads;
+//  - unaligned rows: element loads of clamped ids.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, int lane, u32x4 (&raw)[kVecPerLane]) {
     constexpr int N = ElemTraits<DT>::kPerVec;
@@ -123,13 +137,29 @@ __device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, in
     if (VEC && t0 + TILE <= V) {
         const u32x4* base = reinterpret_cast<const u32x4*>(row + t0 * ElemTraits<DT>::kBytes) + lane;
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) raw[j] = base[j * kWave];
+        for (int j = 0; j < kVecPerLane; ++j) raw[j] = __builtin_nontemporal_load(base + j * kWave);
+    } else if (VEC) {
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) {
+            const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+            const bool whole = e0 + N <= V;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(row + (whole ? e0 : 0) * ElemTraits<DT>::kBytes);
+            raw[j] = whole ? v : neg_inf_vec<DT>();
+        }
+        if (V % N != 0) {
+            const int64_t js = ((int64_t)(V / N) * N - t0) / N;  // vector index (j*64 + lane) that straddles V
+            if (js >= 0 && js < kVecPerLane * kWave && js % kWave == lane) {
+#pragma unroll
+                for (int j = 0; j < kVecPerLane; ++j)
+                    if (j == js / kWave) raw[j] = load_raw_elems<DT>(row, t0 + js * N, V);
+            }
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) raw[j] = load_raw<DT, false>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
+        for (int j = 0; j < kVecPerLane; ++j)
+            raw[j] = load_raw_elems<DT>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
     }
 }
-
 
 template <int DT>
 __device__ __forceinline__ float load_one(const char* row, int64_t id) {
@@ -160,6 +190,14 @@ __device__ __forceinline__ float key_val(uint64_t k) { return unord32((uint32_t)
 // ---------------------------------------------------------------------------- wave ops
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// A value every lane holds alike, moved to a scalar register so that loops and
+// branches on it are scalar (wave-level) control flow, not per-lane masking.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ uint64_t uniform(uint64_t v) {
+    return ((uint64_t)uniform((uint32_t)(v >> 32)) << 32) | uniform((uint32_t)v);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
@@ -168,7 +206,7 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
-    return v;
+    return uniform(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -301,8 +339,8 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
         }
     }
     if (n <= F) return 0ull;
-    orv = wave_or64(orv);
-    andv = wave_and64(andv);
+    orv = uniform(wave_or64(orv));
+    andv = uniform(wave_and64(andv));
     uint64_t diff = orv ^ andv;
     uint64_t T = andv & ~diff;
     while (diff) {
@@ -333,8 +371,8 @@ __device__ inline uint64_t wave_select_lds(const uint64_t* keys, int n, int F) {
         }
     }
     if (cnt0 <= F) return 0ull;
-    orv = wave_or64(orv);
-    andv = wave_and64(andv);
+    orv = uniform(wave_or64(orv));
+    andv = uniform(wave_and64(andv));
     uint64_t diff = orv ^ andv;
     uint64_t T = andv & ~diff;
     while (diff) {
@@ -361,6 +399,8 @@ __device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
         orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
         andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
     }
+    orv = uniform(orv);
+    andv = uniform(andv);
     uint32_t diff = orv ^ andv;
     uint32_t T = andv & ~diff;
     while (diff) {

@@ -38,8 +38,10 @@ struct Pass1Args {
     uint64_t* cand;     // [B][K1][nt][cap]
 };
 
-// Per-sequence finalisation of the vocabulary pass: row statistics, speculation
-// cache, Saguaro normalisers and verification (and, at T = 0, bonus and lookup).
+// Finalisation of the vocabulary pass per (sequence, position): row statistics,
+// speculation cache, Saguaro normaliser and the test of the draft token.  The outcome
+// of each test goes to vflag; the kernels after it take the accepted length from there
+// (and, at T = 0, the bonus and lookup in a per-sequence kernel).
 struct SeqFinal {
     const WavePartial* part;
     const uint64_t* cand;
@@ -73,6 +75,7 @@ struct SeqFinal {
     int32_t* slot;
     int32_t* fallback_tokens;
     int32_t* dev_err;     // nullable
+    int32_t* vflag;       // [B, K] workspace: bit 0 accepted, higher bits error bits
 };
 
 struct Pass2Args {
@@ -93,7 +96,9 @@ struct Pass2Args {
     const double* q_sum;
     const double* Z;
     const int32_t* cache_ids;
-    const int32_t* accept_len;
+    const int32_t* accept_len;  // mode 0 without vflag: the accepted lengths
+    const int32_t* vflag;       // mode 0: per-position test outcomes (accepted length = first rejection)
+    int32_t* accept_len_out;    // with vflag: written by the bonus kernel
     uint64_t seed, round;
     double2* seg;       // [groups][nt] (weight sum, target-law sum) per wave tile
     int32_t* out_tok;   // bonus [B] or draft [B, K]
@@ -111,7 +116,8 @@ int tiles_per_row(int dtype, int V);
 int cand_cap(int Fmax);
 
 hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st);
-hipError_t launch_finalize_seq(int dtype, const SeqFinal& f, hipStream_t st);
+hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st);
+hipError_t launch_finish_greedy(const SeqFinal& f, hipStream_t st);
 hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st);
 hipError_t launch_finalize_bonus(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st);
 hipError_t launch_combine_stats(const Pass1Args& a, float* m, double* s, int32_t* arg, hipStream_t st);

@@ -32,13 +32,14 @@ namespace ssd {
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4 };
 constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
+constexpr int kStageCap = 160;     // LDS slots per wave for one tile's candidate keys (>= any cap)
 
 int tile_elems(int dtype) { return dtype == 1 ? kTile<1> : kTile<0>; }
 int tiles_per_row(int dtype, int V) {
     const int t = tile_elems(dtype);
     return (V + t - 1) / t;
 }
-int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }
+int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }  // <= 144 = cand_cap(64) <= kStageCap
 
 // ============================================================================ shared pieces
 // Row normalisation from the exchanged statistics (row max m, row sum
@@ -75,16 +76,35 @@ __device__ __forceinline__ void merge_stats(float& m, double& s, int& arg, float
     merge_partial(m, s, m2, s2, c);
 }
 
+// What the candidate merge of a draft row needs from the row's tile partials: the
+// largest tile threshold, the largest per-tile candidate count and (in LDS) every
+// tile's count.
+constexpr int kMaxMergeTiles = 512;
+struct CandSummary {
+    uint32_t tr;
+    int max_nc;
+};
+
 // Softmax statistics of one row from its nt tile partials, by one wave in a fixed
 // order (lane-sequential, then a butterfly); every lane returns the same values.
-__device__ inline void row_stats_wave(const WavePartial* P, int nt, float c, float& m, double& s, int& arg) {
+// With with_cands, the same single read of the partials also fills the candidate
+// summary cs (per-tile counts to nc, which holds kMaxMergeTiles entries).
+__device__ __forceinline__ void row_stats_wave(const WavePartial* P, int nt, float c, float& m, double& s, int& arg,
+                                               bool with_cands, CandSummary& cs, uint8_t* nc) {
     const int lane = lane_id();
     m = -INFINITY;
     s = 0.0;
     arg = INT_MAX;
+    uint32_t tr = 0u;
+    int max_nc = 0;
     for (int t = lane; t < nt; t += kWave) {
         const WavePartial q = P[t];
         merge_stats(m, s, arg, q.m, q.s, q.arg, c);
+        if (with_cands) {
+            tr = max(tr, q.tau);
+            max_nc = max(max_nc, q.ncand);
+            if (t < kMaxMergeTiles) nc[t] = (uint8_t)q.ncand;
+        }
     }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -93,33 +113,47 @@ __device__ inline void row_stats_wave(const WavePartial* P, int nt, float c, flo
         const int a2 = __shfl_xor(arg, off, kWave);
         merge_stats(m, s, arg, m2, s2, a2, c);
     }
+    cs.tr = 0u;
+    cs.max_nc = 0;
+    if (with_cands) {
+        cs.tr = wave_max_u32(tr);
+        cs.max_nc = (int)wave_max_u32((uint32_t)max_nc);
+        wave_sync_lds();
+    }
 }
 
 // Merge of the candidates of one draft row by one wave.  Candidate (tile t, slot s)
 // is gathered by lane (s*nt + t) mod 64 into register u = (s*nt + t) / 64, so every
 // load address is known up front and all loads of a row are in flight together.
 constexpr int kCandRegs = 24;    // register slots per lane: up to 1536 candidates per row
-constexpr int kMaxMergeTiles = 512;
 
 struct TopfScratch {
     uint64_t surv[kSurvivorCap];  // keys at or above the value threshold
     uint64_t rank[kWave];         // the top F, placed by rank
+    uint32_t bins[256];           // value histogram of the select
     uint8_t nc[kMaxMergeTiles];   // candidates per tile
 };
 
-// The largest 32-bit value part T such that at least F of the nonzero keys have a
-// value part >= T (the F-th largest value, ties counted), by the same radix select as
-// wave_select_regs restricted to the value bits; 0 when there are at most F keys.
+// The largest 32-bit value part T such that at least F of the nonzero keys among the
+// first U slots have a value part >= T (the F-th largest value, ties counted); 0 when
+// there are at most F keys.  Bits below the common prefix of the keys are resolved 8
+// at a time, most significant first: each step counts the keys that match the value
+// prefix found so far in a 256-bin LDS histogram of their next 8 bits and keeps the
+// bin that holds the rank still sought.
 template <int KREG>
-__device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int F) {
+__device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, int F, uint32_t* bins) {
+    U = uniform(U);
+    const int lane = lane_id();
     int n = 0;
     uint32_t orv = 0u, andv = ~0u;
 #pragma unroll
     for (int u = 0; u < KREG; ++u) {
-        n += wave_popc(k[u] != 0ull);
-        if (k[u] != 0ull) {
-            orv |= (uint32_t)(k[u] >> 32);
-            andv &= (uint32_t)(k[u] >> 32);
+        if (u < U) {
+            n += wave_popc(k[u] != 0ull);
+            if (k[u] != 0ull) {
+                orv |= (uint32_t)(k[u] >> 32);
+                andv &= (uint32_t)(k[u] >> 32);
+            }
         }
     }
     if (n <= F) return 0u;
@@ -128,18 +162,58 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int F) {
         orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
         andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
     }
-    uint32_t diff = orv ^ andv;
-    uint32_t T = andv & ~diff;
-    while (diff) {
-        const int bit = 31 - __clz(diff);
-        diff &= ~(1u << bit);
-        const uint64_t cand = (uint64_t)(T | (1u << bit)) << 32;
-        int cnt = 0;
+    orv = uniform(orv);
+    andv = uniform(andv);
+    const uint32_t diff = orv ^ andv;
+    if (diff == 0u) return andv;
+    int hi = 32 - __clz(diff);                               // bits [hi, 32) are common
+    uint32_t prefix = hi >= 32 ? 0u : (andv >> hi) << hi;
+    int need = F;
+    while (hi > 0) {
+        const int shift = hi > 8 ? hi - 8 : 0;
+        const uint32_t wmask = (1u << (hi - shift)) - 1u;
 #pragma unroll
-        for (int u = 0; u < KREG; ++u) cnt += wave_popc(k[u] >= cand);
-        if (cnt >= F) T |= 1u << bit;
+        for (int j = 0; j < 256 / kWave; ++j) bins[j * kWave + lane] = 0u;
+        wave_sync_lds();
+#pragma unroll
+        for (int u = 0; u < KREG; ++u) {
+            if (u < U) {
+                const uint32_t h = (uint32_t)(k[u] >> 32);
+                const bool match = k[u] != 0ull && (hi >= 32 || (h >> hi) == (prefix >> hi));
+                if (match) atomicAdd(&bins[(h >> shift) & wmask], 1u);
+            }
+        }
+        wave_sync_lds();
+        // lane l holds bins 4l .. 4l+3; counts of the bins above each one
+        uint32_t c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = bins[4 * lane + j];
+        const int lane_sum = (int)(c[0] + c[1] + c[2] + c[3]);
+        int suf = lane_sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_down(suf, off, kWave);
+            if (lane + off < kWave) suf += y;
+        }
+        int above = suf - lane_sum;  // keys in the bins of higher lanes
+        int hit_bin = -1, hit_above = 0;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            if (hit_bin < 0 && above < need && need <= above + (int)c[j]) {
+                hit_bin = 4 * lane + j;
+                hit_above = above;
+            }
+            above += (int)c[j];
+        }
+        const uint64_t hm = __ballot(hit_bin >= 0);
+        const int src = __ffsll((long long)hm) - 1;
+        const int bsel = uniform(__shfl(hit_bin, src, kWave));
+        need -= uniform(__shfl(hit_above, src, kWave));
+        prefix |= (uint32_t)bsel << shift;
+        hi = shift;
+        wave_sync_lds();
     }
-    return T;
+    return prefix;
 }
 
 // Sorts the n <= kSurvivorCap distinct keys in sc.surv by rank and returns lane j =
@@ -172,17 +246,21 @@ __device__ inline uint64_t rank_sort_lds(TopfScratch& sc, int n, int F) {
     return key;
 }
 
-// Appends the keys of k[] that satisfy keep (in register, then lane order) to sc.surv;
-// returns the count (keys past kSurvivorCap are counted, not stored).
+// Appends the nonzero keys >= lo among the first U slots of k[] (in slot, then lane
+// order) to sc.surv; returns their count (keys past kSurvivorCap are counted, not
+// stored).
 template <int KREG>
-__device__ inline int compact_keys(TopfScratch& sc, const uint64_t (&k)[KREG], uint64_t lo) {
+__device__ inline int compact_keys(TopfScratch& sc, const uint64_t (&k)[KREG], int U, uint64_t lo) {
+    U = uniform(U);
     int n = 0;
 #pragma unroll
     for (int u = 0; u < KREG; ++u) {
-        const bool keep = k[u] != 0ull && k[u] >= lo;
-        const int pos = n + lanes_below(keep);
-        if (keep && pos < kSurvivorCap) sc.surv[pos] = k[u];
-        n += wave_popc(keep);
+        if (u < U) {
+            const bool keep = k[u] != 0ull && k[u] >= lo;
+            const int pos = n + lanes_below(keep);
+            if (keep && pos < kSurvivorCap) sc.surv[pos] = k[u];
+            n += wave_popc(keep);
+        }
     }
     wave_sync_lds();
     return n;
@@ -199,58 +277,85 @@ __device__ __forceinline__ uint64_t chunk_key(const uint64_t* cand, int cap, int
     return cand[(int64_t)(c0 + lo) * cap + (j - start[lo])];
 }
 
+// Loads slots s < R of every tile's candidate list (R <= cap, nt*R <= 64*KREG):
+// slot (t, s) goes to lane (s*nt + t) mod 64, register (s*nt + t) / 64.  No load
+// depends on the per-tile counts, so they can be requested with the tile partials.
+template <int KREG>
+__device__ __forceinline__ void gather_slots(const uint64_t* cand, int cap, int nt, int R, uint64_t (&k)[KREG]) {
+    const int lane = lane_id();
+    const int total = nt * R;
+    int t = lane % nt, sl = lane / nt;
+    // opaque to the optimiser: keeps the slot addresses from being hoisted out of a
+    // caller's loop over rows (they would stay live in registers across it)
+    __asm__ volatile("" : "+v"(t), "+v"(sl));
+    const int dt = kWave % nt, ds = kWave / nt;
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) {
+        k[u] = u * kWave + lane < total ? cand[(int64_t)t * cap + sl] : 0ull;
+        t += dt;
+        sl += ds;
+        if (t >= nt) {
+            t -= nt;
+            ++sl;
+        }
+    }
+}
+
+// Keeps the gathered slots that hold a candidate (s < the tile's count, from nc) at
+// or above floor_key; clears the rest.
+template <int KREG>
+__device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, const uint8_t* nc,
+                                           uint64_t floor_key) {
+    const int lane = lane_id();
+    const int total = nt * R;
+    int t = lane % nt, sl = lane / nt;
+    const int dt = kWave % nt, ds = kWave / nt;
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) {
+        const bool live = u * kWave + lane < total && sl < (int)nc[t] && k[u] >= floor_key;
+        k[u] = live ? k[u] : 0ull;
+        t += dt;
+        sl += ds;
+        if (t >= nt) {
+            t -= nt;
+            ++sl;
+        }
+    }
+}
+
+// Top F (sorted, lane j = j-th largest, 0 past F) of the nonzero keys in the first U
+// register slots: the F-th largest value by radix select, the keys at or above it by
+// rank (a whole-key select first when more than kSurvivorCap keys tie there).
+template <int KREG>
+__device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, int F, TopfScratch& sc) {
+    const uint32_t T = wave_select_value<KREG>(k, U, F, sc.bins);
+    const uint64_t lo = (uint64_t)T << 32;
+    int n = compact_keys<KREG>(sc, k, U, lo);
+    if (n > kSurvivorCap) {
+#pragma unroll
+        for (int u = 0; u < KREG; ++u) k[u] = k[u] >= lo ? k[u] : 0ull;
+        const uint64_t T64 = wave_select_regs<KREG>(k, F);
+        n = compact_keys<KREG>(sc, k, U, T64);
+    }
+    return rank_sort_lds(sc, n, F);
+}
+
 // Top F of one draft row from its tiles' candidate keys, by one wave.  The largest
 // tile threshold bounds the row's F-th largest value from below (that tile alone has
 // F elements at or above it), so only keys at or above it can be in the row's top F,
 // and every such key is in its tile's list.  Keys are distinct (they carry the id).
-// Returns lane j = the j-th largest key (0 past F).
+// Returns lane j = the j-th largest key (0 past F).  cs and sc.nc come from
+// row_stats_wave.
 __device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F,
-                                         TopfScratch& sc) {
+                                                  const CandSummary& cs, TopfScratch& sc) {
     const int lane = lane_id();
-    uint32_t tr = 0u;
-    int max_nc = 0;
-    for (int t = lane; t < nt; t += kWave) {
-        const WavePartial q = P[t];
-        tr = max(tr, q.tau);
-        max_nc = max(max_nc, q.ncand);
-        if (t < kMaxMergeTiles) sc.nc[t] = (uint8_t)q.ncand;
-    }
-    tr = wave_max_u32(tr);
-    max_nc = (int)wave_max_u32((uint32_t)max_nc);
-    const uint64_t floor_key = (uint64_t)tr << 32;
-    wave_sync_lds();
-    const int U = (int)(((int64_t)nt * max_nc + kWave - 1) / kWave);
-
-    if (nt <= kMaxMergeTiles && U <= kCandRegs) {
+    const uint64_t floor_key = (uint64_t)cs.tr << 32;
+    const int R = cs.max_nc;
+    if (nt <= kMaxMergeTiles && (int64_t)nt * R <= (int64_t)kWave * kCandRegs) {
         uint64_t k[kCandRegs];
-        int t = lane % nt, sl = lane / nt;
-        // opaque to the optimiser: keeps the 24 slot addresses from being hoisted out of
-        // a caller's loop over rows (they would stay live in registers across it)
-        __asm__ volatile("" : "+v"(t), "+v"(sl));
-        const int dt = kWave % nt, ds = kWave / nt;
-#pragma unroll
-        for (int u = 0; u < kCandRegs; ++u) {
-            uint64_t x = 0ull;
-            if (u < U && sl < (int)sc.nc[t]) x = cand[(int64_t)t * cap + sl];
-            k[u] = x >= floor_key ? x : 0ull;
-            t += dt;
-            sl += ds;
-            if (t >= nt) {
-                t -= nt;
-                ++sl;
-            }
-        }
-        const uint32_t T = wave_select_value<kCandRegs>(k, F);
-        const uint64_t lo = (uint64_t)T << 32;
-        int n = compact_keys<kCandRegs>(sc, k, lo);
-        if (n > kSurvivorCap) {
-            // many keys tie at the threshold value: select on the whole key
-#pragma unroll
-            for (int u = 0; u < kCandRegs; ++u) k[u] = k[u] >= lo ? k[u] : 0ull;
-            const uint64_t T64 = wave_select_regs<kCandRegs>(k, F);
-            n = compact_keys<kCandRegs>(sc, k, T64);
-        }
-        return rank_sort_lds(sc, n, F);
+        gather_slots<kCandRegs>(cand, cap, nt, R, k);
+        mask_slots<kCandRegs>(k, nt, R, sc.nc, floor_key);
+        return select_sorted<kCandRegs>(k, (nt * R + kWave - 1) / kWave, F, sc);
     }
 
     // Rows with more candidates than register slots: exact selection by F rounds of a
@@ -287,13 +392,11 @@ __device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const ui
     return key;
 }
 
-// Cache ids (sorted) and cached mass M = sum of q(x) over them, of one draft row.
-__device__ __forceinline__ double cache_row_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F, float mq,
-                                        double sq, float c, int greedy, int32_t* ids_out, int* ids_lds,
-                                        TopfScratch& sc) {
+// Cache ids and cached mass M = sum of q(x) over them, of one draft row, from its
+// sorted top-F keys (lane j = j-th largest).
+__device__ __forceinline__ double finish_cache_row(uint64_t key, int F, float mq, double sq, float c, int greedy,
+                                                   int32_t* ids_out, int* ids_lds) {
     const int lane = lane_id();
-    if (F <= 0) return 0.0;
-    const uint64_t key = row_topf_wave(P, cand, nt, cap, F, sc);
     const int id = key ? (int)key_id(key) : -1;
     if (lane < F) {
         ids_out[lane] = id;
@@ -352,11 +455,13 @@ struct DraftProbe {
     float u;
 };
 
+// What testing draft token d_i of sequence b needs, loaded ahead of the row statistics:
+// the token, both models' logits at it (when d_i is in range and T > 0) and the
+// acceptance uniform.
 template <int DT>
-__device__ inline DraftProbe probe_draft(const int32_t* draft, const char* p_logits, const char* q_logits,
-                                         int64_t ld_bytes, int b, int K, int V, int greedy, uint64_t seed,
-                                         uint64_t round) {
-    const int i = lane_id();
+__device__ __forceinline__ DraftProbe probe_draft(const int32_t* draft, const char* p_logits, const char* q_logits,
+                                                  int64_t ld_bytes, int b, int i, int K, int V, int greedy,
+                                                  uint64_t seed, uint64_t round) {
     DraftProbe pr;
     pr.d = i < K ? draft[(int64_t)b * K + i] : 0;
     pr.zp = pr.zq = 0.f;
@@ -369,19 +474,17 @@ __device__ inline DraftProbe probe_draft(const int32_t* draft, const char* p_log
     return pr;
 }
 
-// Verification of the K draft tokens of sequence b by one wave: lane i < K tests
-// position i with that position's row statistics.  Returns the accepted length k
-// (same in every lane); writes accept_prob and the OR of the error bits to *errs.
-__device__ inline int verify_wave(int b, int K, int V, const DraftProbe& pr, float mp, double sp, int argp, float mq,
-                                  double sq, double Zi, bool in_cache, float C, float c, int greedy,
-                                  float* accept_prob, int* errs) {
-    const int i = lane_id();
-    const bool act = i < K;
+// Lossless test of one draft token d ~ q' against the target p: accepted when
+// u < p(d) / q'(d) with q'(d) = q(d) (C if d is cached) / Z; at T = 0 accepted when d
+// is the target argmax.  *ratio gets p/q' (0 when not testable), *err the error bits.
+__device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp, double sp, int argp, float mq,
+                                           double sq, double Zi, bool in_cache, float C, float c, int greedy,
+                                           double* ratio_out, int* err_out) {
     const int d = pr.d;
     int err = 0;
-    bool ok = act;
+    bool ok = true;
     double ratio = 0.0;
-    if (act && (d < 0 || d >= V)) {
+    if (d < 0 || d >= V) {
         err |= kErrTokenRange;
         ok = false;
     }
@@ -401,21 +504,15 @@ __device__ inline int verify_wave(int b, int K, int V, const DraftProbe& pr, flo
             }
         }
     }
-    bool acc = false;
-    if (ok) acc = greedy ? ratio == 1.0 : (double)pr.u < ratio;
-    const uint64_t rej = __ballot(act && !acc);
-    const int k = rej ? (__ffsll((long long)rej) - 1) : K;
-    if (act && accept_prob) accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
-    int e = err;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) e |= __shfl_xor(e, m, kWave);
-    *errs = e;
-    return k;
+    *ratio_out = ratio;
+    *err_out = err;
+    return ok && (greedy ? ratio == 1.0 : (double)pr.u < ratio);
 }
 
 // ============================================================================ pass 1
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
+    __shared__ uint64_t cand_stage[kWavesPerBlock][kStageCap];
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -434,20 +531,23 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     const int V = a.V;
     const float c = a.c;
 
-    float x[kVecPerLane][N];
-    {
-        u32x4 raw[kVecPerLane];
-        load_tile<DT, VEC>(row, tile0, V, lane, raw);
-#pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) unpack_vec<DT>(raw[j], x[j]);
-    }
+    // The tile stays in its raw 16-byte vectors (32 registers for bf16, not 64) and is
+    // widened element by element in each use.
+    u32x4 raw[kVecPerLane];
+    load_tile<DT, VEC>(row, tile0, V, lane, raw);
 
+    float vmax[kVecPerLane];  // maximum of each of the lane's vectors
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kVecPerLane; ++j)
+    for (int j = 0; j < kVecPerLane; ++j) {
+        vmax[j] = vec_elem<DT>(raw[j], 0);
 #pragma unroll
-        for (int e = 0; e < N; ++e) m = fmaxf(m, x[j][e]);
+        for (int e = 1; e < N; ++e) vmax[j] = fmaxf(vmax[j], vec_elem<DT>(raw[j], e));
+        m = fmaxf(m, vmax[j]);
+    }
     const float m_lane = m;
+    // each phase widens the elements afresh rather than keeping 64 widened values live
+    opaque_regs(raw);
 
     int arg = INT_MAX;
     if (a.want_arg) {
@@ -456,7 +556,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
 #pragma unroll
             for (int e = 0; e < N; ++e) {
                 const int64_t id = tile0 + (int64_t)(j * kWave + lane) * N + e;
-                if (arg == INT_MAX && id < V && x[j][e] == m_lane) arg = (int)id;
+                if (arg == INT_MAX && id < V && vec_elem<DT>(raw[j], e) == m_lane) arg = (int)id;
             }
     }
 
@@ -468,7 +568,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         for (int j = 0; j < kVecPerLane; ++j) {
             float tt[N];
 #pragma unroll
-            for (int e = 0; e < N; ++e) tt[e] = term(x[j][e], c, o);
+            for (int e = 0; e < N; ++e) tt[e] = term(vec_elem<DT>(raw[j], e), c, o);
 #pragma unroll
             for (int w = N / 2; w >= 1; w >>= 1)
 #pragma unroll
@@ -481,9 +581,12 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             for (int j = 0; j < w; ++j) vs[j] += vs[j + w];
         s = (double)vs[0];
     }
+    opaque_regs(raw);
 
     // ---- candidate keys of this tile (draft rows of the cache): every element at or
-    // above the F-th largest lane maximum.
+    // above the F-th largest lane maximum.  Only vectors whose maximum reaches the
+    // threshold in some lane are examined; keys are staged in LDS element position by
+    // element position and copied out with one coalesced store per 64 keys.
     const int F = a.F[i];
     uint32_t tau = 0u;
     int ncand = 0;
@@ -493,40 +596,31 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         const float tauf = tau ? unord32(tau) : -INFINITY;
         const int id0 = (int)tile0 + lane * N;
         const bool full = tile0 + kTile<DT> <= V;
-        uint32_t mask[kVecPerLane];
-        int cnt = 0;
+        uint64_t* out = a.cand + ((r * a.nt) + t) * a.cap;
+        uint64_t* stage = cand_stage[wave];
+        const int cap = a.cap;
+        const uint64_t below = (1ull << lane) - 1ull;
+        int n = 0;
 #pragma unroll
         for (int j = 0; j < kVecPerLane; ++j) {
-            uint32_t mk = 0u;
+            if (__ballot(vmax[j] >= tauf) == 0ull) continue;
 #pragma unroll
-            for (int e = 0; e < N; ++e)
-                mk |= (x[j][e] >= tauf && (full || id0 + j * kWave * N + e < V)) ? (1u << e) : 0u;
-            mask[j] = mk;
-            cnt += __popc(mk);
-        }
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int y = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += y;
-        }
-        const int tot = __shfl(incl, kWave - 1, kWave);
-        uint64_t* out = a.cand + ((r * a.nt) + t) * a.cap;
-        if (tot <= a.cap) {
-            int pos = incl - cnt;
-#pragma unroll
-            for (int j = 0; j < kVecPerLane; ++j) {
-                uint32_t mk = mask[j];
-                while (mk) {
-                    const int e = __ffs(mk) - 1;
-                    mk &= mk - 1u;
-                    float v = x[j][0];
-#pragma unroll
-                    for (int q = 1; q < N; ++q) v = (e == q) ? x[j][q] : v;
-                    out[pos++] = cand_key(v, (uint32_t)(id0 + j * kWave * N + e));
+            for (int e = 0; e < N; ++e) {
+                const float v = vec_elem<DT>(raw[j], e);
+                const int id = id0 + j * kWave * N + e;
+                const bool hit = v >= tauf && (full || id < V);
+                const uint64_t mk = __ballot(hit);
+                if (mk) {
+                    const int pos = n + __popcll(mk & below);
+                    if (hit && pos < kStageCap) stage[pos] = cand_key(v, (uint32_t)id);
+                    n += __popcll(mk);
                 }
             }
-            ncand = tot;
+        }
+        wave_sync_lds();
+        if (n <= min(cap, kStageCap)) {
+            for (int q = lane; q < n; q += kWave) out[q] = stage[q];
+            ncand = n;
         } else {
             // More tied candidates than slots: store this tile's exact top F, found by
             // F rounds of a wave maximum below the previous key (re-reading the tile).
@@ -578,91 +672,156 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
 }
 
 // ============================================================================ finalise
-constexpr int kFinWaves = 8;
-constexpr int kFinBlock = kFinWaves * kWave;
+// Partial of tile `lane` of a row (the identity past nt), for rows of at most 64 tiles.
+__device__ __forceinline__ WavePartial lane_partial(const WavePartial* P, int nt) {
+    WavePartial q;
+    if (lane_id() < nt) {
+        q = P[lane_id()];
+    } else {
+        q.m = -INFINITY;
+        q.arg = INT_MAX;
+        q.s = 0.0;
+        q.tau = 0u;
+        q.ncand = 0;
+        q.pad0 = q.pad1 = 0;
+    }
+    return q;
+}
 
-struct FinShared {
-    float m[2][kMaxK + 1];
-    double s[2][kMaxK + 1];
-    int arg[2][kMaxK + 1];
-    double Z[kMaxK + 1];
-    int ids[kMaxK + 1][kMaxF];
-    TopfScratch tf[kFinWaves];
-};
+// Softmax statistics from one tile partial per lane; the same merges in the same order
+// as row_stats_wave for a row of at most 64 tiles.
+__device__ __forceinline__ void stats_from_lanes(const WavePartial& q, float c, float& m, double& s, int& arg) {
+    m = -INFINITY;
+    s = 0.0;
+    arg = INT_MAX;
+    merge_stats(m, s, arg, q.m, q.s, q.arg, c);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(m, off, kWave);
+        const double s2 = __shfl_xor(s, off, kWave);
+        const int a2 = __shfl_xor(arg, off, kWave);
+        merge_stats(m, s, arg, m2, s2, a2, c);
+    }
+}
 
-// One block of 8 waves per sequence.  Wave w < K+1 takes draft row w (statistics,
-// cache ids, cached mass M, Saguaro Z = 1 - (1 - C) M), the next K+1 waves the target
-// rows; the last wave loads what verification needs first and verifies once every
-// row is done.
+// Accepted length of sequence b from the per-position test outcomes (the first
+// rejected position, K if none) and the OR of their error bits; every lane returns
+// both.  Outcomes: bit 0 accepted, the bits above it the error bits.
+__device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int K, int* errs) {
+    const int lane = lane_id();
+    const int v = lane < K ? vflag[(int64_t)b * K + lane] : 1;
+    const uint64_t rm = __ballot((v & 1) == 0);
+    int e = v >> 1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) e |= __shfl_xor(e, m, kWave);
+    *errs = e;
+    return rm ? (__ffsll((long long)rm) - 1) : K;
+}
+
+// One wave per (sequence b, position i): the statistics of target row i and draft
+// row i, the cache ids of draft row i, its cached mass M, the Saguaro normaliser
+// Z = 1 - (1 - C) M and the lossless test of draft token d_i.  For rows of at most 64
+// tiles the tile partials, the first 2 F_i + 2 candidate slots of every tile and the
+// logits at d_i are requested together.
 template <int DT>
-__global__ __launch_bounds__(kFinBlock) void finalize_seq_kernel(const SeqFinal f) {
-    __shared__ FinShared fs;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int b = blockIdx.x;
-    const int K = f.K, K1 = K + 1;
-    const WavePartial* part = f.part + (int64_t)b * 2 * K1 * f.nt;
-    const bool verifier = wave == kFinWaves - 1;
-    DraftProbe pr{};
-    if (verifier)
-        pr = probe_draft<DT>(f.draft, f.p_logits, f.q_logits, f.ld_bytes, b, K, f.V, f.greedy, f.seed, f.round);
-
-    for (int rr = wave; rr < 2 * K1; rr += kFinWaves) {
-        const int model = rr < K1 ? 1 : 0, i = rr < K1 ? rr : rr - K1;
-        const int64_t r = (int64_t)b * K1 + i;
-        float m;
-        double s;
-        int arg;
-        row_stats_wave(part + (int64_t)(model * K1 + i) * f.nt, f.nt, f.c, m, s, arg);
-        s = f.greedy ? 1.0 : std_sum(m, s, f.c);
-        if (lane == 0) {
-            fs.m[model][i] = m;
-            fs.s[model][i] = s;
-            fs.arg[model][i] = arg;
-            if (model) {
-                f.q_max[r] = m;
-                f.q_sum[r] = s;
-                if (f.q_arg) f.q_arg[r] = arg;
-            } else {
-                f.p_max[r] = m;
-                f.p_sum[r] = s;
-                if (f.p_arg) f.p_arg[r] = arg;
-            }
+__global__ __launch_bounds__(kBlock) void finalize_pos_kernel(const SeqFinal f) {
+    __shared__ TopfScratch scr[kWavesPerBlock];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int K = f.K, K1 = K + 1, nt = f.nt;
+    const int g = blockIdx.x * kWavesPerBlock + wave;
+    if (g >= f.B * K1) return;
+    const int b = g / K1, i = g % K1;
+    const WavePartial* part = f.part + (int64_t)b * 2 * K1 * nt;
+    const bool fast = nt <= kWave;
+    TopfScratch& sc = scr[wave];
+    const int64_t r = (int64_t)b * K1 + i;
+    const WavePartial* Pp = part + (int64_t)i * nt;
+    const WavePartial* Pq = part + (int64_t)(K1 + i) * nt;
+    const uint64_t* cr = f.cand + r * nt * f.cap;
+    const int F = f.F[i];
+    const DraftProbe pr =
+        probe_draft<DT>(f.draft, f.p_logits, f.q_logits, f.ld_bytes, b, i, K, f.V, f.greedy, f.seed, f.round);
+    float mp, mq;
+    double sp, sq;
+    int ap, aq;
+    CandSummary cs;
+    uint64_t k[kCandRegs];
+    int Rg = 0;
+    if (fast) {
+        const WavePartial qq = lane_partial(Pq, nt), pp = lane_partial(Pp, nt);
+        if (F > 0) {
+            Rg = min(min(2 * F + 2, f.cap), kWave * kCandRegs / nt);
+            gather_slots<kCandRegs>(cr, f.cap, nt, Rg, k);
         }
-        if (model) {
-            const double M = cache_row_wave(part + (int64_t)(K1 + i) * f.nt, f.cand + r * f.nt * f.cap, f.nt, f.cap,
-                                            f.F[i], m, s, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i],
-                                            fs.ids[i], fs.tf[wave]);
-            const double Z = 1.0 - (1.0 - (double)f.C) * M;
-            if (lane == 0) {
-                f.cache_mass[r] = M;
-                f.Z[r] = Z;
-                fs.Z[i] = Z;
-            }
+        stats_from_lanes(qq, f.c, mq, sq, aq);
+        stats_from_lanes(pp, f.c, mp, sp, ap);
+        cs.tr = wave_max_u32(qq.tau);
+        cs.max_nc = (int)wave_max_u32((uint32_t)qq.ncand);
+        if (lane < nt) sc.nc[lane] = (uint8_t)qq.ncand;
+        wave_sync_lds();
+    } else {
+        CandSummary unused;
+        row_stats_wave(Pq, nt, f.c, mq, sq, aq, true, cs, sc.nc);
+        row_stats_wave(Pp, nt, f.c, mp, sp, ap, false, unused, nullptr);
+    }
+    sq = f.greedy ? 1.0 : std_sum(mq, sq, f.c);
+    sp = f.greedy ? 1.0 : std_sum(mp, sp, f.c);
+    if (lane == 0) {
+        f.q_max[r] = mq;
+        f.q_sum[r] = sq;
+        if (f.q_arg) f.q_arg[r] = aq;
+        f.p_max[r] = mp;
+        f.p_sum[r] = sp;
+        if (f.p_arg) f.p_arg[r] = ap;
+    }
+    double M = 0.0;
+    int my_id = -1;
+    if (F > 0) {
+        uint64_t key;
+        if (fast && cs.max_nc <= Rg) {
+            mask_slots<kCandRegs>(k, nt, Rg, sc.nc, (uint64_t)cs.tr << 32);
+            key = select_sorted<kCandRegs>(k, (nt * cs.max_nc + kWave - 1) / kWave, F, sc);
+        } else {
+            key = row_topf_wave(Pq, cr, nt, f.cap, F, cs, sc);
+        }
+        M = finish_cache_row(key, F, mq, sq, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i], nullptr);
+        my_id = lane < F && key ? (int)key_id(key) : -1;
+    }
+    const double Z = 1.0 - (1.0 - (double)f.C) * M;
+    if (lane == 0) {
+        f.cache_mass[r] = M;
+        f.Z[r] = Z;
+    }
+    if (i < K) {
+        const bool in_cache = __ballot(my_id >= 0 && my_id == pr.d) != 0ull;
+        double ratio;
+        int err;
+        const bool acc = test_draft(pr, f.V, mp, sp, ap, mq, sq, Z, in_cache, f.C, f.c, f.greedy, &ratio, &err);
+        if (lane == 0) {
+            f.vflag[(int64_t)b * K + i] = (acc ? 1 : 0) | (err << 1);
+            if (f.accept_prob) f.accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
         }
     }
-    __syncthreads();
+}
 
-    if (!verifier) return;
-    const int i = lane;
-    const int ic = i < K ? i : 0;
-    bool in_cache = false;
-    for (int j = 0; j < f.F[ic]; ++j) in_cache |= fs.ids[ic][j] == pr.d;
+// T = 0: one wave per sequence takes the accepted length from the test outcomes, the
+// bonus (target argmax at that position) and the cache lookup.
+__global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int b = blockIdx.x * kWavesPerBlock + wave;
+    if (b >= f.B) return;
+    const int K = f.K;
     int errs;
-    const int k = verify_wave(b, K, f.V, pr, fs.m[0][ic], fs.s[0][ic], fs.arg[0][ic], fs.m[1][ic], fs.s[1][ic],
-                              fs.Z[ic], in_cache, f.C, f.c, f.greedy, f.accept_prob, &errs);
+    const int k = accepted_length(f.vflag, b, K, &errs);
+    const int tok = f.p_arg[(int64_t)b * (K + 1) + k];
+    const int my_id = cached_id(f.cache_ids, b, f.Bf, k, K, f.F, f.O);
     if (lane == 0) {
         f.accept_len[b] = k;
         if (f.dev_err && errs) f.dev_err[b] |= errs;
+        f.bonus[b] = tok;
+        if (f.resid_mass) f.resid_mass[b] = 1.0;
     }
-    if (f.greedy) {
-        const int tok = fs.arg[0][k];
-        if (lane == 0) {
-            f.bonus[b] = tok;
-            if (f.resid_mass) f.resid_mass[b] = 1.0;
-        }
-        const int my_id = lane < f.F[k] ? fs.ids[k][lane] : -1;
-        lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens);
-    }
+    lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens);
 }
 
 // ============================================================================ pass 2
@@ -789,10 +948,12 @@ __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const c
     }
 }
 
-__device__ inline void pass2_group(const Pass2Args& a, int g, int& b, int& pos, bool& valid) {
+__device__ inline void pass2_group(const Pass2Args& a, int g, int& b, int& pos, bool& valid, int* errs = nullptr) {
     if (a.mode == 0) {
         b = g;
-        pos = a.accept_len[b];
+        int e = 0;
+        pos = a.vflag ? accepted_length(a.vflag, b, a.K, &e) : a.accept_len[b];
+        if (errs) *errs = e;
         valid = pos >= 0 && pos <= a.K;
     } else {
         b = g / a.K;
@@ -906,9 +1067,9 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int g = blockIdx.x * kWavesPerBlock + wave;
     if (g >= ngroups) return;
-    int b, pos;
+    int b, pos, verrs = 0;
     bool valid;
-    pass2_group(a, g, b, pos, valid);
+    pass2_group(a, g, b, pos, valid, &verrs);
     const int K = a.K;
     const int nt = a.nt;
     const double2* seg = a.seg + (int64_t)g * nt;
@@ -985,6 +1146,10 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
         if (a.mode == 0) {
             a.out_tok[b] = tok;
             if (a.resid_mass) a.resid_mass[b] = Zused;
+            if (a.vflag) {
+                a.accept_len_out[b] = pos;
+                if (a.dev_err && verrs) a.dev_err[b] |= verrs;
+            }
             if (!valid && a.dev_err) a.dev_err[b] |= kErrLenRange;
         } else {
             a.out_tok[(int64_t)b * K + pos] = tok;
@@ -1005,7 +1170,8 @@ __global__ __launch_bounds__(kBlock) void combine_stats_kernel(const Pass1Args a
     float m;
     double s;
     int arg;
-    row_stats_wave(a.part + r * a.nt, a.nt, a.c, m, s, arg);
+    CandSummary cs;
+    row_stats_wave(a.part + r * a.nt, a.nt, a.c, m, s, arg, false, cs, nullptr);
     if (lane == 0) {
         m_out[r] = m;
         s_out[r] = a.greedy ? 1.0 : std_sum(m, s, a.c);
@@ -1021,8 +1187,17 @@ __global__ __launch_bounds__(kBlock) void combine_topf_kernel(const Pass1Args a,
     const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (r >= (int64_t)a.B * a.K1) return;
     const int b = (int)(r / a.K1), i = (int)(r % a.K1);
-    const double M = cache_row_wave(a.part + r * a.nt, a.cand + r * a.nt * a.cap, a.nt, a.cap, a.F[i], q_max[r],
-                                    q_sum[r], a.c, a.greedy, cache_ids + (int64_t)b * Bf + a.O[i], nullptr, sc[wave]);
+    float m;
+    double s;
+    int arg;
+    CandSummary cs;
+    row_stats_wave(a.part + r * a.nt, a.nt, a.c, m, s, arg, true, cs, sc[wave].nc);
+    const int F = a.F[i];
+    double M = 0.0;
+    if (F > 0) {
+        const uint64_t key = row_topf_wave(a.part + r * a.nt, a.cand + r * a.nt * a.cap, a.nt, a.cap, F, cs, sc[wave]);
+        M = finish_cache_row(key, F, q_max[r], q_sum[r], a.c, a.greedy, cache_ids + (int64_t)b * Bf + a.O[i], nullptr);
+    }
     if (lane == 0) cache_mass[r] = M;
 }
 
@@ -1070,9 +1245,10 @@ __global__ void verify_kernel(const char* p_logits, const char* q_logits, int B,
     if (b >= B) return;
     const int lane = lane_id();
     const int K1 = K + 1;
-    const int ic = lane < K ? lane : 0;
+    const bool act = lane < K;
+    const int ic = act ? lane : 0;
     const int64_t r = (int64_t)b * K1 + ic;
-    const DraftProbe pr = probe_draft<DT>(draft, p_logits, q_logits, ld_bytes, b, K, V, greedy, seed, round);
+    const DraftProbe pr = probe_draft<DT>(draft, p_logits, q_logits, ld_bytes, b, lane, K, V, greedy, seed, round);
     bool in_cache = false;
     const int32_t* ids = cache_ids + (int64_t)b * Bf + fo.O[ic];
     for (int j = 0; j < fo.F[ic]; ++j) in_cache |= ids[j] == pr.d;
@@ -1080,11 +1256,18 @@ __global__ void verify_kernel(const char* p_logits, const char* q_logits, int B,
     const double sp = greedy ? 1.0 : p_sum[r], sq = greedy ? 1.0 : q_sum[r];
     const int argp = greedy ? p_arg[r] : 0;
     const double Zi = greedy ? 1.0 : Z[r];
-    int errs;
-    const int k = verify_wave(b, K, V, pr, mp, sp, argp, mq, sq, Zi, in_cache, C, c, greedy, accept_prob, &errs);
+    double ratio = 0.0;
+    int err = 0;
+    bool acc = false;
+    if (act) acc = test_draft(pr, V, mp, sp, argp, mq, sq, Zi, in_cache, C, c, greedy, &ratio, &err);
+    const uint64_t rej = __ballot(act && !acc);
+    const int k = rej ? (__ffsll((long long)rej) - 1) : K;
+    if (act && accept_prob) accept_prob[(int64_t)b * K + lane] = (float)(ratio < 1.0 ? ratio : 1.0);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, kWave);
     if (lane == 0) {
         accept_len[b] = k;
-        if (dev_err && errs) dev_err[b] |= errs;
+        if (dev_err && err) dev_err[b] |= err;
     }
 }
 
@@ -1151,11 +1334,17 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
     });
 }
 
-hipError_t launch_finalize_seq(int dtype, const SeqFinal& f, hipStream_t st) {
+hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
+    const int grid = (f.B * (f.K + 1) + kWavesPerBlock - 1) / kWavesPerBlock;
     if (dtype == 1)
-        finalize_seq_kernel<1><<<f.B, kFinBlock, 0, st>>>(f);
+        finalize_pos_kernel<1><<<grid, kBlock, 0, st>>>(f);
     else
-        finalize_seq_kernel<0><<<f.B, kFinBlock, 0, st>>>(f);
+        finalize_pos_kernel<0><<<grid, kBlock, 0, st>>>(f);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish_greedy(const SeqFinal& f, hipStream_t st) {
+    finish_greedy_kernel<<<(f.B + kWavesPerBlock - 1) / kWavesPerBlock, kBlock, 0, st>>>(f);
     return hipGetLastError();
 }
 
