@@ -198,30 +198,74 @@ __device__ __forceinline__ uint64_t uniform(uint64_t v) {
     return ((uint64_t)uniform((uint32_t)(v >> 32)) << 32) | uniform((uint32_t)v);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+// ---------------------------------------------------------------------------- wave reductions
+// Reductions over the whole wave (all lanes active), result uniform.  Four row shifts
+// by 1, 2, 4 and 8 lanes (DPP moves, no LDS round trip) reduce each 16-lane row into
+// its last lane; lanes 15, 31, 47 and 63 are then combined as (r0 . r1) . (r2 . r3).
+// A shift that would read from outside the row reads the identity instead.  The
+// combination order is fixed, so floating-point results are reproducible.
+enum { kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118 };
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t ident, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t ident, Op op) {
+    v = op(v, dpp_u32<kRowShr1>(ident, v));
+    v = op(v, dpp_u32<kRowShr2>(ident, v));
+    v = op(v, dpp_u32<kRowShr4>(ident, v));
+    v = op(v, dpp_u32<kRowShr8>(ident, v));
+    return op(op(lane_u32(v, 15), lane_u32(v, 31)), op(lane_u32(v, 47), lane_u32(v, 63)));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
-    return uniform(v);
+    return wave_reduce_u32(v, 0u, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+__device__ __forceinline__ int wave_min_i32(int v) {
+    return (int)wave_reduce_u32((uint32_t)v, 0x7FFFFFFFu,
+                                [](uint32_t x, uint32_t y) { return (int)x < (int)y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0u, [](uint32_t x, uint32_t y) { return x | y; });
+}
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
+    return wave_reduce_u32(v, ~0u, [](uint32_t x, uint32_t y) { return x & y; });
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(v), 0xFF800000u, [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    }));
 }
 __device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
-    return v;
+    return ((uint64_t)wave_or_u32((uint32_t)(v >> 32)) << 32) | wave_or_u32((uint32_t)v);
 }
 __device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v &= __shfl_xor(v, m, kWave);
-    return v;
+    return ((uint64_t)wave_and_u32((uint32_t)(v >> 32)) << 32) | wave_and_u32((uint32_t)v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64_zero(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL>(0u, (uint32_t)b), hi = dpp_u32<CTRL>(0u, (uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double lane_f64(double v, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    return __longlong_as_double((long long)(((uint64_t)lane_u32((uint32_t)(b >> 32), l) << 32) |
+                                            lane_u32((uint32_t)b, l)));
+}
+// Sum over the wave in fp64 (fixed order).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64_zero<kRowShr1>(v);
+    v += dpp_f64_zero<kRowShr2>(v);
+    v += dpp_f64_zero<kRowShr4>(v);
+    v += dpp_f64_zero<kRowShr8>(v);
+    return (lane_f64(v, 15) + lane_f64(v, 31)) + (lane_f64(v, 47) + lane_f64(v, 63));
 }
 __device__ __forceinline__ int wave_popc(bool p) { return __popcll(__ballot(p)); }
 // Number of lanes below this one with p set.
@@ -339,8 +383,8 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
         }
     }
     if (n <= F) return 0ull;
-    orv = uniform(wave_or64(orv));
-    andv = uniform(wave_and64(andv));
+    orv = wave_or64(orv);
+    andv = wave_and64(andv);
     uint64_t diff = orv ^ andv;
     uint64_t T = andv & ~diff;
     while (diff) {
@@ -371,8 +415,8 @@ __device__ inline uint64_t wave_select_lds(const uint64_t* keys, int n, int F) {
         }
     }
     if (cnt0 <= F) return 0ull;
-    orv = uniform(wave_or64(orv));
-    andv = uniform(wave_and64(andv));
+    orv = wave_or64(orv);
+    andv = wave_and64(andv);
     uint64_t diff = orv ^ andv;
     uint64_t T = andv & ~diff;
     while (diff) {
@@ -394,13 +438,8 @@ __device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
     const int n = wave_popc(k != 0u);
     if (n <= F) return 0u;
     uint32_t orv = k, andv = k ? k : ~0u;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
-        andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
-    }
-    orv = uniform(orv);
-    andv = uniform(andv);
+    orv = wave_or_u32(orv);
+    andv = wave_and_u32(andv);
     uint32_t diff = orv ^ andv;
     uint32_t T = andv & ~diff;
     while (diff) {

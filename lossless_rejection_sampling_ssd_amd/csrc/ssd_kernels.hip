@@ -70,6 +70,17 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// (max, sum relative to o(max), lowest-id argmax) of the whole wave from one partial
+// per lane, each lane's sum relative to the offset of its own maximum; uniform result.
+// Partial sums are moved to the common offset exactly (ldexp) and added in fp64.
+__device__ __forceinline__ void wave_stats(float m_l, double s_l, int arg_l, float c, float& m, double& s, int& arg) {
+    m = wave_max_f32(m_l);
+    const float o = offset_of(m, c);
+    const double sl = m_l == -INFINITY ? 0.0 : ldexp(s_l, (int)(offset_of(m_l, c) - o));
+    s = wave_sum_f64(sl);
+    arg = wave_min_i32(m_l == m ? arg_l : INT_MAX);
+}
+
 // (max, lowest-id argmax, sum relative to o(max)) merge; symmetric bit for bit.
 __device__ __forceinline__ void merge_stats(float& m, double& s, int& arg, float m2, double s2, int a2, float c) {
     if (m2 > m || (m2 == m && a2 < arg)) arg = a2;
@@ -106,13 +117,7 @@ __device__ __forceinline__ void row_stats_wave(const WavePartial* P, int nt, flo
             if (t < kMaxMergeTiles) nc[t] = (uint8_t)q.ncand;
         }
     }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const float m2 = __shfl_xor(m, off, kWave);
-        const double s2 = __shfl_xor(s, off, kWave);
-        const int a2 = __shfl_xor(arg, off, kWave);
-        merge_stats(m, s, arg, m2, s2, a2, c);
-    }
+    wave_stats(m, s, arg, c, m, s, arg);
     cs.tr = 0u;
     cs.max_nc = 0;
     if (with_cands) {
@@ -157,13 +162,8 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, i
         }
     }
     if (n <= F) return 0u;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        orv |= (uint32_t)__shfl_xor((int)orv, m, kWave);
-        andv &= (uint32_t)__shfl_xor((int)andv, m, kWave);
-    }
-    orv = uniform(orv);
-    andv = uniform(andv);
+    orv = wave_or_u32(orv);
+    andv = wave_and_u32(andv);
     const uint32_t diff = orv ^ andv;
     if (diff == 0u) return andv;
     int hi = 32 - __clz(diff);                               // bits [hi, 32) are common
@@ -411,9 +411,7 @@ __device__ __forceinline__ double finish_cache_row(uint64_t key, int F, float mq
             t = (double)term(key_val(key), c, nq.o) * nq.inv;
         }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
-    return t;
+    return wave_sum_f64(t);
 }
 
 // Cache lookup of one verified outcome (k, tok) by one wave, plus the uniform
@@ -652,13 +650,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     }
 
     // ---- tile partial
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off, kWave);
-        const double s2 = __shfl_xor(s, off, kWave);
-        const int a2 = __shfl_xor(arg, off, kWave);
-        merge_stats(m, s, arg, m2, s2, a2, c);
-    }
+    wave_stats(m_lane, s, arg, c, m, s, arg);
     if (lane == 0) {
         WavePartial P;
         P.m = m;
@@ -695,13 +687,7 @@ __device__ __forceinline__ void stats_from_lanes(const WavePartial& q, float c, 
     s = 0.0;
     arg = INT_MAX;
     merge_stats(m, s, arg, q.m, q.s, q.arg, c);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const float m2 = __shfl_xor(m, off, kWave);
-        const double s2 = __shfl_xor(s, off, kWave);
-        const int a2 = __shfl_xor(arg, off, kWave);
-        merge_stats(m, s, arg, m2, s2, a2, c);
-    }
+    wave_stats(m, s, arg, c, m, s, arg);
 }
 
 // Accepted length of sequence b from the per-position test outcomes (the first
@@ -711,10 +697,7 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
     const int lane = lane_id();
     const int v = lane < K ? vflag[(int64_t)b * K + lane] : 1;
     const uint64_t rm = __ballot((v & 1) == 0);
-    int e = v >> 1;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) e |= __shfl_xor(e, m, kWave);
-    *errs = e;
+    *errs = (int)wave_or_u32((uint32_t)(v >> 1));
     return rm ? (__ffsll((long long)rm) - 1) : K;
 }
 
@@ -994,11 +977,8 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
         else
             tile_sums<DT, VEC, kWQprime>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        sw += __shfl_xor(sw, m, kWave);
-        sp += __shfl_xor(sp, m, kWave);
-    }
+    sw = wave_sum_f64(sw);
+    sp = wave_sum_f64(sp);
     if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
 }
 
@@ -1263,8 +1243,7 @@ __global__ void verify_kernel(const char* p_logits, const char* q_logits, int B,
     const uint64_t rej = __ballot(act && !acc);
     const int k = rej ? (__ffsll((long long)rej) - 1) : K;
     if (act && accept_prob) accept_prob[(int64_t)b * K + lane] = (float)(ratio < 1.0 ? ratio : 1.0);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, kWave);
+    err = (int)wave_or_u32((uint32_t)err);
     if (lane == 0) {
         accept_len[b] = k;
         if (dev_err && err) dev_err[b] |= err;
