@@ -4,10 +4,16 @@ MI355X: rounds per second and achieved HBM bandwidth of the vocabulary pass.
 
 One step is one whole round over one batch: softmax statistics of both models,
 top-F speculation cache with geometric fan-out, Saguaro reweighting, lossless
-verification, residual bonus sampling and cache lookup (two HIP kernels).  Inputs
-(seeded synthetic logits, draft tokens from the library's own Saguaro sampler) are
-resident in HBM before timing; the timed loop rotates over distinct logit buffers
-totalling more than the 256 MB last-level cache so that rows come from HBM.
+verification, residual bonus sampling and cache lookup (one ssd_round call: two
+streaming HIP kernels, each followed by a small one).  Inputs (seeded synthetic
+logits, draft tokens from the library's own Saguaro sampler) are resident in HBM
+before timing; the timed loop rotates over distinct logit buffers totalling more
+than the 256 MB last-level cache so that rows come from HBM.
+
+The roofline figure is for pass 1 (the vocabulary pass over all 2 B (K+1) rows),
+timed live with HIP events recorded on the launch stream.  Its HBM traffic comes
+from the rocprofv3 byte counters summarised under profiles/, and is reported only
+while the kernel sources are the ones those counters were taken from.
 
 Prints one JSON line on stdout.  With --gpus above 1 it exits: this build measures
 one GPU.
@@ -23,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass1_kernel_c3_traffic.md")
+KERNEL_SOURCES = ["ssd_kernels.hip", "ssd_device.h", "ssd_kernels.h"]
 
 
 def log(*a):
@@ -41,7 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a plain device copy of 1 GiB (reference for HBM byte counters)")
+                    help="3 copies of 1 GiB instead of 5 (the count the byte-counter calibration expects)")
     return ap.parse_args()
 
 
@@ -142,13 +150,23 @@ def main():
     round_gbps = round_bytes / (ms_per_step * 1e-3) / 1e9
     pass1_gbps = pass1_bytes / (pass1_avg_ms * 1e-3) / 1e9
 
-    if args.copy_calib:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy-calib: 3 x device copy of %d bytes" % (src.numel() * 4))
+    # a plain device copy of 1 GiB in the same run: reference for the HBM byte counters
+    # (rocprofv3 --pmc) and for the achievable streaming rate on this machine
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    ncopy = 3 if args.copy_calib else 5
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(ncopy):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * ncopy / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log("device copy: %d x %d bytes, %.1f GB/s (read + write)" % (ncopy, src.numel() * 4, copy_gbps))
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -178,6 +196,7 @@ def main():
             "round_GBps": round(round_gbps, 1),
             "round_frac_of_peak": round(round_gbps / PEAK_HBM_GBPS, 4),
             "pass1_us": round(pass1_avg_ms * 1e3, 2),
+            "copy_GBps_read_plus_write": round(copy_gbps, 1),
             "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
             "mean_accept_len": round(float(ks.mean()), 3),
             "hit_rate": round(float(hits.mean()), 4),
@@ -189,13 +208,45 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(pass1_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "pass1_kernel (vocabulary pass over all 2*B*(K+1) rows)",
             "bytes_per_launch": int(pass1_bytes),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def kernel_digest():
+    """sha256 over the device sources of the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "lossless_rejection_sampling_ssd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per pass-1 launch from the committed counter summary, or None when
+    it is missing or was taken from other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`-* ")
+        if ":" in line:
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, buf, T, C, F, seconds):

@@ -1,6 +1,6 @@
 // ssd_device.h -- device helpers for the gfx950 kernels of the SSD / Saguaro round:
-// wave64 reductions, the Philox4x64-10 generator, order-preserving keys, bf16 / fp32
-// vector loads, a wave-level radix select and a wave-level bitonic sort.
+// bf16 / fp32 tile loads, order-preserving keys, wave64 reductions (DPP), softmax
+// terms with integer offsets, the Philox4x64-10 generator and wave-level radix selects.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,7 +14,6 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kVecPerLane = 8;   // 16-byte vectors each lane keeps in flight per tile
 constexpr int kMaxK = 16;
 constexpr int kMaxF = 64;
-constexpr int kCandCap = 128;    // top-F candidates one wave may stage in LDS
 
 template <int DT> struct ElemTraits;
 template <> struct ElemTraits<0> {  // fp32
@@ -26,7 +25,6 @@ template <> struct ElemTraits<1> {  // bf16
     static constexpr int kBytes = 2;
 };
 template <int DT> constexpr int kTile = kVecPerLane * kWave * ElemTraits<DT>::kPerVec;  // per wave
-template <int DT> constexpr int kChunk = kWavesPerBlock * kTile<DT>;                     // per block
 
 // ---------------------------------------------------------------------------- loads
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -109,18 +107,6 @@ __device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
     }
     return __uint_as_float(v[e]);
 }
-// The same for an element index known only at run time.
-template <int DT>
-__device__ __forceinline__ float vec_elem_dyn(const u32x4& v, int e) {
-    const int q = DT == 1 ? e >> 1 : e;
-    uint32_t w = v.x;
-    w = q == 1 ? v.y : w;
-    w = q == 2 ? v.z : w;
-    w = q == 3 ? v.w : w;
-    if (DT == 1) w = (e & 1) ? (w & 0xFFFF0000u) : (w << 16);
-    return __uint_as_float(w);
-}
-
 // The kVecPerLane raw vectors one lane owns in a wave tile starting at element t0
 // (vector j covers [t0 + (j*64 + lane)*kPerVec, +kPerVec)), elements at or past V
 // replaced by -inf.  VEC: the row is 16-byte aligned.
@@ -274,38 +260,6 @@ __device__ __forceinline__ int lanes_below(bool p) {
     return __popcll(m & ((1ull << lane_id()) - 1ull));
 }
 
-// (max value, lowest id) reduction.
-__device__ __forceinline__ void arg_merge(float& m, int& a, float m2, int a2) {
-    if (m2 > m || (m2 == m && a2 < a)) {
-        m = m2;
-        a = a2;
-    }
-}
-
-// ---------------------------------------------------------------------------- cross-block data
-// Blocks hand partial results to the last block of their group through memory that
-// may sit in another XCD's L2.  Published values are written and read with
-// agent-scope relaxed atomics (sc1 accesses, coherent across XCDs without the
-// whole-L2 write-back / invalidate an agent-scope fence costs); a writer waits for
-// its stores to complete before it bumps the group's counter.  Every group's
-// published region is padded to whole cache lines and read by one block only.
-template <typename T>
-__device__ __forceinline__ void publish(T* p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T observe(const T* p) {
-    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-__device__ __forceinline__ unsigned arrive(unsigned* counter) {
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ---------------------------------------------------------------------------- softmax terms
 // With c = log2(e)/T every term of a row is 2^{z c - o} for an integer-valued offset
 // o = rint(m c) taken from a maximum m, so the exponent is formed by one fma with a
@@ -399,40 +353,6 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
     return T;
 }
 
-// Same selection over n keys in LDS (zeros are ignored), read afresh per tested bit
-// so that no register array is needed.
-__device__ inline uint64_t wave_select_lds(const uint64_t* keys, int n, int F) {
-    const int lane = lane_id();
-    int cnt0 = 0;
-    uint64_t orv = 0ull, andv = ~0ull;
-    for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + lane;
-        const uint64_t k = j < n ? keys[j] : 0ull;
-        cnt0 += wave_popc(k != 0ull);
-        if (k != 0ull) {
-            orv |= k;
-            andv &= k;
-        }
-    }
-    if (cnt0 <= F) return 0ull;
-    orv = wave_or64(orv);
-    andv = wave_and64(andv);
-    uint64_t diff = orv ^ andv;
-    uint64_t T = andv & ~diff;
-    while (diff) {
-        const int bit = 63 - __clzll(diff);
-        diff &= ~(1ull << bit);
-        const uint64_t cand = T | (1ull << bit);
-        int cnt = 0;
-        for (int j0 = 0; j0 < n; j0 += kWave) {
-            const int j = j0 + lane;
-            cnt += wave_popc(j < n && keys[j] >= cand);
-        }
-        if (cnt >= F) T = cand;
-    }
-    return T;
-}
-
 // Same for one nonzero 32-bit key per lane (0 = no key).
 __device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
     const int n = wave_popc(k != 0u);
@@ -449,24 +369,6 @@ __device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
         if (wave_popc(k >= cand) >= F) T = cand;
     }
     return T;
-}
-
-// Sorts one 64-bit key per lane in descending order across the wave (bitonic).
-__device__ inline uint64_t wave_sort_desc(uint64_t key) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t other = __shfl_xor(key, j, kWave);
-            const bool desc = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            const uint64_t hi = key > other ? key : other;
-            const uint64_t lo = key > other ? other : key;
-            key = (desc == lower) ? hi : lo;
-        }
-    }
-    return key;
 }
 
 }  // namespace ssd

@@ -1,22 +1,25 @@
 // ssd_kernels.hip -- gfx950 kernels of the verify-and-pre-speculate round of
 // Speculative Speculative Decoding with the Saguaro algorithm.
 //
-// One round is four kernels; the two streaming ones carry all the bytes:
+// One round is four kernels (three at T = 0); the two streaming ones carry all
+// the bytes:
 //  pass 1      every row of the target and draft logits [B, K+1, V] is read once.  The
-//              unit of work is one wave64 and one tile of 8 x 16-byte vectors per
-//              lane (4096 bf16 / 2048 fp32 elements); waves never wait for each
-//              other.  Per tile: the softmax partial (max, sum of 2^{z c - o}), the
-//              lowest-id argmax and, for draft rows of the cache, every element at
-//              or above the F-th largest lane maximum of the tile (a lower bound of
-//              the tile's F-th largest value) as a candidate key.
-//  finalise    one block per sequence merges its rows: softmax statistics, cache ids
-//              S_k (top F_k draft ids, ties to the lower id), M_k, the Saguaro
-//              normaliser Z_k, and the lossless verification of the K draft tokens.
+//              unit of work is one wave64 and one tile of 8 x 16-byte vectors per lane
+//              (4096 bf16 / 2048 fp32 elements); waves never wait for each other.  Per
+//              tile: the softmax partial (max, sum of 2^{z c - o}), the lowest-id argmax
+//              and, for draft rows of the cache, every element at or above the F-th
+//              largest lane maximum of the tile (a lower bound of the tile's F-th
+//              largest value) as a candidate key.
+//  finalise    one wave per (sequence, position i): softmax statistics of both rows,
+//              cache ids S_i (top F_i draft ids, ties to the lower id), M_i, the Saguaro
+//              normaliser Z_i and the lossless test of draft token d_i, whose outcome
+//              goes to a per-position flag.
 //  pass 2      only the rows the bonus needs (target row k, plus draft row k when
-//              k < K) are read again; each wave sums the residual max(p - q', 0) of
-//              its tile.
+//              k < K, k = the first rejected position) are read again; each wave sums
+//              the residual max(p - q', 0) of its tile.
 //  bonus       one wave per sequence locates the tile where the running sum crosses
 //              u * sum, rescans that tile for the bonus id and does the cache lookup.
+//              At T = 0 pass 2 does not run and a per-sequence kernel takes the argmax.
 // Normalisers, cached masses, Z and every running sum that decides an integer are
 // kept in fp64; per-element terms are fp32 exp2 of an exactly formed exponent.  The
 // separate C-ABI calls reuse the same device code, so their results are
