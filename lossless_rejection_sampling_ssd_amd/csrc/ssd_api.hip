@@ -23,19 +23,21 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // and read by a later kernel of the same call; nothing persists between calls.
 //   part   [B][2][K+1][nt]        WavePartial, one per wave tile
 //   cand   [B][K+1][nt][cap]      top-F candidate keys of the draft rows' tiles
-//   seg    [max(B, B K)][nt]      (weight sum, target-law sum) per pass-2 tile
+//   seg    [max(B, B K)][nt2]     (weight sum, target-law sum) per pass-2 tile
 //   stats  [B (K+1)]              fp64 p_sum q_sum cache_mass Z, fp32 p_max q_max,
 //                                 int32 p_arg (for outputs the caller leaves NULL)
 //   vflag  [B K]                  int32 outcome of each draft-token test
+//   probe  [B K 2]                fp32 logits at the draft tokens (target, draft)
 struct Layout {
-    size_t part, cand, seg, stats, vflag, total;
-    int nt, cap;
+    size_t part, cand, seg, stats, vflag, probe, total;
+    int nt, nt2, cap;
 };
 
 void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     const int64_t K1 = s->K + 1;
     const int64_t R = (int64_t)s->B * K1;
     const int nt = ssd::tiles_per_row(s->dtype, s->V);
+    const int nt2 = ssd::tiles_per_row2(s->dtype, s->V);
     const int Fmax = Bf < 1 ? 1 : (Bf > SSD_MAX_F ? SSD_MAX_F : Bf);
     const int cap = ssd::cand_cap(Fmax);
     const int64_t groups = std::max<int64_t>(s->B, (int64_t)s->B * s->K);
@@ -45,13 +47,16 @@ void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     L->cand = off;
     off = align_up(off + (size_t)R * nt * cap * sizeof(uint64_t));
     L->seg = off;
-    off = align_up(off + (size_t)groups * nt * 16);
+    off = align_up(off + (size_t)groups * nt2 * 16);
     L->stats = off;
     off = align_up(off + (size_t)R * (4 * 8 + 2 * 4 + 4));
     L->vflag = off;
     off = align_up(off + (size_t)s->B * s->K * 4);
+    L->probe = off;
+    off = align_up(off + (size_t)s->B * s->K * 8);
     L->total = off;
     L->nt = nt;
+    L->nt2 = nt2;
     L->cap = cap;
 }
 
@@ -65,9 +70,10 @@ ssd_status check_shape(const ssd_shape* s) {
     if (s->B < 1 || s->K < 1 || s->K > SSD_MAX_K || s->V < 2 || s->ld < s->V) return SSD_ERR_ARG;
     if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_ARG;
     if (!std::isfinite(s->T) || s->T < 0.f) return SSD_ERR_ARG;
-    const int64_t nt = ssd::tiles_per_row(s->dtype, s->V);
-    const int64_t grid = (int64_t)s->B * 2 * (s->K + 1) * ((nt + 3) / 4);
-    if (grid > 0x7FFFFFFF || (int64_t)s->B * s->K * ((nt + 3) / 4) > 0x7FFFFFFF) return SSD_ERR_UNSUPPORTED;
+    const int64_t nt = ssd::tiles_per_row(s->dtype, s->V), nt2 = ssd::tiles_per_row2(s->dtype, s->V);
+    const int64_t grid1 = ((int64_t)s->B * (s->K + 1) + 7) / 8 * 8 * 2 * ((nt + 3) / 4);
+    const int64_t grid2 = (int64_t)s->B * s->K * ((nt2 + 3) / 4);
+    if (grid1 > 0x7FFFFFFF || grid2 > 0x7FFFFFFF) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -292,7 +298,7 @@ ssd_status ssd_saguaro_reweight(const ssd_shape* s, const double* cache_mass, fl
             a.c = c;
             a.C = C;
             a.mode = 1;
-            a.nt = L.nt;
+            a.nt = L.nt2;
             fill_fo(a, F_host, O, K1);
             a.Bf = Bf;
             a.q_max = q_max;
@@ -367,7 +373,7 @@ ssd_status ssd_residual_sample(const ssd_shape* s, const void* p_logits, const v
     a.c = temp_scale(s->T);
     a.C = C;
     a.mode = 0;
-    a.nt = L.nt;
+    a.nt = L.nt2;
     fill_fo(a, F_host, O, s->K + 1);
     a.Bf = Bf;
     a.p_max = p_max;
@@ -442,6 +448,8 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     a.want_arg = greedy || out->p_argmax || out->q_argmax;
     fill_fo(a, F_host, O, K1);
     set_ws(a, ws, L);
+    a.draft = draft;
+    a.probe = at<float>(ws, L.probe);
 
     ssd::SeqFinal f{};
     f.part = a.part;
@@ -459,6 +467,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     for (int i = 0; i <= ssd::kMaxKc; ++i) f.F[i] = a.F[i];
     for (int i = 0; i <= ssd::kMaxKc + 1; ++i) f.O[i] = a.O[i];
     f.draft = draft;
+    f.probe = a.probe;
     f.C = C;
     f.seed = rng.seed;
     f.round = rng.round;
@@ -509,7 +518,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.c = a.c;
     b.C = C;
     b.mode = 0;
-    b.nt = L.nt;
+    b.nt = L.nt2;
     fill_fo(b, F_host, O, K1);
     b.Bf = Bf;
     b.p_max = f.p_max;

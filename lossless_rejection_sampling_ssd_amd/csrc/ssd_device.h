@@ -25,6 +25,10 @@ template <> struct ElemTraits<1> {  // bf16
     static constexpr int kBytes = 2;
 };
 template <int DT> constexpr int kTile = kVecPerLane * kWave * ElemTraits<DT>::kPerVec;  // per wave
+// Pass 2 (residual sums) works on half tiles: twice the waves for the same bytes, so that
+// the arithmetic of early waves overlaps the loads of later ones.
+constexpr int kVecPass2 = 4;
+template <int DT> constexpr int kTile2 = kVecPass2 * kWave * ElemTraits<DT>::kPerVec;
 
 // ---------------------------------------------------------------------------- loads
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -93,9 +97,10 @@ __device__ __forceinline__ void unpack_vec(u32x4 v, float* x) {
 
 // Marks the vectors as rewritten, so that values derived from them before this point
 // are recomputed after it instead of being kept in registers.
-__device__ __forceinline__ void opaque_regs(u32x4 (&raw)[kVecPerLane]) {
+template <int NV>
+__device__ __forceinline__ void opaque_regs(u32x4 (&raw)[NV]) {
 #pragma unroll
-    for (int j = 0; j < kVecPerLane; ++j) __asm__ volatile("" : "+v"(raw[j]));
+    for (int j = 0; j < NV; ++j) __asm__ volatile("" : "+v"(raw[j]));
 }
 
 // Element e (a compile-time constant after unrolling) of a raw vector, widened to fp32.
@@ -107,7 +112,7 @@ __device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
     }
     return __uint_as_float(v[e]);
 }
-// The kVecPerLane raw vectors one lane owns in a wave tile starting at element t0
+// The NV raw vectors one lane owns in a wave tile starting at element t0
 // (vector j covers [t0 + (j*64 + lane)*kPerVec, +kPerVec)), elements at or past V
 // replaced by -inf.  VEC: the row is 16-byte aligned.
 //  - whole tile in range: unconditional 16-byte loads, issued back to back,
@@ -116,17 +121,17 @@ __device__ __forceinline__ float vec_elem(const u32x4& v, int e) {
 //    past the end load the row's first vector instead and discard it, so the loads
 //    stay unconditional); the one vector that straddles V, if any, by element loads;
 //  - unaligned rows: element loads of clamped ids.
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, int lane, u32x4 (&raw)[kVecPerLane]) {
+template <int DT, bool VEC, int NV>
+__device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, int lane, u32x4 (&raw)[NV]) {
     constexpr int N = ElemTraits<DT>::kPerVec;
-    constexpr int TILE = kVecPerLane * kWave * N;
+    constexpr int TILE = NV * kWave * N;
     if (VEC && t0 + TILE <= V) {
         const u32x4* base = reinterpret_cast<const u32x4*>(row + t0 * ElemTraits<DT>::kBytes) + lane;
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) raw[j] = __builtin_nontemporal_load(base + j * kWave);
+        for (int j = 0; j < NV; ++j) raw[j] = __builtin_nontemporal_load(base + j * kWave);
     } else if (VEC) {
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) {
+        for (int j = 0; j < NV; ++j) {
             const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
             const bool whole = e0 + N <= V;
             const u32x4 v = *reinterpret_cast<const u32x4*>(row + (whole ? e0 : 0) * ElemTraits<DT>::kBytes);
@@ -134,15 +139,15 @@ __device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, in
         }
         if (V % N != 0) {
             const int64_t js = ((int64_t)(V / N) * N - t0) / N;  // vector index (j*64 + lane) that straddles V
-            if (js >= 0 && js < kVecPerLane * kWave && js % kWave == lane) {
+            if (js >= 0 && js < NV * kWave && js % kWave == lane) {
 #pragma unroll
-                for (int j = 0; j < kVecPerLane; ++j)
+                for (int j = 0; j < NV; ++j)
                     if (j == js / kWave) raw[j] = load_raw_elems<DT>(row, t0 + js * N, V);
             }
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j)
+        for (int j = 0; j < NV; ++j)
             raw[j] = load_raw_elems<DT>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
     }
 }
@@ -253,6 +258,28 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     v += dpp_f64_zero<kRowShr8>(v);
     return (lane_f64(v, 15) + lane_f64(v, 31)) + (lane_f64(v, 47) + lane_f64(v, 63));
 }
+// Inclusive prefix sums over lanes in lane order (all lanes active): row shifts give
+// the prefix within each 16-lane row, then the totals of the rows below are added.
+__device__ __forceinline__ uint32_t wave_prefix_u32(uint32_t v) {
+    v += dpp_u32<kRowShr1>(0u, v);
+    v += dpp_u32<kRowShr2>(0u, v);
+    v += dpp_u32<kRowShr4>(0u, v);
+    v += dpp_u32<kRowShr8>(0u, v);
+    const uint32_t r0 = lane_u32(v, 15), r1 = lane_u32(v, 31), r2 = lane_u32(v, 47);
+    const int row = lane_id() >> 4;
+    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+__device__ __forceinline__ double wave_prefix_f64(double v) {
+    v += dpp_f64_zero<kRowShr1>(v);
+    v += dpp_f64_zero<kRowShr2>(v);
+    v += dpp_f64_zero<kRowShr4>(v);
+    v += dpp_f64_zero<kRowShr8>(v);
+    const double r0 = lane_f64(v, 15), r1 = lane_f64(v, 31), r2 = lane_f64(v, 47);
+    const int row = lane_id() >> 4;
+    const double below = row == 0 ? 0.0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+    return v + below;
+}
+
 __device__ __forceinline__ int wave_popc(bool p) { return __popcll(__ballot(p)); }
 // Number of lanes below this one with p set.
 __device__ __forceinline__ int lanes_below(bool p) {

@@ -36,6 +36,8 @@ struct Pass1Args {
     int O[kMaxKc + 2];
     WavePartial* part;  // [B][nmodel][K1][nt]
     uint64_t* cand;     // [B][K1][nt][cap]
+    const int32_t* draft;  // nullable [B, K]: the wave holding logit d_i of row i records it
+    float* probe;          // [B][K][nmodel] logits at the draft tokens (when draft is set)
 };
 
 // Finalisation of the vocabulary pass per (sequence, position): row statistics,
@@ -54,6 +56,7 @@ struct SeqFinal {
     int F[kMaxKc + 1];
     int O[kMaxKc + 2];
     const int32_t* draft;  // [B, K]
+    const float* probe;    // [B][K][2] logits at the draft tokens, recorded by pass 1
     float C;
     uint64_t seed, round;
     int fallback;
@@ -86,7 +89,7 @@ struct Pass2Args {
     float c;
     float C;
     int mode;         // 0: bonus from the residual (per sequence); 1: draft tokens from q' (per (b, i))
-    int nt;
+    int nt;           // pass-2 tiles per row
     int F[kMaxKc + 1];
     int O[kMaxKc + 2];
     int Bf;
@@ -112,7 +115,8 @@ struct Pass2Args {
 };
 
 int tile_elems(int dtype);
-int tiles_per_row(int dtype, int V);
+int tiles_per_row(int dtype, int V);   // pass-1 tiles
+int tiles_per_row2(int dtype, int V);  // pass-2 tiles (half size)
 int cand_cap(int Fmax);
 
 hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st);

@@ -34,12 +34,17 @@ namespace ssd {
 
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4 };
+constexpr int kXcds = 8;            // accelerator complex dies of MI355X
 constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
 constexpr int kStageCap = 160;     // LDS slots per wave for one tile's candidate keys (>= any cap)
 
 int tile_elems(int dtype) { return dtype == 1 ? kTile<1> : kTile<0>; }
 int tiles_per_row(int dtype, int V) {
     const int t = tile_elems(dtype);
+    return (V + t - 1) / t;
+}
+int tiles_per_row2(int dtype, int V) {
+    const int t = dtype == 1 ? kTile2<1> : kTile2<0>;
     return (V + t - 1) / t;
 }
 int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }  // <= 144 = cand_cap(64) <= kStageCap
@@ -136,10 +141,12 @@ __device__ __forceinline__ void row_stats_wave(const WavePartial* P, int nt, flo
 constexpr int kCandRegs = 24;    // register slots per lane: up to 1536 candidates per row
 
 struct TopfScratch {
-    uint64_t surv[kSurvivorCap];  // keys at or above the value threshold
-    uint64_t rank[kWave];         // the top F, placed by rank
-    uint32_t bins[256];           // value histogram of the select
-    uint8_t nc[kMaxMergeTiles];   // candidates per tile
+    uint64_t surv[kSurvivorCap + kWave];  // keys at or above the value threshold (+ one
+                                          // discard slot per lane)
+    uint64_t rank[kWave];                 // the top F, placed by rank
+    uint32_t bins[256 + kWave];           // value histogram of the select (+ one discard
+                                          // bin per lane)
+    uint8_t nc[kMaxMergeTiles];           // candidates per tile
 };
 
 // The largest 32-bit value part T such that at least F of the nonzero keys among the
@@ -149,7 +156,8 @@ struct TopfScratch {
 // prefix found so far in a 256-bin LDS histogram of their next 8 bits and keeps the
 // bin that holds the rank still sought.
 template <int KREG>
-__device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, int F, uint32_t* bins) {
+__device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, int F, uint32_t* bins,
+                                             bool first_step_only = false) {
     U = uniform(U);
     const int lane = lane_id();
     int n = 0;
@@ -170,20 +178,23 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, i
     const uint32_t diff = orv ^ andv;
     if (diff == 0u) return andv;
     int hi = 32 - __clz(diff);                               // bits [hi, 32) are common
-    uint32_t prefix = hi >= 32 ? 0u : (andv >> hi) << hi;
+    const int lo = __ffs(diff) - 1;                          // so are bits [0, lo)
+    uint32_t prefix = (hi >= 32 ? 0u : (andv >> hi) << hi) | (andv & ((1u << lo) - 1u));
     int need = F;
-    while (hi > 0) {
-        const int shift = hi > 8 ? hi - 8 : 0;
+    while (hi > lo) {
+        const int shift = hi - lo > 8 ? hi - 8 : lo;
         const uint32_t wmask = (1u << (hi - shift)) - 1u;
 #pragma unroll
         for (int j = 0; j < 256 / kWave; ++j) bins[j * kWave + lane] = 0u;
         wave_sync_lds();
+        // every lane adds in every slot (no per-lane branch): non-matching keys add to
+        // the lane's own discard bin
 #pragma unroll
         for (int u = 0; u < KREG; ++u) {
             if (u < U) {
                 const uint32_t h = (uint32_t)(k[u] >> 32);
-                const bool match = k[u] != 0ull && (hi >= 32 || (h >> hi) == (prefix >> hi));
-                if (match) atomicAdd(&bins[(h >> shift) & wmask], 1u);
+                const bool match = (k[u] != 0ull) & ((hi >= 32) | ((h >> (hi & 31)) == (prefix >> (hi & 31))));
+                atomicAdd(&bins[match ? (h >> shift) & wmask : 256 + lane], 1u);
             }
         }
         wave_sync_lds();
@@ -191,14 +202,9 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, i
         uint32_t c[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) c[j] = bins[4 * lane + j];
-        const int lane_sum = (int)(c[0] + c[1] + c[2] + c[3]);
-        int suf = lane_sum;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int y = __shfl_down(suf, off, kWave);
-            if (lane + off < kWave) suf += y;
-        }
-        int above = suf - lane_sum;  // keys in the bins of higher lanes
+        const uint32_t lane_sum = c[0] + c[1] + c[2] + c[3];
+        const uint32_t incl = wave_prefix_u32(lane_sum);
+        int above = (int)(lane_u32(incl, kWave - 1) - incl);  // keys in the bins of higher lanes
         int hit_bin = -1, hit_above = 0;
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
@@ -209,12 +215,16 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, i
             above += (int)c[j];
         }
         const uint64_t hm = __ballot(hit_bin >= 0);
-        const int src = __ffsll((long long)hm) - 1;
-        const int bsel = uniform(__shfl(hit_bin, src, kWave));
-        need -= uniform(__shfl(hit_above, src, kWave));
+        const int src = uniform(__ffsll((long long)hm) - 1);
+        const int bsel = (int)lane_u32((uint32_t)hit_bin, src);
+        need -= (int)lane_u32((uint32_t)hit_above, src);
         prefix |= (uint32_t)bsel << shift;
         hi = shift;
         wave_sync_lds();
+        if (first_step_only) {
+            // lower bound of the bin holding the F-th largest value
+            return (hi >= 32 ? 0u : (prefix >> hi) << hi) | (andv & ((1u << lo) - 1u) & ((1u << hi) - 1u));
+        }
     }
     return prefix;
 }
@@ -259,9 +269,9 @@ __device__ inline int compact_keys(TopfScratch& sc, const uint64_t (&k)[KREG], i
 #pragma unroll
     for (int u = 0; u < KREG; ++u) {
         if (u < U) {
-            const bool keep = k[u] != 0ull && k[u] >= lo;
+            const bool keep = (k[u] != 0ull) & (k[u] >= lo);
             const int pos = n + lanes_below(keep);
-            if (keep && pos < kSurvivorCap) sc.surv[pos] = k[u];
+            sc.surv[keep && pos < kSurvivorCap ? pos : kSurvivorCap + lane_id()] = k[u];
             n += wave_popc(keep);
         }
     }
@@ -280,26 +290,33 @@ __device__ __forceinline__ uint64_t chunk_key(const uint64_t* cand, int cap, int
     return cand[(int64_t)(c0 + lo) * cap + (j - start[lo])];
 }
 
-// Loads slots s < R of every tile's candidate list (R <= cap, nt*R <= 64*KREG):
-// slot (t, s) goes to lane (s*nt + t) mod 64, register (s*nt + t) / 64.  No load
-// depends on the per-tile counts, so they can be requested with the tile partials.
+// Loads slots s < R of every tile's candidate list (R <= cap, nt*R <= 64*KREG) in
+// tile-major order: flat index f = t*R + s goes to lane f mod 64, register f / 64, so
+// the lanes of one load cover consecutive slots of one or two tiles (few cache
+// lines).  No load depends on the per-tile counts, so they can be requested with the
+// tile partials.
 template <int KREG>
 __device__ __forceinline__ void gather_slots(const uint64_t* cand, int cap, int nt, int R, uint64_t (&k)[KREG]) {
     const int lane = lane_id();
     const int total = nt * R;
-    int t = lane % nt, sl = lane / nt;
+    int t = lane / R, sl = lane % R;
     // opaque to the optimiser: keeps the slot addresses from being hoisted out of a
     // caller's loop over rows (they would stay live in registers across it)
     __asm__ volatile("" : "+v"(t), "+v"(sl));
-    const int dt = kWave % nt, ds = kWave / nt;
+    const int dt = kWave / R, ds = kWave % R;
+    // Every slot of a used register is loaded (no per-lane branch); slots past nt*R
+    // read slot 0 of tile 0 and are dropped.
 #pragma unroll
     for (int u = 0; u < KREG; ++u) {
-        k[u] = u * kWave + lane < total ? cand[(int64_t)t * cap + sl] : 0ull;
+        uint64_t x = 0ull;
+        const bool in = u * kWave + lane < total;
+        if (u * kWave < total) x = cand[in ? (int64_t)t * cap + sl : 0];  // uniform test
+        k[u] = in ? x : 0ull;
         t += dt;
         sl += ds;
-        if (t >= nt) {
-            t -= nt;
-            ++sl;
+        if (sl >= R) {
+            sl -= R;
+            ++t;
         }
     }
 }
@@ -310,19 +327,24 @@ template <int KREG>
 __device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, const uint8_t* nc,
                                            uint64_t floor_key) {
     const int lane = lane_id();
-    const int total = nt * R;
-    int t = lane % nt, sl = lane / nt;
-    const int dt = kWave % nt, ds = kWave / nt;
+    int t = lane / R, sl = lane % R;
+    const int dt = kWave / R, ds = kWave % R;
+    int cnt[KREG], sls[KREG];
 #pragma unroll
-    for (int u = 0; u < KREG; ++u) {
-        const bool live = u * kWave + lane < total && sl < (int)nc[t] && k[u] >= floor_key;
-        k[u] = live ? k[u] : 0ull;
+    for (int u = 0; u < KREG; ++u) {  // all count reads first, then the tests
+        cnt[u] = nc[min(t, nt - 1)];
+        sls[u] = sl;
         t += dt;
         sl += ds;
-        if (t >= nt) {
-            t -= nt;
-            ++sl;
+        if (sl >= R) {
+            sl -= R;
+            ++t;
         }
+    }
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) {
+        const bool live = (sls[u] < cnt[u]) & (k[u] >= floor_key);
+        k[u] = live ? k[u] : 0ull;
     }
 }
 
@@ -331,9 +353,14 @@ __device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, c
 // rank (a whole-key select first when more than kSurvivorCap keys tie there).
 template <int KREG>
 __device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, int F, TopfScratch& sc) {
-    const uint32_t T = wave_select_value<KREG>(k, U, F, sc.bins);
-    const uint64_t lo = (uint64_t)T << 32;
+    // One histogram step usually leaves few enough keys (those in or above the bin of
+    // the F-th largest value) to rank them all; otherwise resolve the value exactly.
+    uint64_t lo = (uint64_t)wave_select_value<KREG>(k, U, F, sc.bins, true) << 32;
     int n = compact_keys<KREG>(sc, k, U, lo);
+    if (n > kSurvivorCap) {
+        lo = (uint64_t)wave_select_value<KREG>(k, U, F, sc.bins) << 32;
+        n = compact_keys<KREG>(sc, k, U, lo);
+    }
     if (n > kSurvivorCap) {
 #pragma unroll
         for (int u = 0; u < KREG; ++u) k[u] = k[u] >= lo ? k[u] : 0ull;
@@ -513,17 +540,20 @@ __device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp
 // ============================================================================ pass 1
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
-    __shared__ uint64_t cand_stage[kWavesPerBlock][kStageCap];
+    __shared__ uint64_t cand_stage[kWavesPerBlock][kStageCap + kWave];
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    int bid = blockIdx.x;
-    const int blk = bid % nblk;
-    bid /= nblk;
-    const int i = bid % a.K1;
-    bid /= a.K1;
-    const int model = bid % a.nmodel;
-    const int b = bid / a.nmodel;
+    // Block -> (row pair, model, tile group): the blocks of one (b, i) pair go to the
+    // same XCD (blocks are dealt to the 8 XCDs round-robin), where the finalisation
+    // wave of that pair later reads the partials; each XCD streams its rows in order.
+    const int bid = blockIdx.x;
+    const int per = a.nmodel * nblk;
+    const int y = bid / kXcds;
+    const int pr = (y / per) * kXcds + bid % kXcds;
+    if (pr >= a.B * a.K1) return;
+    const int model = (y % per) / nblk, blk = (y % per) % nblk;
+    const int i = pr % a.K1, b = pr / a.K1;
     const int t = blk * kWavesPerBlock + wave;
     if (t >= a.nt) return;
     const int64_t r = (int64_t)b * a.K1 + i;
@@ -535,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     // The tile stays in its raw 16-byte vectors (32 registers for bf16, not 64) and is
     // widened element by element in each use.
     u32x4 raw[kVecPerLane];
-    load_tile<DT, VEC>(row, tile0, V, lane, raw);
+    load_tile<DT, VEC, kVecPerLane>(row, tile0, V, lane, raw);
 
     float vmax[kVecPerLane];  // maximum of each of the lane's vectors
     float m = -INFINITY;
@@ -611,9 +641,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 const int id = id0 + j * kWave * N + e;
                 const bool hit = v >= tauf && (full || id < V);
                 const uint64_t mk = __ballot(hit);
-                if (mk) {
+                if (mk) {  // uniform; the store itself is unconditional (misses go to the
+                           // lane's discard slot)
                     const int pos = n + __popcll(mk & below);
-                    if (hit && pos < kStageCap) stage[pos] = cand_key(v, (uint32_t)id);
+                    stage[hit && pos < kStageCap ? pos : kStageCap + lane] = cand_key(v, (uint32_t)id);
                     n += __popcll(mk);
                 }
             }
@@ -649,6 +680,27 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 prev = best;
             }
             ncand = F;
+        }
+    }
+
+    // ---- logit at the draft token of this row, if it falls in this tile
+    if (a.draft && i < a.K1 - 1) {
+        const int d = a.draft[(int64_t)b * (a.K1 - 1) + i];
+        const int64_t off = (int64_t)d - tile0;
+        if (d >= 0 && d < V && off >= 0 && off < kTile<DT>) {  // uniform
+            const int owner = (int)((off / N) % kWave), jd = (int)(off / (N * kWave)), ed = (int)(off % N);
+            if (lane == owner) {
+                u32x4 v = raw[0];
+#pragma unroll
+                for (int j = 1; j < kVecPerLane; ++j) v = jd == j ? raw[j] : v;
+                uint32_t w = v.x;
+                const int q = DT == 1 ? ed >> 1 : ed;
+                w = q == 1 ? v.y : w;
+                w = q == 2 ? v.z : w;
+                w = q == 3 ? v.w : w;
+                if (DT == 1) w = (ed & 1) ? (w & 0xFFFF0000u) : (w << 16);
+                a.probe[((int64_t)b * (a.K1 - 1) + i) * a.nmodel + model] = __uint_as_float(w);
+            }
         }
     }
 
@@ -710,23 +762,24 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
 // tiles the tile partials, the first 2 F_i + 2 candidate slots of every tile and the
 // logits at d_i are requested together.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void finalize_pos_kernel(const SeqFinal f) {
-    __shared__ TopfScratch scr[kWavesPerBlock];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+__global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
+    __shared__ TopfScratch sc;
+    const int lane = threadIdx.x;
     const int K = f.K, K1 = K + 1, nt = f.nt;
-    const int g = blockIdx.x * kWavesPerBlock + wave;
-    if (g >= f.B * K1) return;
+    const int g = blockIdx.x;  // one wave per block
     const int b = g / K1, i = g % K1;
     const WavePartial* part = f.part + (int64_t)b * 2 * K1 * nt;
     const bool fast = nt <= kWave;
-    TopfScratch& sc = scr[wave];
     const int64_t r = (int64_t)b * K1 + i;
     const WavePartial* Pp = part + (int64_t)i * nt;
     const WavePartial* Pq = part + (int64_t)(K1 + i) * nt;
     const uint64_t* cr = f.cand + r * nt * f.cap;
     const int F = f.F[i];
-    const DraftProbe pr =
-        probe_draft<DT>(f.draft, f.p_logits, f.q_logits, f.ld_bytes, b, i, K, f.V, f.greedy, f.seed, f.round);
+    DraftProbe pr;
+    pr.d = i < K ? f.draft[(int64_t)b * K + i] : 0;
+    pr.zp = i < K ? f.probe[((int64_t)b * K + i) * 2 + 0] : 0.f;  // valid when d_i is in range
+    pr.zq = i < K ? f.probe[((int64_t)b * K + i) * 2 + 1] : 0.f;
+    pr.u = (i < K && !f.greedy) ? philox_uniform(f.seed, f.round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
     float mp, mq;
     double sp, sq;
     int ap, aq;
@@ -766,7 +819,7 @@ __global__ __launch_bounds__(kBlock) void finalize_pos_kernel(const SeqFinal f) 
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
             mask_slots<kCandRegs>(k, nt, Rg, sc.nc, (uint64_t)cs.tr << 32);
-            key = select_sorted<kCandRegs>(k, (nt * cs.max_nc + kWave - 1) / kWave, F, sc);
+            key = select_sorted<kCandRegs>(k, (nt * Rg + kWave - 1) / kWave, F, sc);  // tile-major slots
         } else {
             key = row_topf_wave(Pq, cr, nt, f.cap, F, cs, sc);
         }
@@ -874,9 +927,9 @@ __device__ __forceinline__ double elem_weight_t(const WParams& w, float zp, floa
 template <int DT>
 __device__ inline void tile_bitmap(uint32_t* bits, int64_t t0, int my_id) {
     const int lane = lane_id();
-    for (int w = lane; w < kTile<DT> / 32; w += kWave) bits[w] = 0u;
+    for (int w = lane; w < kTile2<DT> / 32; w += kWave) bits[w] = 0u;
     wave_sync_lds();
-    if (my_id >= t0 && my_id < t0 + kTile<DT>)
+    if (my_id >= t0 && my_id < t0 + kTile2<DT>)
         atomicOr(&bits[(my_id - t0) >> 5], 1u << ((my_id - t0) & 31));
     wave_sync_lds();
 }
@@ -910,16 +963,16 @@ __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const c
                                           const int32_t* ids, int Fk, uint32_t* bits, double& sw, double& sp) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int lane = lane_id();
-    u32x4 rp[kVecPerLane], rq[kVecPerLane];
-    if (MODE != kWQprime) load_tile<DT, VEC>(prow, t0, a.V, lane, rp);
-    if (MODE != kWP) load_tile<DT, VEC>(qrow, t0, a.V, lane, rq);
+    u32x4 rp[kVecPass2], rq[kVecPass2];
+    if (MODE != kWQprime) load_tile<DT, VEC, kVecPass2>(prow, t0, a.V, lane, rp);
+    if (MODE != kWP) load_tile<DT, VEC, kVecPass2>(qrow, t0, a.V, lane, rq);
     int my_id = -1;
     if (MODE != kWP && lane < Fk) my_id = ids[lane];
     const LawIn L = load_law(a, r);
     const WParams wp = make_wparams(a.c, a.C, MODE != kWQprime, L);
     if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
 #pragma unroll
-    for (int j = 0; j < kVecPerLane; ++j) {
+    for (int j = 0; j < kVecPass2; ++j) {
         const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
         double w[N], p[N];
         vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, a.V, bits, t0, w, p);
@@ -953,43 +1006,11 @@ __device__ __forceinline__ int pass2_mode(const Pass2Args& a, int pos) {
     return a.mode == 1 ? kWQprime : (pos < a.K ? kWResid : kWP);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
-    __shared__ uint32_t bits[kWavesPerBlock][kTile<1> / 32];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int g = blockIdx.x / nblk;
-    const int t = (blockIdx.x % nblk) * kWavesPerBlock + wave;
-    if (t >= a.nt) return;
-    int b, pos;
-    bool valid;
-    pass2_group(a, g, b, pos, valid);
-    double sw = 0.0, sp = 0.0;
-    if (valid) {
-        const int64_t r = (int64_t)b * (a.K + 1) + pos;
-        const int mode = pass2_mode(a, pos);
-        const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
-        const char* qrow = a.q_logits + r * a.ld_bytes;
-        const int64_t t0 = (int64_t)t * kTile<DT>;
-        const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
-        const int Fk = a.F[pos];
-        if (mode == kWResid)
-            tile_sums<DT, VEC, kWResid>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
-        else if (mode == kWP)
-            tile_sums<DT, VEC, kWP>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
-        else
-            tile_sums<DT, VEC, kWQprime>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
-    }
-    sw = wave_sum_f64(sw);
-    sp = wave_sum_f64(sp);
-    if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
-}
-
 // Rescan of one tile element by element in id order: the first id whose running sum
 // (starting at base) exceeds thr, or with pick_last the last id of positive weight.
 // The caller has issued the tile loads (rp, rq).
 template <int DT, int MODE>
-__device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPerLane], const u32x4 (&rq)[kVecPerLane],
+__device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPass2], const u32x4 (&rq)[kVecPass2],
                                   int64_t t0, int V, int my_id, uint32_t* bits, double base, double thr,
                                   bool pick_last) {
     constexpr int N = ElemTraits<DT>::kPerVec;
@@ -998,19 +1019,14 @@ __device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPerLa
     double run = base;
     int found = -1, last_pos = -1;
 #pragma unroll
-    for (int j = 0; j < kVecPerLane; ++j) {
+    for (int j = 0; j < kVecPass2; ++j) {
         const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
         double w[N], p[N];
         vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, V, bits, t0, w, p);
         double ls = 0.0;
 #pragma unroll
         for (int e = 0; e < N; ++e) ls += w[e];
-        double incl = ls;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const double y = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += y;
-        }
+        const double incl = wave_prefix_f64(ls);
         double cum = run + (incl - ls);
         int hitpos = -1, lastp = -1;
 #pragma unroll
@@ -1021,48 +1037,34 @@ __device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPerLa
         }
         if (!pick_last && found < 0) {
             const uint64_t hm = __ballot(hitpos >= 0);
-            if (hm) found = __shfl(hitpos, __ffsll((long long)hm) - 1, kWave);
+            if (hm) found = (int)lane_u32((uint32_t)hitpos, uniform(__ffsll((long long)hm) - 1));
         }
         const uint64_t lm = __ballot(lastp >= 0);
-        if (lm) last_pos = __shfl(lastp, 63 - __clzll(lm), kWave);
-        run += __shfl(incl, kWave - 1, kWave);
+        if (lm) last_pos = (int)lane_u32((uint32_t)lastp, uniform(63 - __clzll(lm)));
+        run += lane_f64(incl, kWave - 1);
     }
     return found >= 0 ? found : (last_pos >= 0 ? last_pos : (int)min<int64_t>(t0, V - 1));
 }
 
 // Inclusive wave scan of x (fp64, lane order).
-__device__ __forceinline__ double wave_scan_incl(double x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const double y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
+__device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_f64(x); }
 
-// One wave per group: totals over the tiles in tile order, the tile where the running
-// sum crosses u * total, the id inside it, and the cache lookup.  The tile sums of the
-// first 64 tiles, the row statistics and the cached ids are requested together.
+// Bonus of one group by one wave: totals over the tiles in tile order, the tile where
+// the running sum crosses u * total, the id inside it, and the cache lookup.  The tile
+// sums of the first 64 tiles, the row statistics and the cached ids are requested
+// together.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args a, int ngroups) {
-    __shared__ uint32_t bits[kWavesPerBlock][kTile<1> / 32];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int g = blockIdx.x * kWavesPerBlock + wave;
-    if (g >= ngroups) return;
-    int b, pos, verrs = 0;
-    bool valid;
-    pass2_group(a, g, b, pos, valid, &verrs);
+__device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
+                                           double2 v0, uint32_t* bits) {
+    const int lane = lane_id();
     const int K = a.K;
     const int nt = a.nt;
     const double2* seg = a.seg + (int64_t)g * nt;
     int tok = -1;
     double Zused = 0.0;
-    const int my_id = valid ? cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O) : -1;
+    int my_id = -1;
     if (valid) {
         const int64_t r = (int64_t)b * (K + 1) + pos;
-        const double2 v0 = lane < nt ? seg[lane] : make_double2(0.0, 0.0);
-        const LawIn L = load_law(a, r);
         const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
         const double u = (double)philox_uniform(a.seed, a.round, purpose, (uint64_t)b, (uint64_t)pos);
         double tot_w = 0.0, tot_p = 0.0;
@@ -1070,8 +1072,8 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
             const int j = g0 + lane;
             double2 v = v0;
             if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
-            tot_w += __shfl(wave_scan_incl(v.x), kWave - 1, kWave);
-            tot_p += __shfl(wave_scan_incl(v.y), kWave - 1, kWave);
+            tot_w += lane_f64(wave_scan_incl(v.x), kWave - 1);
+            tot_p += lane_f64(wave_scan_incl(v.y), kWave - 1);
         }
         int mode = pass2_mode(a, pos);
         double Z = tot_w;
@@ -1094,16 +1096,16 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
             const uint64_t cross = __ballot(j < nt && incl > thr);
             const uint64_t posm = __ballot(j < nt && x > 0.0);
             if (gsel < 0 && cross) {
-                const int l = __ffsll((long long)cross) - 1;
+                const int l = uniform(__ffsll((long long)cross) - 1);
                 gsel = g0 + l;
-                gbase = __shfl(excl, l, kWave);
+                gbase = lane_f64(excl, l);
             }
             if (posm) {
-                const int l = 63 - __clzll(posm);
+                const int l = uniform(63 - __clzll(posm));
                 glast = g0 + l;
-                lastbase = __shfl(excl, l, kWave);
+                lastbase = lane_f64(excl, l);
             }
-            carry = __shfl(incl, kWave - 1, kWave);
+            carry = lane_f64(incl, kWave - 1);
         }
         bool pick_last = false;
         if (gsel < 0) {
@@ -1111,19 +1113,22 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
             gbase = lastbase;
             pick_last = true;
         }
-        const int64_t t0 = (int64_t)gsel * kTile<DT>;
+        // the crossing tile, the row statistics and the cached ids travel together
+        const int64_t t0 = (int64_t)gsel * kTile2<DT>;
         const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
         const char* qrow = a.q_logits + r * a.ld_bytes;
-        u32x4 rp[kVecPerLane], rq[kVecPerLane];
-        if (mode != kWQprime) load_tile<DT, VEC>(prow, t0, a.V, lane, rp);
-        if (mode != kWP) load_tile<DT, VEC>(qrow, t0, a.V, lane, rq);
+        u32x4 rp[kVecPass2], rq[kVecPass2];
+        if (mode != kWQprime) load_tile<DT, VEC, kVecPass2>(prow, t0, a.V, lane, rp);
+        if (mode != kWP) load_tile<DT, VEC, kVecPass2>(qrow, t0, a.V, lane, rq);
+        const LawIn L = load_law(a, r);
+        my_id = cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O);
         const WParams wp = make_wparams(a.c, a.C, mode != kWQprime, L);
         if (mode == kWResid)
-            tok = rescan_tile<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
+            tok = rescan_tile<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
         else if (mode == kWP)
-            tok = rescan_tile<DT, kWP>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
+            tok = rescan_tile<DT, kWP>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
         else
-            tok = rescan_tile<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits[wave], gbase, thr, pick_last);
+            tok = rescan_tile<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
     }
     if (lane == 0) {
         if (a.mode == 0) {
@@ -1141,6 +1146,55 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     if (a.mode == 0 && a.do_lookup)
         lookup_wave(b, K, a.V, valid ? pos : -1, valid ? a.O[pos] : 0, my_id, tok, a.fallback, a.seed, a.round, a.hit,
                     a.slot, a.fallback_tokens);
+}
+
+// One wave per group when the bonus runs as a kernel of its own.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args a, int ngroups) {
+    __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
+    const int wave = threadIdx.x / kWave;
+    const int g = blockIdx.x * kWavesPerBlock + wave;
+    if (g >= ngroups) return;
+    const int lane = threadIdx.x % kWave;
+    // the group's tile sums do not depend on the accepted length: request them first
+    const double2 v0 = lane < a.nt ? a.seg[(int64_t)g * a.nt + lane] : make_double2(0.0, 0.0);
+    int b, pos, verrs = 0;
+    bool valid;
+    pass2_group(a, g, b, pos, valid, &verrs);
+    bonus_wave<DT, VEC>(a, g, b, pos, valid, verrs, v0, bits[wave]);
+}
+
+// One wave per (group, tile): the residual (or target-law) sums of the tile.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
+    __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int g = blockIdx.x / nblk;
+    const int t = (blockIdx.x % nblk) * kWavesPerBlock + wave;
+    if (t >= a.nt) return;
+    int b, pos;
+    bool valid;
+    pass2_group(a, g, b, pos, valid);
+    double sw = 0.0, sp = 0.0;
+    if (valid) {
+        const int64_t r = (int64_t)b * (a.K + 1) + pos;
+        const int mode = pass2_mode(a, pos);
+        const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
+        const char* qrow = a.q_logits + r * a.ld_bytes;
+        const int64_t t0 = (int64_t)t * kTile2<DT>;
+        const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
+        const int Fk = a.F[pos];
+        if (mode == kWResid)
+            tile_sums<DT, VEC, kWResid>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+        else if (mode == kWP)
+            tile_sums<DT, VEC, kWP>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+        else
+            tile_sums<DT, VEC, kWQprime>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+    }
+    sw = wave_sum_f64(sw);
+    sp = wave_sum_f64(sp);
+    if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
 }
 
 // ============================================================================ small kernels
@@ -1309,7 +1363,7 @@ static hipError_t by_type(int dtype, bool vec, Fn&& fn) {
 
 hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st) {
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t grid = (int64_t)a.B * a.nmodel * a.K1 * nblk;
+    const int64_t grid = ((int64_t)a.B * a.K1 + kXcds - 1) / kXcds * kXcds * a.nmodel * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
         pass1_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
@@ -1317,11 +1371,11 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
 }
 
 hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
-    const int grid = (f.B * (f.K + 1) + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int grid = f.B * (f.K + 1);
     if (dtype == 1)
-        finalize_pos_kernel<1><<<grid, kBlock, 0, st>>>(f);
+        finalize_pos_kernel<1><<<grid, kWave, 0, st>>>(f);
     else
-        finalize_pos_kernel<0><<<grid, kBlock, 0, st>>>(f);
+        finalize_pos_kernel<0><<<grid, kWave, 0, st>>>(f);
     return hipGetLastError();
 }
 
