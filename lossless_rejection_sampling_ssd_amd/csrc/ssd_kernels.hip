@@ -567,17 +567,40 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     u32x4 raw[kVecPerLane];
     load_tile<DT, VEC, kVecPerLane>(row, tile0, V, lane, raw);
 
+    // One pass over the lane's vectors: the maximum of each vector and, unless greedy,
+    // the sum of 2^{z c - o} with o the offset of the running maximum; when the maximum
+    // grows the partial sum moves to the new offset exactly (ldexp by o_old - o_new).
     float vmax[kVecPerLane];  // maximum of each of the lane's vectors
     float m = -INFINITY;
+    float s32 = 0.f, o = 0.f;
+    const bool want_sum = !a.greedy;
 #pragma unroll
     for (int j = 0; j < kVecPerLane; ++j) {
-        vmax[j] = vec_elem<DT>(raw[j], 0);
+        float x[N];
 #pragma unroll
-        for (int e = 1; e < N; ++e) vmax[j] = fmaxf(vmax[j], vec_elem<DT>(raw[j], e));
-        m = fmaxf(m, vmax[j]);
+        for (int e = 0; e < N; ++e) x[e] = vec_elem<DT>(raw[j], e);
+        float vm = x[0];
+#pragma unroll
+        for (int e = 1; e < N; ++e) vm = fmaxf(vm, x[e]);
+        vmax[j] = vm;
+        m = fmaxf(m, vm);
+        if (want_sum) {
+            const float on = offset_of(m, c);
+            s32 = ldexpf(s32, (int)(o - on));
+            o = on;
+            float tt[N];
+#pragma unroll
+            for (int e = 0; e < N; ++e) tt[e] = term(x[e], c, o);
+#pragma unroll
+            for (int w = N / 2; w >= 1; w >>= 1)
+#pragma unroll
+                for (int e = 0; e < w; ++e) tt[e] += tt[e + w];
+            s32 += tt[0];
+        }
     }
     const float m_lane = m;
-    // each phase widens the elements afresh rather than keeping 64 widened values live
+    const double s_lane = (double)s32;  // relative to offset_of(m_lane)
+    // each later phase widens the elements afresh rather than keeping them live
     opaque_regs(raw);
 
     int arg = INT_MAX;
@@ -590,28 +613,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 if (arg == INT_MAX && id < V && vec_elem<DT>(raw[j], e) == m_lane) arg = (int)id;
             }
     }
-
-    double s = 0.0;
-    if (!a.greedy && m_lane != -INFINITY) {
-        const float o = offset_of(m_lane, c);
-        float vs[kVecPerLane];
-#pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) {
-            float tt[N];
-#pragma unroll
-            for (int e = 0; e < N; ++e) tt[e] = term(vec_elem<DT>(raw[j], e), c, o);
-#pragma unroll
-            for (int w = N / 2; w >= 1; w >>= 1)
-#pragma unroll
-                for (int e = 0; e < w; ++e) tt[e] += tt[e + w];
-            vs[j] = tt[0];
-        }
-#pragma unroll
-        for (int w = kVecPerLane / 2; w >= 1; w >>= 1)
-#pragma unroll
-            for (int j = 0; j < w; ++j) vs[j] += vs[j + w];
-        s = (double)vs[0];
-    }
+    double s = s_lane;
     opaque_regs(raw);
 
     // ---- candidate keys of this tile (draft rows of the cache): every element at or
