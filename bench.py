@@ -102,7 +102,11 @@ def main():
     torch.cuda.synchronize()
     shape = ssd.shape_of(bufs[0][0], T)
     fallback = ssd.SSD_FALLBACK_UNIFORM if w.fallback_uniform else ssd.SSD_FALLBACK_NONE
-    outb = ssd.RoundBuffers(B, K, w.Bf, with_stats=False)
+    # value store [B, B_f, K]: synthetic continuations (real ones come from draft forward
+    # passes); each round also gathers the next draft from it
+    values = torch.randint(0, V, (B, w.Bf, K), dtype=torch.int32, device=dev,
+                           generator=torch.Generator(device=dev).manual_seed(w.seed))
+    outb = ssd.RoundBuffers(B, K, w.Bf, with_stats=False, cache_values=values)
 
     def step(i, events=None):
         zp, zq, d = bufs[i % nbuf]
@@ -191,6 +195,7 @@ def main():
             "workload": label,
             "logits": w.dtype,
             "fan_out": F,
+            "next_draft_gather": True,
             "buffers": nbuf,
             "round_bytes": int(round_bytes),
             "round_GBps": round(round_gbps, 1),

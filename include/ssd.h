@@ -64,7 +64,8 @@ enum { SSD_PURPOSE_ACCEPT = 0, SSD_PURPOSE_BONUS = 1, SSD_PURPOSE_DRAFT = 2, SSD
 enum {
     SSD_DEVERR_TOKEN_RANGE = 1,  /* a draft token outside [0, V): treated as rejected */
     SSD_DEVERR_QPRIME_ZERO = 2,  /* q'(d) == 0 in fp32 for a tested draft token: rejected */
-    SSD_DEVERR_LEN_RANGE = 4     /* accept_len outside [0, K]: bonus -1, miss */
+    SSD_DEVERR_LEN_RANGE = 4,    /* accept_len outside [0, K]: bonus -1, miss */
+    SSD_DEVERR_SLOT_RANGE = 8    /* a hit whose slot lies outside [0, Bf): next draft -1 */
 };
 
 /* Limits of this build. */
@@ -170,6 +171,19 @@ ssd_status ssd_cache_lookup(int32_t B, int32_t K, int32_t V, const int32_t* F_ho
                             int32_t fallback, ssd_rng rng, uint8_t* hit, int32_t* slot,
                             int32_t* fallback_tokens, int32_t* dev_err, void* stream);
 
+/* ssd_cache_gather -- the next round's draft from the speculation cache ([zh] section
+ * 2 basic flow step 4: on a hit the pre-speculated tokens are available at once, on a
+ * miss the fallback speculator takes over; [nl] section 2 Kernprincipes).  Reading of
+ * the pages: the cache holds one continuation of K tokens per cached outcome, in a
+ * value store values[B, Bf, K] (int32, slot-major as ssd_cache_lookup numbers the
+ * slots).  next_draft[b, :] = values[b, slot[b], :] when hit[b], else
+ * fallback_tokens[b, :] (uniform random tokens, or -1 = the caller's speculator).  A
+ * hit whose slot lies outside [0, Bf) gives -1 and sets SSD_DEVERR_SLOT_RANGE.
+ * hit [B] uint8, slot [B], fallback_tokens [B, K], next_draft [B, K] int32. */
+ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* values, const uint8_t* hit,
+                            const int32_t* slot, const int32_t* fallback_tokens, int32_t* next_draft,
+                            int32_t* dev_err, void* stream);
+
 /* Outputs of the fused round.  Required: cache_ids [B, Bf], accept_len [B], bonus
  * [B], hit [B], slot [B], fallback_tokens [B, K].  The rest are nullable. */
 typedef struct {
@@ -190,6 +204,9 @@ typedef struct {
     int32_t* slot;
     int32_t* fallback_tokens;
     int32_t* dev_err;   /* [B], OR-accumulated */
+    const int32_t* cache_values;  /* input [B, Bf, K]: continuation per cache slot (needed when
+                                     next_draft is given and Bf > 0) */
+    int32_t* next_draft;          /* nullable [B, K]: the next draft, as ssd_cache_gather makes it */
 } ssd_round_out;
 
 /* Optional HIP events (hipEvent_t, may be NULL) recorded on `stream` around the

@@ -24,8 +24,8 @@ SSD_DEVERR_TOKEN_RANGE, SSD_DEVERR_QPRIME_ZERO, SSD_DEVERR_LEN_RANGE = 1, 2, 4
 SSD_MAX_K, SSD_MAX_F = 16, 64
 
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
-            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_round", "ssd_status_string",
-            "ssd_last_error")
+            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_round",
+            "ssd_status_string", "ssd_last_error")
 
 
 class SSDError(RuntimeError):
@@ -49,7 +49,7 @@ _P = ctypes.c_void_p
 class ssd_round_out(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("p_max", "p_sum", "p_argmax", "q_max", "q_sum", "q_argmax", "cache_ids",
                                   "cache_mass", "Z", "accept_len", "accept_prob", "bonus", "resid_mass", "hit",
-                                  "slot", "fallback_tokens", "dev_err")]
+                                  "slot", "fallback_tokens", "dev_err", "cache_values", "next_draft")]
 
 
 class ssd_round_events(ctypes.Structure):
@@ -72,6 +72,7 @@ def _load():
     L.ssd_verify.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, f32, ssd_rng, _P, _P, _P, _P]
     L.ssd_residual_sample.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, f32, _P, ssd_rng, _P, _P, _P,
                                       _P, sz, _P]
+    L.ssd_cache_gather.argtypes = [i32, i32, i32, _P, _P, _P, _P, _P, _P, _P]
     L.ssd_cache_lookup.argtypes = [i32, i32, i32, _P, i32, _P, _P, _P, i32, ssd_rng, _P, _P, _P, _P, _P]
     L.ssd_round.argtypes = [S, _P, _P, _P, _P, i32, f32, ssd_rng, i32, ctypes.POINTER(ssd_round_out),
                             ctypes.POINTER(ssd_round_events), _P, sz, _P]
@@ -265,11 +266,21 @@ def ssd_cache_lookup(B, K, V, F, cache_ids, accept_len, bonus, fallback, seed, r
                                  _stream(stream)), "ssd_cache_lookup")
 
 
+def ssd_cache_gather(values, hit, slot, fallback_tokens, next_draft, dev_err=None, stream=None):
+    """values [B, Bf, K] int32 -> next_draft [B, K] (device tensors)."""
+    B, Bf, K = (int(x) for x in values.shape)
+    _check(_lib.ssd_cache_gather(B, K, Bf, _ptr(values, torch.int32), _ptr(hit, torch.uint8, "hit"),
+                                 _ptr(slot, torch.int32, "slot"), _ptr(fallback_tokens, torch.int32, "fallback_tokens"),
+                                 _ptr(next_draft, torch.int32, "next_draft"), _ptr(dev_err, torch.int32),
+                                 _stream(stream)), "ssd_cache_gather")
+
+
 _ROUND_DTYPES = {"p_max": torch.float32, "p_sum": torch.float64, "p_argmax": torch.int32, "q_max": torch.float32,
                  "q_sum": torch.float64, "q_argmax": torch.int32, "cache_ids": torch.int32,
                  "cache_mass": torch.float64, "Z": torch.float64, "accept_len": torch.int32,
                  "accept_prob": torch.float32, "bonus": torch.int32, "resid_mass": torch.float64,
-                 "hit": torch.uint8, "slot": torch.int32, "fallback_tokens": torch.int32, "dev_err": torch.int32}
+                 "hit": torch.uint8, "slot": torch.int32, "fallback_tokens": torch.int32, "dev_err": torch.int32,
+                 "cache_values": torch.int32, "next_draft": torch.int32}
 
 
 def make_round_out(**tensors) -> ssd_round_out:
@@ -297,7 +308,7 @@ def ssd_round(shape, p_logits, q_logits, draft, F, C, seed, round_, fallback, ou
 class RoundBuffers:
     """Device output tensors of one fused round (all outputs materialised)."""
 
-    def __init__(self, B: int, K: int, Bf: int, device=None, with_stats: bool = True):
+    def __init__(self, B: int, K: int, Bf: int, device=None, with_stats: bool = True, cache_values=None):
         dev = device or torch.cuda.current_device()
         R = B * (K + 1)
         f32, f64, i32 = torch.float32, torch.float64, torch.int32
@@ -309,7 +320,12 @@ class RoundBuffers:
         if with_stats:
             self.t.update({"p_max": z(R, f32), "p_sum": z(R, f64), "p_argmax": z(R, i32), "q_max": z(R, f32),
                            "q_sum": z(R, f64), "q_argmax": z(R, i32)})
-        self.out = make_round_out(**self.t)
+        if cache_values is not None:  # value store [B, Bf, K]: the round also writes the next draft
+            self.t["next_draft"] = z((B, K), i32)
+            self.values = cache_values
+            self.out = make_round_out(cache_values=cache_values if Bf > 0 else None, **self.t)
+        else:
+            self.out = make_round_out(**self.t)
 
     def __getitem__(self, k):
         return self.t[k]

@@ -414,6 +414,18 @@ ssd_status ssd_cache_lookup(int32_t B, int32_t K, int32_t V, const int32_t* F_ho
     return SSD_OK;
 }
 
+ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* values, const uint8_t* hit,
+                            const int32_t* slot, const int32_t* fallback_tokens, int32_t* next_draft,
+                            int32_t* dev_err, void* stream) {
+    if (B < 1 || K < 1 || K > SSD_MAX_K || Bf < 0) return SSD_ERR_ARG;
+    if ((Bf > 0 && !values) || !hit || !slot || !fallback_tokens || !next_draft) return SSD_ERR_ARG;
+    if ((int64_t)B * K > 0x7FFFFFFFLL) return SSD_ERR_UNSUPPORTED;  // one thread per token, 32-bit grid
+    hipError_t e = ssd::launch_gather(B, K, Bf, values, hit, slot, fallback_tokens, next_draft, dev_err,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "ssd_cache_gather");
+    return SSD_OK;
+}
+
 ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
                      const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, int32_t fallback,
                      const ssd_round_out* out, const ssd_round_events* ev, void* ws, size_t ws_bytes, void* stream) {
@@ -426,6 +438,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     if ((Bf > 0 && !out->cache_ids) || !out->accept_len || !out->bonus || !out->hit || !out->slot ||
         !out->fallback_tokens)
         return SSD_ERR_ARG;
+    if (out->next_draft && Bf > 0 && !out->cache_values) return SSD_ERR_ARG;
     Layout L;
     if ((st = check_ws(s, Bf, ws, ws_bytes, &L)) != SSD_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
@@ -491,6 +504,8 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     f.fallback_tokens = out->fallback_tokens;
     f.dev_err = out->dev_err;
     f.vflag = at<int32_t>(ws, L.vflag);
+    f.cache_values = out->cache_values;
+    f.next_draft = out->next_draft;
 
     const bool vec = vec_ok(s, p_logits) && vec_ok(s, q_logits);
     hipError_t e;
@@ -536,6 +551,8 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.resid_mass = out->resid_mass;
     b.dev_err = out->dev_err;
     b.do_lookup = 1;
+    b.cache_values = out->cache_values;
+    b.next_draft = out->next_draft;
     b.fallback = fallback;
     b.hit = out->hit;
     b.slot = out->slot;

@@ -78,6 +78,8 @@ struct SeqFinal {
     int32_t* slot;
     int32_t* fallback_tokens;
     int32_t* dev_err;     // nullable
+    const int32_t* cache_values;  // nullable [B, Bf, K]: continuation per cache slot
+    int32_t* next_draft;          // [B, K] when cache_values is set
     int32_t* vflag;       // [B, K] workspace: bit 0 accepted, higher bits error bits
 };
 
@@ -108,6 +110,8 @@ struct Pass2Args {
     double* resid_mass; // nullable
     int32_t* dev_err;   // nullable
     int do_lookup;
+    const int32_t* cache_values;  // nullable [B, Bf, K] (with do_lookup)
+    int32_t* next_draft;          // [B, K] when cache_values is set
     int fallback;
     uint8_t* hit;
     int32_t* slot;
@@ -142,6 +146,8 @@ hipError_t launch_verify(int dtype, const char* p_logits, const char* q_logits, 
 // (bonus), mass[b] = 1.
 hipError_t launch_greedy_pick(const int32_t* arg, int B, int K, const int32_t* accept_len, int32_t* out,
                               double* mass, int32_t* dev_err, hipStream_t st);
+hipError_t launch_gather(int B, int K, int Bf, const int32_t* values, const uint8_t* hit, const int32_t* slot,
+                         const int32_t* fallback_tokens, int32_t* next_draft, int32_t* dev_err, hipStream_t st);
 hipError_t launch_lookup(int B, int K, int V, const int* F, const int* O, int Bf, const int32_t* cache_ids,
                          const int32_t* accept_len, const int32_t* bonus, int fallback, uint64_t seed,
                          uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* dev_err,

@@ -33,7 +33,7 @@
 namespace ssd {
 
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
-enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4 };
+enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange = 8 };
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
 constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
 constexpr int kStageCap = 160;     // LDS slots per wave for one tile's candidate keys (>= any cap)
@@ -444,17 +444,27 @@ __device__ __forceinline__ double finish_cache_row(uint64_t key, int F, float mq
     return wave_sum_f64(t);
 }
 
+// Value store of the speculation cache: one continuation of K tokens per cache slot
+// (values [B, Bf, K]); when values is set the lookup also writes the next draft.
+struct ValueStore {
+    const int32_t* values = nullptr;
+    int Bf = 0;
+    int32_t* next_draft = nullptr;
+};
+
 // Cache lookup of one verified outcome (k, tok) by one wave, plus the uniform
 // fallback draft on a miss.  my_id: lane j < F_k holds the j-th cached id of outcome
 // k (slot O_k + j); other lanes, and every lane when k is invalid (k < 0), hold -1.
 __device__ inline void lookup_wave(int b, int K, int V, int k, int Ok, int my_id, int tok, int fallback,
-                                   uint64_t seed, uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fb) {
+                                   uint64_t seed, uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fb,
+                                   const ValueStore& vs = ValueStore{}) {
     const int lane = lane_id();
     const uint64_t mk = __ballot(k >= 0 && my_id >= 0 && my_id == tok);
     const bool h = mk != 0ull;
+    const int sl = h ? Ok + (__ffsll((long long)mk) - 1) : -1;
     if (lane == 0) {
         hit[b] = h ? 1 : 0;
-        slot[b] = h ? Ok + (__ffsll((long long)mk) - 1) : -1;
+        slot[b] = sl;
     }
     for (int j = lane; j < K; j += kWave) {
         int32_t t = -1;
@@ -463,6 +473,8 @@ __device__ inline void lookup_wave(int b, int K, int V, int k, int Ok, int my_id
             t = (int32_t)((u32 * (uint64_t)V) >> 32);
         }
         fb[(int64_t)b * K + j] = t;
+        // next round's draft: the cached continuation on a hit, the fallback otherwise
+        if (vs.next_draft) vs.next_draft[(int64_t)b * K + j] = h ? vs.values[((int64_t)b * vs.Bf + sl) * K + j] : t;
     }
 }
 
@@ -862,7 +874,8 @@ __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f)
         f.bonus[b] = tok;
         if (f.resid_mass) f.resid_mass[b] = 1.0;
     }
-    lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens);
+    lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens,
+                ValueStore{f.cache_values, f.Bf, f.next_draft});
 }
 
 // ============================================================================ pass 2
@@ -1147,7 +1160,7 @@ __device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int
     }
     if (a.mode == 0 && a.do_lookup)
         lookup_wave(b, K, a.V, valid ? pos : -1, valid ? a.O[pos] : 0, my_id, tok, a.fallback, a.seed, a.round, a.hit,
-                    a.slot, a.fallback_tokens);
+                    a.slot, a.fallback_tokens, ValueStore{a.cache_values, a.Bf, a.next_draft});
 }
 
 // One wave per group when the bonus runs as a kernel of its own.
@@ -1339,6 +1352,24 @@ __global__ void lookup_kernel(int B, int K, int V, FO fo, int Bf, const int32_t*
     lookup_wave(b, K, V, ok ? k : -1, ok ? fo.O[k] : 0, my_id, bonus[b], fallback, seed, round, hit, slot, fb);
 }
 
+// Next draft from the value store for the separate call: one thread per (b, j).
+__global__ void gather_kernel(int B, int K, int Bf, const int32_t* values, const uint8_t* hit, const int32_t* slot,
+                              const int32_t* fb, int32_t* next_draft, int32_t* dev_err) {
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (int64_t)B * K) return;
+    const int b = (int)(x / K), j = (int)(x % K);
+    int32_t t;
+    if (!hit[b]) {
+        t = fb[x];
+    } else if (slot[b] < 0 || slot[b] >= Bf) {
+        t = -1;
+        if (j == 0 && dev_err) dev_err[b] |= kErrSlotRange;
+    } else {
+        t = values[((int64_t)b * Bf + slot[b]) * K + j];
+    }
+    next_draft[x] = t;
+}
+
 // ============================================================================ launchers
 static FO make_fo(const int* F, const int* O, int K1) {
     FO fo;
@@ -1458,6 +1489,14 @@ hipError_t launch_greedy_pick(const int32_t* arg, int B, int K, const int32_t* a
                               int32_t* dev_err, hipStream_t st) {
     const int n = accept_len ? B : B * K;
     greedy_pick_kernel<<<(n + 255) / 256, 256, 0, st>>>(arg, B, K, accept_len, out, mass, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(int B, int K, int Bf, const int32_t* values, const uint8_t* hit, const int32_t* slot,
+                         const int32_t* fallback_tokens, int32_t* next_draft, int32_t* dev_err, hipStream_t st) {
+    const int64_t n = (int64_t)B * K;
+    gather_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(B, K, Bf, values, hit, slot, fallback_tokens,
+                                                               next_draft, dev_err);
     return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
 
 F32, BF16 = 0, 1
 PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
-ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE = 1, 2, 4
+ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE, ERR_SLOT_RANGE = 1, 2, 4, 8
 E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
 FANOUT_EPS = 1e-9
 # Half-width of the inverse-CDF near-tie band (E2) on the normalised CDF.
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.orc_residual_sample.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, P, P, P, P, P, P, i32, P,
                                           P, dbl, P, u64, u64, i64, dbl, P, P, P, P, P, P]
         L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, i64, P, P, P, P]
+        L.orc_cache_gather.argtypes = [i32, i32, i32, P, P, P, P, P, P]
         L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i64, dbl, i32,
                                 P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -239,6 +240,21 @@ def cache_lookup(K, V, F, cache_ids, accept_len, bonus, fallback_uniform, seed, 
                            int(bool(fallback_uniform)), seed, round_, b_base, _ptr(hit), _ptr(slot), _ptr(fb),
                            _ptr(err))
     return hit, slot, fb, err
+
+
+def cache_gather(values, hit, slot, fallback_tokens):
+    """Next round's draft [B, K] from the value store values [B, Bf, K] (int32): the
+    cached continuation on a hit, the fallback tokens on a miss."""
+    values = np.ascontiguousarray(values, dtype=np.int32)
+    hit = np.ascontiguousarray(hit, dtype=np.uint8)
+    slot = np.ascontiguousarray(slot, dtype=np.int32)
+    fallback_tokens = np.ascontiguousarray(fallback_tokens, dtype=np.int32)
+    B, Bf, K = values.shape
+    nd = np.zeros((B, K), dtype=np.int32)
+    err = np.zeros(B, dtype=np.int32)
+    lib().orc_cache_gather(B, K, Bf, _ptr(values), _ptr(hit), _ptr(slot), _ptr(fallback_tokens), _ptr(nd),
+                           _ptr(err))
+    return nd, err
 
 
 @dataclass

@@ -57,6 +57,7 @@
 #define ORC_ERR_TOKEN_RANGE 1   /* a draft token outside [0, V) */
 #define ORC_ERR_QPRIME_ZERO 2   /* q'(d) == 0 for a tested draft token */
 #define ORC_ERR_LEN_RANGE 4     /* accept_len outside [0, K] given to a step */
+#define ORC_ERR_SLOT_RANGE 8    /* a hit whose slot lies outside [0, Bf) */
 
 /* Near-tie / range exception bits (per sequence), decided from fp64 values. */
 #define ORC_E1_ACCEPT_TIE 1
@@ -555,6 +556,34 @@ void orc_cache_lookup(int B, int K, int V, const int32_t* F, int Bf, const int32
                 t = (int32_t)((x * (uint64_t)V) >> 32);
             }
             fallback_tokens[(int64_t)b * K + j] = t;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Next round's draft from the speculation cache ([zh] section 2 basic flow, step 4:
+ * on a hit the pre-speculated tokens are returned at once; on a miss the fallback
+ * speculator takes over; [nl] section 2 Kernprincipes).
+ * READING: the cache holds, for every cached outcome (slot = O_k + rank), one
+ * continuation of K tokens, values[b][slot][0..K-1].  On a hit the next draft is that
+ * continuation; on a miss it is the fallback tokens of the lookup (the uniform random
+ * speculator's K tokens, or -1 = left to the caller's primary speculator).  A hit
+ * whose slot lies outside [0, Bf) is invalid input: error bit, next draft -1. */
+void orc_cache_gather(int B, int K, int Bf, const int32_t* values, const uint8_t* hit,
+                      const int32_t* slot, const int32_t* fallback_tokens, int32_t* next_draft,
+                      int32_t* err) {
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < K; ++j) {
+            int32_t t;
+            if (!hit[b]) {
+                t = fallback_tokens[(int64_t)b * K + j];
+            } else if (slot[b] < 0 || slot[b] >= Bf) {
+                t = -1;
+                if (err && j == 0) err[b] |= ORC_ERR_SLOT_RANGE;
+            } else {
+                t = values[((int64_t)b * Bf + slot[b]) * K + j];
+            }
+            next_draft[(int64_t)b * K + j] = t;
         }
     }
 }

@@ -30,19 +30,22 @@ def oracle_draft(zp_np, zq_np, T, F, C, seed, rnd, b_base=0):
     return d, flags
 
 
-def gpu_round(zp, zq, T, F, C, draft, seed, rnd, fallback, ws=None):
+def gpu_round(zp, zq, T, F, C, draft, seed, rnd, fallback, ws=None, values=None):
+    """One fused round; values (numpy [B, Bf, K] int32) also asks for the next draft."""
     shape = ssd.shape_of(zp, T)
     B, K = shape.B, shape.K
-    buf = ssd.RoundBuffers(B, K, int(sum(F)))
+    vals = None if values is None else torch.as_tensor(np.ascontiguousarray(values), device="cuda")
+    buf = ssd.RoundBuffers(B, K, int(sum(F)), cache_values=vals)
     d = torch.as_tensor(np.ascontiguousarray(draft), dtype=torch.int32, device="cuda")
     ssd.ssd_round(shape, zp, zq, d, list(F), C, seed, rnd, fallback, buf.out, ws=ws)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in buf.t.items()}
 
 
-def compare_round(g, o, K, Bf, check_stats=True, label=""):
+def compare_round(g, o, K, Bf, check_stats=True, label="", values=None):
     """Asserts parity of a GPU fused round g (dict of numpy) with an oracle round o
-    (oracle.RoundResult).  Returns the number of flagged sequences."""
+    (oracle.RoundResult); with the value store values [B, Bf, K] also the next draft.
+    Returns the number of flagged sequences."""
     B = o.accept_len.shape[0]
     R = B * (K + 1)
     if check_stats:
@@ -70,4 +73,11 @@ def compare_round(g, o, K, Bf, check_stats=True, label=""):
     assert np.array_equal(g["hit"][ok2], o.hit[ok2]), label
     assert np.array_equal(g["slot"][ok2], o.slot[ok2]), label
     assert np.array_equal(g["fallback_tokens"][ok2], o.fallback_tokens[ok2]), label
+    if values is not None:
+        nd, nerr = oracle.cache_gather(values, o.hit, o.slot, o.fallback_tokens)
+        assert not nerr.any(), label
+        assert np.array_equal(g["next_draft"][ok2], nd[ok2]), (label, "next_draft")
+        # flagged sequences: the next draft still follows the GPU's own hit / slot
+        nd_g, _ = oracle.cache_gather(values, g["hit"], g["slot"], g["fallback_tokens"])
+        assert np.array_equal(g["next_draft"], nd_g), (label, "next_draft self")
     return int(e_any.sum())

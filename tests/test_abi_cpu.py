@@ -146,6 +146,15 @@ def test_cache_and_round_validation(ssd):
                        ws, 1 << 30, None) == ssd.SSD_ERR_ARG
     assert L.ssd_round(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0, ctypes.byref(out), None,
                        ws, 64, None) == ssd.SSD_ERR_WORKSPACE
+    # fused round: a next draft with Bf > 0 needs the value store
+    out.next_draft = 0x3000
+    assert L.ssd_round(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0, ctypes.byref(out), None,
+                       ws, 1 << 30, None) == ssd.SSD_ERR_ARG
+    # gather: bad sizes, missing buffers, too many tokens for one launch
+    for B, K, Bf, vals, nd in ((0, 4, 3, BAD, BAD), (2, 0, 3, BAD, BAD), (2, 17, 3, BAD, BAD), (2, 4, -1, BAD, BAD),
+                               (2, 4, 3, None, BAD), (2, 4, 3, BAD, None)):
+        assert L.ssd_cache_gather(B, K, Bf, vals, BAD, BAD, BAD, nd, None, None) == ssd.SSD_ERR_ARG
+    assert L.ssd_cache_gather(1 << 28, 16, 3, BAD, BAD, BAD, BAD, BAD, None, None) == ssd.SSD_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_host_tensors(ssd):

@@ -200,15 +200,20 @@ def test_round_vs_oracle_and_chain(case):
     draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
     o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, fb)
     zpd, zqd = zp.cuda(), zq.cuda()
-    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb)
-    compare_round(g, o, K, sum(F), label=label)
+    values = np.random.default_rng(B + K).integers(0, V, (B, sum(F), K)).astype(np.int32)
+    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb, values=values)
+    compare_round(g, o, K, sum(F), label=label, values=values)
     ch = _chain(zpd, zqd, T, F, C, draft, seed, rnd, fb)
     for k in ch:
         a, b = g[k], ch[k]
         if k == "cache_ids":
             a, b = a[:, :sum(F)], b[:, :sum(F)]
         assert np.array_equal(a, b), (label, k)
-    g2 = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    t = lambda x: torch.as_tensor(np.ascontiguousarray(x), device="cuda")  # noqa: E731
+    nd = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+    ssd.ssd_cache_gather(t(values), t(ch["hit"]), t(ch["slot"]), t(ch["fallback_tokens"]), nd)
+    assert np.array_equal(nd.cpu().numpy(), g["next_draft"]), (label, "next_draft chain")
+    g2 = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb, values=values)
     for k in g:
         assert np.array_equal(g[k], g2[k]), ("determinism", label, k)
 
@@ -272,6 +277,27 @@ def test_lookup_oracle_fed():
         assert np.array_equal(slot.cpu().numpy(), osl)
         assert np.array_equal(fb.cpu().numpy(), ofb)
         assert np.array_equal(err.cpu().numpy(), oerr)
+
+
+def test_cache_gather_oracle_fed():
+    """ssd_cache_gather on oracle-made inputs: hits, misses with uniform or -1
+    fallback tokens, and hits whose slot lies outside [0, Bf)."""
+    rng = np.random.default_rng(11)
+    for B, K, Bf in ((300, 4, 15), (5, 16, 1), (4, 3, 0), (70000, 8, 40)):
+        _case("gather oracle-fed B=%d K=%d Bf=%d" % (B, K, Bf))
+        values = rng.integers(0, 128256, (B, Bf, K)).astype(np.int32)
+        hit = (rng.random(B) < 0.6).astype(np.uint8) if Bf > 0 else np.zeros(B, np.uint8)
+        slot = np.where(hit == 1, rng.integers(-2, Bf + 2, B), -1).astype(np.int32)
+        fbt = rng.integers(-1, 128256, (B, K)).astype(np.int32)
+        ond, oerr = oracle.cache_gather(values, hit, slot, fbt)
+        t = lambda x: torch.as_tensor(np.ascontiguousarray(x), device="cuda")  # noqa: E731
+        nd = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+        err = torch.zeros(B, dtype=torch.int32, device="cuda")
+        ssd.ssd_cache_gather(t(values), t(hit), t(slot), t(fbt), nd, err)
+        torch.cuda.synchronize()
+        assert np.array_equal(nd.cpu().numpy(), ond)
+        assert np.array_equal(err.cpu().numpy(), oerr)
+        assert B < 100 or oerr.any()
 
 
 def test_residual_bad_len_and_greedy():
@@ -349,7 +375,8 @@ def test_full_size_sampled(name, C, sig):
         draft[b] = d[0]
         per[int(b)] = (zp_np, zq_np)
     _case("full-size %s: GPU round" % name)
-    g = gpu_round(zp, zq, T, F.tolist(), C, draft, seed, rnd, int(w.fallback_uniform))
+    values = rng.integers(0, w.V, size=(w.B, w.Bf, w.K)).astype(np.int32)
+    g = gpu_round(zp, zq, T, F.tolist(), C, draft, seed, rnd, int(w.fallback_uniform), values=values)
     _case("full-size %s: oracle on %s" % (name, sample.tolist()))
     for b in sample:
         zp_np, zq_np = per[int(b)]
@@ -357,7 +384,7 @@ def test_full_size_sampled(name, C, sig):
         K1 = w.K + 1
         gb = {k: (v[b * K1:(b + 1) * K1] if v.ndim == 1 and v.shape[0] == w.B * K1 else v[b:b + 1])
               for k, v in g.items()}
-        compare_round(gb, o, w.K, w.Bf, label="%s b=%d" % (name, b))
+        compare_round(gb, o, w.K, w.Bf, label="%s b=%d" % (name, b), values=values[b:b + 1])
     # properties that hold for every sequence
     assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= w.K))
     assert np.all((g["bonus"] >= 0) & (g["bonus"] < w.V))
@@ -369,4 +396,6 @@ def test_full_size_sampled(name, C, sig):
         assert g["hit"][b] == h
         if not h and w.fallback_uniform:
             assert np.all((g["fallback_tokens"][b] >= 0) & (g["fallback_tokens"][b] < w.V))
+    nd, _ = oracle.cache_gather(values, g["hit"], g["slot"], g["fallback_tokens"])
+    assert np.array_equal(g["next_draft"], nd)
     assert np.all(g["dev_err"] == 0)

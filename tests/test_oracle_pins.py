@@ -365,3 +365,25 @@ def test_lookup_bruteforce(orc):
                     assert 0 <= fb[b, j] < V
         assert np.all(err == 0)
     assert 0 < hit.sum() < B
+
+
+def test_cache_gather_matches_fancy_indexing(orc):
+    """Pin of the next-draft gather: on a hit the cached continuation
+    values[b, slot[b], :], on a miss the fallback tokens; a hit with a slot outside
+    [0, Bf) is flagged and yields -1 (numpy fancy indexing as the reference)."""
+    rng = np.random.default_rng(11)
+    B, Bf, K = 40, 24, 6
+    values = rng.integers(0, 50000, size=(B, Bf, K), dtype=np.int32)
+    hit = (rng.random(B) < 0.5).astype(np.uint8)
+    slot = np.where(hit == 1, rng.integers(0, Bf, size=B), -1).astype(np.int32)
+    fb = rng.integers(-1, 50000, size=(B, K), dtype=np.int32)
+    bad = [3, 7]
+    hit[bad] = 1
+    slot[3], slot[7] = Bf, -2
+    nd, err = orc.cache_gather(values, hit, slot, fb)
+    ok = (hit == 1) & (slot >= 0) & (slot < Bf)
+    expect = np.where(ok[:, None], values[np.arange(B), np.clip(slot, 0, Bf - 1)], fb)
+    expect[(hit == 1) & ~ok] = -1
+    assert np.array_equal(nd, expect)
+    assert np.array_equal(err != 0, (hit == 1) & ~ok)
+    assert np.all(err[(hit == 1) & ~ok] == orc.ERR_SLOT_RANGE)
