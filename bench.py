@@ -124,17 +124,21 @@ def main():
         b.record()
     torch.cuda.synchronize()
     evs = [ssd.ssd_round_events(a.cuda_event, b.cuda_event, None, None) for a, b in ev]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # the K rounds run back to back; events at 5 chunk boundaries give the repeat spread
+    nrep = 5 if n >= 5 else 1
+    bounds = [n * j // nrep for j in range(nrep + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record()
-    for i in range(n):
-        step(args.warmup + i, evs[i])
-    t1.record()
+    marks[0].record()
+    for j in range(nrep):
+        for i in range(bounds[j], bounds[j + 1]):
+            step(args.warmup + i, evs[i])
+        marks[j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    rep_us = [marks[j].elapsed_time(marks[j + 1]) * 1e3 / (bounds[j + 1] - bounds[j]) for j in range(nrep)]
     pass1_ms = [a.elapsed_time(b) for a, b in ev]
     pass1_avg_ms = float(np.mean(pass1_ms))
     ms_per_step = total_ms / n
@@ -201,7 +205,10 @@ def main():
             "round_GBps": round(round_gbps, 1),
             "round_frac_of_peak": round(round_gbps / PEAK_HBM_GBPS, 4),
             "pass1_us": round(pass1_avg_ms * 1e3, 2),
+            "us_per_round_median_of_%d_repeats" % nrep: round(float(np.median(rep_us)), 2),
+            "us_per_round_repeats": [round(x, 2) for x in rep_us],
             "copy_GBps_read_plus_write": round(copy_gbps, 1),
+            "pass1_frac_of_copy": round(pass1_gbps / copy_gbps, 4),
             "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
             "mean_accept_len": round(float(ks.mean()), 3),
             "hit_rate": round(float(hits.mean()), 4),
@@ -267,6 +274,7 @@ def cpu_baseline(w, buf, T, C, F, seconds):
     ids, mass = oracle.build_cache(zq_np, T, Fa)
     Z, _ = oracle.saguaro(zq_np, T, Fa, ids, mass, C)
     draft, _ = oracle.draft_sample(zq_np, T, Fa, ids, Z, C, w.seed, 0)
+    threads = oracle.num_threads()
     rounds = 0
     t0 = time.perf_counter()
     while True:
@@ -275,10 +283,35 @@ def cpu_baseline(w, buf, T, C, F, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or rounds >= 50:
             break
-    log("cpu baseline: %d oracle rounds in %.2f s" % (rounds, el))
-    return {"value": round(rounds / el, 4), "unit": "rounds/s", "cores": oracle.num_threads(), "kind": "oracle",
+    log("cpu baseline: %d oracle rounds in %.2f s on %d threads" % (rounds, el, threads))
+    # one thread, on the first 4 sequences of the batch, scaled to whole rounds
+    nb = min(4, w.B)
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.round_(zp_np[:nb], zq_np[:nb], T, Fa, C, draft[:nb], w.seed, 0, w.fallback_uniform)
+        el1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    one = nb / w.B / el1
+    log("cpu baseline, 1 thread: %d sequences in %.2f s" % (nb, el1))
+    return {"value": round(rounds / el, 4), "unit": "rounds/s", "cores": threads, "kind": "oracle",
             "sample": "%d whole rounds (B=%d sequences each) of the timed workload's first logit buffer" % (
-                rounds, w.B)}
+                rounds, w.B),
+            "cpu_model": cpu_model(),
+            "value_1_thread": round(one, 5),
+            "sample_1_thread": "one round of the first %d sequences, scaled to B=%d" % (nb, w.B)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.partition(":")[2].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         i32, i64, u64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = None
         L.orc_philox4x64_10.argtypes = [P, P, P]
         L.orc_uniform.argtypes = [u64, u64, i32, i64, i64]
         L.orc_uniform.restype = dbl
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
                                           P, dbl, P, u64, u64, i64, dbl, P, P, P, P, P, P]
         L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, i64, P, P, P, P]
         L.orc_cache_gather.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+        L.orc_bonus_rank.argtypes = [i32, i32, i32, i64, i32, P, P, P, i32, P, P]
         L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i64, dbl, i32,
                                 P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         _lib = L
@@ -107,6 +110,10 @@ def _base(z):
 # ---------------------------------------------------------------------------
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 def philox4x64_10(ctr, key):
@@ -255,6 +262,75 @@ def cache_gather(values, hit, slot, fallback_tokens):
     lib().orc_cache_gather(B, K, Bf, _ptr(values), _ptr(hit), _ptr(slot), _ptr(fallback_tokens), _ptr(nd),
                            _ptr(err))
     return nd, err
+
+
+def bonus_rank(zq, accept_len, bonus, R: int, hist=None):
+    """Rank of each bonus token within draft row k = accept_len (cache order: larger
+    logit first, ties to the lower id), -1 for an invalid (k, bonus); and the
+    coverage histogram hist[K+1, R+1] (uint32, bin R = rank >= R), accumulated into
+    `hist` when given."""
+    code, B, K, V, ld = _logit_info(zq)
+    accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
+    bonus = np.ascontiguousarray(bonus, dtype=np.int32)
+    rank = np.zeros(B, dtype=np.int32)
+    if hist is None:
+        hist = np.zeros((K + 1, R + 1), dtype=np.uint32)
+    assert hist.dtype == np.uint32 and hist.shape == (K + 1, R + 1) and hist.flags.c_contiguous
+    lib().orc_bonus_rank(B, K, V, ld, code, _base(zq), _ptr(accept_len), _ptr(bonus), R, _ptr(rank), _ptr(hist))
+    return rank, hist
+
+
+def fanout_optimize(hist, Bf: int, Fmax: int):
+    """Fan-out that maximises the number of hits the coverage histogram predicts
+    ([zh] section 2 Challenge 1 and [nl] section 3 A: the fan-out solves a
+    constrained optimisation; the objective is a reading).
+
+    hist [K+1, R+1]: sequences verified with acceptance length k whose bonus had rank
+    j in the draft row k (bin R: rank >= R).  Caching F_k candidates at length k
+    catches the ranks below F_k, so the predicted hits are
+        H(F) = sum_k sum_{j < F_k} hist[k, j],
+    maximised over integers 0 <= F_k <= min(Fmax, R) with sum_k F_k = Bf.  Among
+    maximisers the lexicographically largest F (most candidates at the shortest
+    lengths) is returned.  Exact integer dynamic programme over (k, budget left),
+    written as plain loops.  Returns (F int32 [K+1], predicted hits, total count);
+    None when Bf exceeds (K+1) * min(Fmax, R)."""
+    hist = np.asarray(hist)
+    K1, R1 = hist.shape
+    R = R1 - 1
+    cap = min(Fmax, R)
+    if Bf < 0 or Bf > K1 * cap:
+        return None
+    # cov[k][f] = hits caught at length k by caching f candidates
+    cov = [[0] * (cap + 1) for _ in range(K1)]
+    for k in range(K1):
+        run = 0
+        for f in range(1, cap + 1):
+            run += int(hist[k, f - 1])
+            cov[k][f] = run
+    # best[k][b]: most hits from lengths k..K with exactly b candidates (None: infeasible)
+    best = [[None] * (Bf + 1) for _ in range(K1 + 1)]
+    best[K1][0] = 0
+    for k in range(K1 - 1, -1, -1):
+        for b in range(Bf + 1):
+            top = None
+            for f in range(0, min(cap, b) + 1):
+                rest = best[k + 1][b - f]
+                if rest is None:
+                    continue
+                v = cov[k][f] + rest
+                if top is None or v > top:
+                    top = v
+            best[k][b] = top
+    F = np.zeros(K1, dtype=np.int32)
+    b = Bf
+    for k in range(K1):
+        for f in range(min(cap, b), -1, -1):  # largest f that stays optimal
+            rest = best[k + 1][b - f]
+            if rest is not None and cov[k][f] + rest == best[k][b]:
+                F[k] = f
+                b -= f
+                break
+    return F, int(best[0][Bf]), int(hist.sum())
 
 
 @dataclass

@@ -80,6 +80,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Sets the thread count of the OpenMP loops (no effect without OpenMP). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------- */
 /* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  * 1, 2, 3", SC'11): ten rounds of two 64x64->128 multiplications per round with the
@@ -585,6 +594,38 @@ void orc_cache_gather(int B, int K, int Bf, const int32_t* values, const uint8_t
             }
             next_draft[(int64_t)b * K + j] = t;
         }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Coverage statistics for choosing the fan-out ([zh] section 2 Challenge 1 and [nl]
+ * section 3 A call the fan-out the solution of a constrained optimisation over
+ * acceptance lengths).  READING: what the optimisation needs from each verified
+ * round is, per sequence, the acceptance length k and the rank of the bonus token
+ * within the draft row k in the cache order (larger logit first, ties to the lower
+ * id): the bonus would have been a hit with any F_k > rank.
+ *   rank = #{x : z_q[k](x) > z_q[k](t)} + #{x < t : z_q[k](x) = z_q[k](t)},
+ * t the bonus.  hist[k][min(rank, R)] counts the sequences (bin R: rank >= R).
+ * A sequence with k outside [0, K] or t outside [0, V) gets rank -1 and is not
+ * counted.  hist (nullable) is accumulated, not cleared. */
+void orc_bonus_rank(int B, int K, int V, int64_t ld, int dtype, const void* q_logits,
+                    const int32_t* accept_len, const int32_t* bonus, int R, int32_t* rank_out,
+                    uint32_t* hist) {
+    for (int b = 0; b < B; ++b) {
+        const int k = accept_len[b], t = bonus[b];
+        if (k < 0 || k > K || t < 0 || t >= V) {
+            if (rank_out) rank_out[b] = -1;
+            continue;
+        }
+        const int64_t row = ((int64_t)b * (K + 1) + k) * ld;
+        const double zt = load_logit(q_logits, dtype, row + t);
+        int64_t rank = 0;
+        for (int x = 0; x < V; ++x) {
+            const double zx = load_logit(q_logits, dtype, row + x);
+            if (zx > zt || (zx == zt && x < t)) ++rank;
+        }
+        if (rank_out) rank_out[b] = (int32_t)rank;
+        if (hist) hist[(int64_t)k * (R + 1) + (rank < R ? rank : R)] += 1u;
     }
 }
 

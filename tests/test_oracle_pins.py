@@ -387,3 +387,109 @@ def test_cache_gather_matches_fancy_indexing(orc):
     assert np.array_equal(nd, expect)
     assert np.array_equal(err != 0, (hit == 1) & ~ok)
     assert np.all(err[(hit == 1) & ~ok] == orc.ERR_SLOT_RANGE)
+
+
+# --------------------------------------------------------------------------- fan-out statistics
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bonus_rank_is_sorted_position(orc, dtype):
+    """Pin of the bonus rank: the position of the bonus token in draft row k sorted
+    by numpy lexsort (logit descending, id ascending), with heavy ties (coarse
+    logits), -inf entries and invalid (k, bonus) pairs; the histogram is numpy's
+    add.at of the capped ranks."""
+    rng = np.random.default_rng(21)
+    B, K, V, R = 60, 3, 97, 10
+    z = np.round(rng.standard_normal((B, K + 1, V)) * 2.0) / 2.0
+    z[rng.random(z.shape) < 0.05] = -np.inf
+    z = z.astype(np.float32)
+    if dtype == "bf16":
+        z = (z.view(np.uint32) >> 16).astype(np.uint16)  # exact: the values have short mantissas
+    acc = rng.integers(-1, K + 2, B).astype(np.int32)
+    bon = rng.integers(-2, V + 2, B).astype(np.int32)
+    hist0 = rng.integers(0, 5, (K + 1, R + 1)).astype(np.uint32)
+    rank, hist = orc.bonus_rank(z, acc, bon, R, hist=hist0.copy())
+    zw = _widen(z)
+    expect_hist = hist0.copy()
+    for b in range(B):
+        k, t = acc[b], bon[b]
+        if not (0 <= k <= K and 0 <= t < V):
+            assert rank[b] == -1
+            continue
+        order = np.lexsort((np.arange(V), -zw[b, k]))
+        pos = int(np.nonzero(order == t)[0][0])
+        assert rank[b] == pos, (b, k, t)
+        np.add.at(expect_hist, (k, min(pos, R)), 1)
+    assert np.array_equal(hist, expect_hist)
+    assert (rank >= 0).sum() > B // 3
+
+
+def test_bonus_rank_agrees_with_cache_membership(orc):
+    """rank < F_k exactly when the token is among the F_k cached ids of row k (the
+    cache build is an independent sort of the same row)."""
+    rng = np.random.default_rng(22)
+    B, K, V = 12, 4, 300
+    z = _rand_logits(rng, B, K, V, dtype="bf16")
+    F = np.array([9, 5, 3, 2, 1], np.int32)
+    ids, _ = orc.build_cache(z, 1.0, F)
+    O = np.concatenate([[0], np.cumsum(F)])
+    for k in range(K + 1):
+        for trial in range(6):
+            tok = rng.integers(0, V, B).astype(np.int32)
+            if trial % 2:
+                tok = ids[:, O[k] + rng.integers(0, F[k])] if F[k] else tok
+            rank, _ = orc.bonus_rank(z, np.full(B, k, np.int32), tok, 64)
+            for b in range(B):
+                assert (rank[b] < F[k]) == (tok[b] in ids[b, O[k]:O[k + 1]]), (k, b)
+
+
+def _brute_fanout(hist, Bf, Fmax):
+    K1, R1 = hist.shape
+    cap = min(Fmax, R1 - 1)
+    best, arg = None, None
+    for F in itertools.product(range(cap + 1), repeat=K1):
+        if sum(F) != Bf:
+            continue
+        v = sum(int(hist[k, :F[k]].sum()) for k in range(K1))
+        if best is None or v > best or (v == best and F > arg):
+            best, arg = v, F
+    return arg, best
+
+
+def test_fanout_optimize_brute_force(orc):
+    """Pin of the fan-out optimiser: exhaustive search over every composition of Bf
+    (the same objective, the same lexicographic rule among maximisers)."""
+    rng = np.random.default_rng(23)
+    n = 0
+    for K1 in (1, 2, 3, 4):
+        for R in (1, 3, 5):
+            for Fmax in (2, 4, 8):
+                cap = min(Fmax, R)
+                for Bf in sorted({0, 1, cap, K1 * cap // 2, K1 * cap}):
+                    hist = rng.integers(0, 6, (K1, R + 1)) * (rng.random((K1, R + 1)) < 0.7)
+                    F, hits, total = orc.fanout_optimize(hist, Bf, Fmax)
+                    aF, ahits = _brute_fanout(hist, Bf, Fmax)
+                    assert tuple(int(x) for x in F) == aF, (K1, R, Fmax, Bf, hist)
+                    assert hits == ahits and total == int(hist.sum())
+                    n += 1
+    assert n > 100
+    assert orc.fanout_optimize(np.ones((3, 5)), 13, 4) is None
+    assert orc.fanout_optimize(np.ones((3, 5)), -1, 4) is None
+
+
+def test_fanout_optimize_special_cases(orc):
+    """No data: the budget fills the shortest lengths first.  A coverage that falls
+    off geometrically in both k and rank (every marginal distinct): the optimum
+    equals greedy allocation by largest marginal, which is exact for concave
+    coverage."""
+    F, hits, total = orc.fanout_optimize(np.zeros((4, 9), np.int64), 13, 6)
+    assert F.tolist() == [6, 6, 1, 0] and hits == 0 and total == 0
+    K1, R, Bf, Fmax = 9, 64, 64, 64
+    hist = np.array([[int(1e9 * 0.6 ** k * 0.83 ** j) + 3 * k + 7 * j for j in range(R + 1)]
+                     for k in range(K1)], np.int64)
+    F, hits, _ = orc.fanout_optimize(hist, Bf, Fmax)
+    g = np.zeros(K1, int)
+    for _ in range(Bf):
+        k = max(range(K1), key=lambda k: hist[k, g[k]] if g[k] < min(R, Fmax) else -1)
+        g[k] += 1
+    assert hits == sum(int(hist[k, :g[k]].sum()) for k in range(K1))
+    assert F.tolist() == g.tolist()
+    assert F.sum() == Bf and np.all(np.diff(F) <= 0)
