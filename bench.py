@@ -4,8 +4,11 @@ MI355X: rounds per second and achieved HBM bandwidth of the vocabulary pass.
 
 One step is one whole round over one batch: softmax statistics of both models,
 top-F speculation cache with geometric fan-out, Saguaro reweighting, lossless
-verification, residual bonus sampling and cache lookup (one ssd_round call: two
-streaming HIP kernels, each followed by a small one).  Inputs (seeded synthetic
+verification, residual bonus sampling, cache lookup and the next draft gathered
+from a synthetic value store (one ssd_round call: two streaming HIP kernels, each
+followed by a small one).  Outside the timed rounds it also measures the coverage
+statistics pass (bonus rank within the draft row) and reports the fan-out the
+optimiser picks from them.  Inputs (seeded synthetic
 logits, draft tokens from the library's own Saguaro sampler) are resident in HBM
 before timing; the timed loop rotates over distinct logit buffers totalling more
 than the 256 MB last-level cache so that rows come from HBM.
@@ -145,13 +148,34 @@ def main():
     rounds_per_s = 1000.0 / ms_per_step
 
     # ---- algorithmic bytes of the same rounds (deterministic replay, untimed)
+    # with the coverage histogram of the same rounds (bonus rank within draft row k)
+    RB = 64
+    hist = torch.zeros((K1, RB + 1), dtype=torch.int32, device=dev)
+    rank = torch.zeros(B, dtype=torch.int32, device=dev)
     ks, hits = [], []
     for i in range(min(n, 64)):
         step(args.warmup + i)
+        zq_i = bufs[(args.warmup + i) % nbuf][1]
+        ssd.ssd_bonus_rank(shape, zq_i, outb["accept_len"], outb["bonus"], RB, rank, hist, ws=ws)
         ks.append(outb["accept_len"].cpu().numpy().copy())
         hits.append(outb["hit"].cpu().numpy().copy())
     ks = np.stack(ks)
     hits = np.stack(hits)
+    h_np = hist.cpu().numpy()
+    covered = sum(int(h_np[k, :F[k]].sum()) for k in range(K1))
+    F_opt, hits_opt, total = ssd.ssd_fanout_optimize(K, w.Bf, RB, h_np)
+
+    # the coverage pass alone: one draft row per sequence (B V s bytes per call)
+    nr = 200
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for i in range(nr):
+        ssd.ssd_bonus_rank(shape, bufs[i % nbuf][1], outb["accept_len"], outb["bonus"], RB, rank, hist, ws=ws)
+    r1.record()
+    torch.cuda.synchronize()
+    rank_us = r0.elapsed_time(r1) * 1e3 / nr
+    rank_bytes = B * V * esize
     rows2 = np.where(ks < K, 2, 1).sum(axis=1).mean() if T > 0 else 0.0
     pass2_bytes = rows2 * V * esize
     round_bytes = pass1_bytes + pass2_bytes
@@ -212,6 +236,11 @@ def main():
             "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
             "mean_accept_len": round(float(ks.mean()), 3),
             "hit_rate": round(float(hits.mean()), 4),
+            "hit_rate_from_rank_hist": round(covered / max(total, 1), 4),
+            "fanout_optimized": F_opt,
+            "predicted_hit_rate_optimized": round(hits_opt / max(total, 1), 4),
+            "bonus_rank_us": round(rank_us, 2),
+            "bonus_rank_GBps": round(rank_bytes / (rank_us * 1e-6) / 1e9, 1),
             "wall_s": round(wall, 3),
         },
         "roofline": {

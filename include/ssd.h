@@ -234,6 +234,73 @@ ssd_status ssd_round(const ssd_shape* shape, const void* p_logits, const void* q
                      int32_t fallback, const ssd_round_out* out, const ssd_round_events* events,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Choosing the fan-out from measured coverage.  [zh] section 2 Challenge 1 and [nl]
+ * section 3 A say the fan-out solves a constrained optimisation over acceptance
+ * lengths, favouring short, likely lengths; they print no objective.  Reading used
+ * here: maximise the number of verified rounds whose bonus token the cache would
+ * have held.  A bonus t verified at acceptance length k is held by the cache when
+ * F_k exceeds its rank in the draft row k (cache order: larger logit first, ties to
+ * the lower id), so the statistics are a histogram over (k, rank).
+ *
+ * ssd_bonus_rank -- per sequence, the rank of bonus[b] within draft row
+ * k = accept_len[b]:  rank = #{x : z_q(x) > z_q(t)} + #{x < t : z_q(x) = z_q(t)}
+ * (logits compared as fp32, -0 equal to +0).  rank_out [B] (nullable) receives it,
+ * -1 when k lies outside [0, K] or t outside [0, V).  rank_hist (nullable,
+ * [(K+1), R+1] uint32, accumulated: the caller zeroes it once and may add many
+ * rounds) counts valid sequences per (k, min(rank, R)); bin R holds ranks >= R.
+ * 1 <= R <= SSD_MAX_F; at least one output.  shape.T is not used (the order does
+ * not depend on the temperature).  ws as for the other calls.  Calls that overlap
+ * in time may share rank_hist (the merge is atomic). */
+ssd_status ssd_bonus_rank(const ssd_shape* shape, const void* q_logits, const int32_t* accept_len,
+                          const int32_t* bonus, int32_t R, int32_t* rank_out, uint32_t* rank_hist, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ssd_fanout_optimize -- host only.  From rank_hist_host [(K+1), R+1] (as
+ * ssd_bonus_rank accumulates it), the fan-out F_host [K+1] that maximises the
+ * predicted hits  H(F) = sum_k sum_{j < F_k} hist[k][j]  over integers
+ * 0 <= F_k <= min(Fmax, R) with sum F = Bf.  Among maximisers, the lexicographically
+ * largest F (most candidates at the shortest lengths).  Exact (integer dynamic
+ * programme).  hits_host / total_host (nullable) receive H(F) and the count of all
+ * sequences in the histogram, so H / total is the predicted hit rate.
+ * SSD_ERR_ARG when Bf > (K+1) min(Fmax, R) or an argument is out of range
+ * (1 <= K <= SSD_MAX_K, 1 <= R <= SSD_MAX_F, 0 <= Fmax <= SSD_MAX_F, Bf >= 0). */
+ssd_status ssd_fanout_optimize(int32_t K, int32_t Bf, int32_t Fmax, int32_t R, const uint32_t* rank_hist_host,
+                               int32_t* F_host, uint64_t* hits_host, uint64_t* total_host);
+
+/* ---------------------------------------------------------------------------
+ * Fallback policy by batch size ([zh] section 2 Challenge 3; [nl] section 3 C):
+ * on a miss the whole batch waits for the fallback speculator; small batches use
+ * the slow, accurate primary speculator, large ones a fast, weak one (random
+ * tokens, SSD_FALLBACK_UNIFORM), with a critical batch size b* between them.  The
+ * pages print no formula.  Reading used here, with every input measured by the
+ * caller:
+ *   P(any miss) = 1 - prod_b h_b                 (h_b: hit probability of sequence b)
+ *   time(f)     = t_verify + P(any miss) * t_f
+ *   tokens(f)   = sum_b [ h_b n_hit + (1 - h_b) n_f ]
+ *   f*          = argmax_f tokens(f) / time(f),   ties to the primary speculator. */
+typedef struct {
+    double t_verify;   /* time of one verification round (any unit, > 0) */
+    double t_primary;  /* wait added when a miss falls back to the primary speculator (>= 0) */
+    double t_random;   /* wait added when a miss falls back to random tokens (>= 0) */
+    double n_hit;      /* expected tokens a sequence gains in a round after a hit (>= 0) */
+    double n_primary;  /* ... after a miss served by the primary speculator (>= 0) */
+    double n_random;   /* ... after a miss served by random tokens (>= 0) */
+} ssd_fallback_model;
+
+/* ssd_fallback_choose -- host only.  h_host [B] in [0, 1].  choice_host receives
+ * SSD_FALLBACK_NONE (the caller's primary speculator) or SSD_FALLBACK_UNIFORM, the
+ * value ssd_round and ssd_cache_lookup take; tput_primary / tput_random (nullable)
+ * receive tokens / time of each. */
+ssd_status ssd_fallback_choose(const ssd_fallback_model* model, int32_t B, const double* h_host,
+                               int32_t* choice_host, double* tput_primary, double* tput_random);
+
+/* ssd_fallback_critical_batch -- host only.  For a common hit probability h in
+ * [0, 1], the smallest batch size b in [1, b_max] at which random tokens give a
+ * strictly higher throughput than the primary speculator; 0 if there is none. */
+ssd_status ssd_fallback_critical_batch(const ssd_fallback_model* model, double h, int32_t b_max,
+                                       int32_t* b_star_host);
+
 const char* ssd_status_string(ssd_status s);
 
 /* Text of the last HIP error seen by this thread (empty if none). */

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_HERE, "liblrs_ssd.so")
 SSD_OK, SSD_ERR_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_HIP, SSD_ERR_WORKSPACE = 0, 1, 2, 3, 4
 SSD_F32, SSD_BF16 = 0, 1
 SSD_FALLBACK_NONE, SSD_FALLBACK_UNIFORM = 0, 1
-SSD_DEVERR_TOKEN_RANGE, SSD_DEVERR_QPRIME_ZERO, SSD_DEVERR_LEN_RANGE = 1, 2, 4
+SSD_DEVERR_TOKEN_RANGE, SSD_DEVERR_QPRIME_ZERO, SSD_DEVERR_LEN_RANGE, SSD_DEVERR_SLOT_RANGE = 1, 2, 4, 8
 SSD_MAX_K, SSD_MAX_F = 16, 64
 
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
             "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_round",
+            "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
             "ssd_status_string", "ssd_last_error")
 
 
@@ -52,6 +53,11 @@ class ssd_round_out(ctypes.Structure):
                                   "slot", "fallback_tokens", "dev_err", "cache_values", "next_draft")]
 
 
+class ssd_fallback_model(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("t_verify", "t_primary", "t_random", "n_hit", "n_primary",
+                                               "n_random")]
+
+
 class ssd_round_events(ctypes.Structure):
     _fields_ = [("pass1_start", _P), ("pass1_stop", _P), ("pass2_start", _P), ("pass2_stop", _P)]
 
@@ -76,12 +82,18 @@ def _load():
     L.ssd_cache_lookup.argtypes = [i32, i32, i32, _P, i32, _P, _P, _P, i32, ssd_rng, _P, _P, _P, _P, _P]
     L.ssd_round.argtypes = [S, _P, _P, _P, _P, i32, f32, ssd_rng, i32, ctypes.POINTER(ssd_round_out),
                             ctypes.POINTER(ssd_round_events), _P, sz, _P]
+    L.ssd_bonus_rank.argtypes = [S, _P, _P, _P, i32, _P, _P, _P, sz, _P]
+    L.ssd_fanout_optimize.argtypes = [i32, i32, i32, i32, _P, _P, _P, _P]
+    FM = ctypes.POINTER(ssd_fallback_model)
+    L.ssd_fallback_choose.argtypes = [FM, i32, _P, _P, _P, _P]
+    L.ssd_fallback_critical_batch.argtypes = [FM, f64, i32, _P]
     L.ssd_status_string.argtypes = [i32]
     L.ssd_status_string.restype = ctypes.c_char_p
     L.ssd_last_error.argtypes = []
     L.ssd_last_error.restype = ctypes.c_char_p
     for name in ("ssd_fanout", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight", "ssd_verify",
-                 "ssd_residual_sample", "ssd_cache_lookup", "ssd_round"):
+                 "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_round", "ssd_bonus_rank",
+                 "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
         getattr(L, name).restype = i32
     return L
 
@@ -273,6 +285,52 @@ def ssd_cache_gather(values, hit, slot, fallback_tokens, next_draft, dev_err=Non
                                  _ptr(slot, torch.int32, "slot"), _ptr(fallback_tokens, torch.int32, "fallback_tokens"),
                                  _ptr(next_draft, torch.int32, "next_draft"), _ptr(dev_err, torch.int32),
                                  _stream(stream)), "ssd_cache_gather")
+
+
+def ssd_bonus_rank(shape, q_logits, accept_len, bonus, R, rank_out=None, rank_hist=None, ws=None, stream=None):
+    """Rank of each bonus within draft row accept_len (rank_out [B] int32) and the
+    coverage histogram rank_hist [K+1, R+1] (int32 tensor holding uint32 counts,
+    accumulated)."""
+    _check(_lib.ssd_bonus_rank(ctypes.byref(shape), _logit_ptr(q_logits, "q_logits"),
+                               _ptr(accept_len, torch.int32, "accept_len"), _ptr(bonus, torch.int32, "bonus"),
+                               int(R), _ptr(rank_out, torch.int32, "rank_out"),
+                               _ptr(rank_hist, torch.int32, "rank_hist"), *_ws(ws, shape, 1), _stream(stream)),
+           "ssd_bonus_rank")
+
+
+def ssd_fanout_optimize(K: int, Bf: int, Fmax: int, hist):
+    """Host: the fan-out [K+1] maximising the hits predicted by hist [K+1, R+1]
+    (any integer array-like); returns (F, hits, total)."""
+    import numpy as np
+    h = np.ascontiguousarray(np.asarray(hist), dtype=np.uint32)
+    if h.ndim != 2 or h.shape[0] != K + 1:
+        raise ValueError("hist must be [K+1, R+1]")
+    F = (ctypes.c_int32 * (K + 1))()
+    hits, total = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(_lib.ssd_fanout_optimize(int(K), int(Bf), int(Fmax), h.shape[1] - 1, h.ctypes.data_as(_P), F,
+                                    ctypes.byref(hits), ctypes.byref(total)), "ssd_fanout_optimize")
+    return list(F), int(hits.value), int(total.value)
+
+
+def ssd_fallback_choose(model: "ssd_fallback_model", h):
+    """Host: SSD_FALLBACK_NONE or SSD_FALLBACK_UNIFORM for hit probabilities h [B];
+    returns (choice, tokens/time with the primary speculator, with random tokens)."""
+    import numpy as np
+    hv = np.ascontiguousarray(np.asarray(h, dtype=np.float64).reshape(-1))
+    choice = ctypes.c_int32()
+    tp, tr = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.ssd_fallback_choose(ctypes.byref(model), hv.size, hv.ctypes.data_as(_P), ctypes.byref(choice),
+                                    ctypes.byref(tp), ctypes.byref(tr)), "ssd_fallback_choose")
+    return int(choice.value), tp.value, tr.value
+
+
+def ssd_fallback_critical_batch(model: "ssd_fallback_model", h: float, b_max: int) -> int:
+    """Host: the smallest batch size at which random tokens beat the primary
+    speculator (0: none up to b_max)."""
+    b = ctypes.c_int32()
+    _check(_lib.ssd_fallback_critical_batch(ctypes.byref(model), float(h), int(b_max), ctypes.byref(b)),
+           "ssd_fallback_critical_batch")
+    return int(b.value)
 
 
 _ROUND_DTYPES = {"p_max": torch.float32, "p_sum": torch.float64, "p_argmax": torch.int32, "q_max": torch.float32,

@@ -414,6 +414,33 @@ ssd_status ssd_cache_lookup(int32_t B, int32_t K, int32_t V, const int32_t* F_ho
     return SSD_OK;
 }
 
+ssd_status ssd_bonus_rank(const ssd_shape* s, const void* q_logits, const int32_t* accept_len,
+                          const int32_t* bonus, int32_t R, int32_t* rank_out, uint32_t* rank_hist, void* ws,
+                          size_t ws_bytes, void* stream) {
+    ssd_status st = check_shape(s);
+    if (st != SSD_OK) return st;
+    if (!q_logits || !accept_len || !bonus || (!rank_out && !rank_hist) || R < 1 || R > SSD_MAX_F)
+        return SSD_ERR_ARG;
+    Layout L;
+    if ((st = check_ws(s, 1, ws, ws_bytes, &L)) != SSD_OK) return st;
+    ssd::RankArgs a{};
+    a.q_logits = static_cast<const char*>(q_logits);
+    a.B = s->B;
+    a.K = s->K;
+    a.V = s->V;
+    a.ld_bytes = ld_bytes(s);
+    a.nt = L.nt;
+    a.accept_len = accept_len;
+    a.bonus = bonus;
+    a.counts = at<uint32_t>(ws, L.part);  // B nt words: far below the pass-1 partials region
+    a.R = R;
+    a.rank_out = rank_out;
+    a.hist = rank_hist;
+    hipError_t e = ssd::launch_rank(s->dtype, vec_ok(s, q_logits), a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "ssd_bonus_rank");
+    return SSD_OK;
+}
+
 ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* values, const uint8_t* hit,
                             const int32_t* slot, const int32_t* fallback_tokens, int32_t* next_draft,
                             int32_t* dev_err, void* stream) {

@@ -221,6 +221,9 @@ __device__ __forceinline__ int wave_min_i32(int v) {
     return (int)wave_reduce_u32((uint32_t)v, 0x7FFFFFFFu,
                                 [](uint32_t x, uint32_t y) { return (int)x < (int)y ? x : y; });
 }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    return wave_reduce_u32(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+}
 __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
     return wave_reduce_u32(v, 0u, [](uint32_t x, uint32_t y) { return x | y; });
 }

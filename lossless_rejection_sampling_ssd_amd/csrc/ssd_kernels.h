@@ -148,6 +148,22 @@ hipError_t launch_greedy_pick(const int32_t* arg, int B, int K, const int32_t* a
                               double* mass, int32_t* dev_err, hipStream_t st);
 hipError_t launch_gather(int B, int K, int Bf, const int32_t* values, const uint8_t* hit, const int32_t* slot,
                          const int32_t* fallback_tokens, int32_t* next_draft, int32_t* dev_err, hipStream_t st);
+// Rank of the bonus token within the draft row of its acceptance length, and the
+// coverage histogram over (length, rank).
+struct RankArgs {
+    const char* q_logits;
+    int B, K, V;
+    int64_t ld_bytes;
+    int nt;                     // pass-1 tiles per row
+    const int32_t* accept_len;  // [B]
+    const int32_t* bonus;       // [B]
+    uint32_t* counts;           // workspace [B][nt]: per-tile count of ids ranked above the bonus
+    int R;                      // histogram bins per length: ranks 0..R-1, bin R = rank >= R
+    int32_t* rank_out;          // nullable [B]
+    uint32_t* hist;             // nullable [(K+1)][R+1], accumulated
+};
+hipError_t launch_rank(int dtype, bool vec, const RankArgs& a, hipStream_t st);
+
 hipError_t launch_lookup(int B, int K, int V, const int* F, const int* O, int Bf, const int32_t* cache_ids,
                          const int32_t* accept_len, const int32_t* bonus, int fallback, uint64_t seed,
                          uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* dev_err,

@@ -27,6 +27,7 @@
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -1370,6 +1371,79 @@ __global__ void gather_kernel(int B, int K, int Bf, const int32_t* values, const
     next_draft[x] = t;
 }
 
+// ============================================================================ coverage statistics
+// Rank of the bonus t within draft row k (k the acceptance length) in the cache
+// order, larger logit first and ties to the lower id: the ids x with z(x) > z(t),
+// plus those x < t with z(x) = z(t).  One wave per (sequence, tile) counts its tile;
+// the comparison is on fp32 values (-0 equals +0, as in the order of the cache keys).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void rank_tile_kernel(const RankArgs a) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int b = blockIdx.x / nblk;
+    const int t = (blockIdx.x % nblk) * kWavesPerBlock + wave;
+    if (t >= a.nt) return;
+    const int k = uniform(a.accept_len[b]), tok = uniform(a.bonus[b]);
+    uint32_t cnt = 0;
+    if (k >= 0 && k <= a.K && tok >= 0 && tok < a.V) {
+        const char* row = a.q_logits + ((int64_t)b * (a.K + 1) + k) * a.ld_bytes;
+        const int64_t t0 = (int64_t)t * kTile<DT>;
+        u32x4 raw[kVecPerLane];
+        load_tile<DT, VEC, kVecPerLane>(row, t0, a.V, lane, raw);
+        const float zt = load_one<DT>(row, tok);
+        if (t0 + kTile<DT> <= tok || t0 > tok) {
+            // the whole tile lies on one side of t: one comparison for all of it
+            const bool below = t0 < tok;
+#pragma unroll
+            for (int j = 0; j < kVecPerLane; ++j) {
+                float x[N];
+                unpack_vec<DT>(raw[j], x);
+#pragma unroll
+                for (int e = 0; e < N; ++e) cnt += below ? (x[e] >= zt) : (x[e] > zt);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kVecPerLane; ++j) {
+                float x[N];
+                unpack_vec<DT>(raw[j], x);
+                const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+#pragma unroll
+                for (int e = 0; e < N; ++e) cnt += (e0 + e < tok) ? (x[e] >= zt) : (x[e] > zt);
+            }
+        }
+    }
+    cnt = wave_sum_u32(cnt);
+    if (lane == 0) a.counts[(int64_t)b * a.nt + t] = cnt;
+}
+
+// Sum of the tile counts per sequence (one wave per sequence, strided over the
+// grid), histogram in LDS per block, merged into the global histogram with one
+// vector atomic add per non-empty bin.
+constexpr int kRankWaves = 16;
+__global__ __launch_bounds__(kRankWaves * kWave) void rank_finish_kernel(const RankArgs a) {
+    __shared__ uint32_t h[(kMaxK + 1) * (kMaxF + 1)];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nbins = (a.K + 1) * (a.R + 1);
+    for (int i = threadIdx.x; i < nbins; i += blockDim.x) h[i] = 0u;
+    __syncthreads();
+    for (int b = blockIdx.x * kRankWaves + wave; b < a.B; b += gridDim.x * kRankWaves) {
+        uint32_t c = 0;
+        for (int t = lane; t < a.nt; t += kWave) c += a.counts[(int64_t)b * a.nt + t];
+        const uint32_t rank = wave_sum_u32(c);
+        const int k = a.accept_len[b], tok = a.bonus[b];
+        const bool valid = k >= 0 && k <= a.K && tok >= 0 && tok < a.V;
+        if (lane == 0) {
+            if (a.rank_out) a.rank_out[b] = valid ? (int32_t)rank : -1;
+            if (valid && a.hist) atomicAdd(&h[k * (a.R + 1) + (rank < (uint32_t)a.R ? (int)rank : a.R)], 1u);
+        }
+    }
+    __syncthreads();
+    if (a.hist)
+        for (int i = threadIdx.x; i < nbins; i += blockDim.x)
+            if (h[i]) atomicAdd(&a.hist[i], h[i]);
+}
+
 // ============================================================================ launchers
 static FO make_fo(const int* F, const int* O, int K1) {
     FO fo;
@@ -1497,6 +1571,19 @@ hipError_t launch_gather(int B, int K, int Bf, const int32_t* values, const uint
     const int64_t n = (int64_t)B * K;
     gather_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(B, K, Bf, values, hit, slot, fallback_tokens,
                                                                next_draft, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_rank(int dtype, bool vec, const RankArgs& a, hipStream_t st) {
+    const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t grid = (int64_t)a.B * nblk;
+    if (grid <= 0 || grid > INT_MAX || a.R < 1 || a.R > kMaxF || a.K > kMaxK) return hipErrorInvalidValue;
+    hipError_t e = by_type(dtype, vec, [&](auto DT, auto VEC) {
+        rank_tile_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
+    });
+    if (e != hipSuccess) return e;
+    const int g2 = (int)std::min<int64_t>(((int64_t)a.B + kRankWaves - 1) / kRankWaves, 256);
+    rank_finish_kernel<<<g2, kRankWaves * kWave, 0, st>>>(a);
     return hipGetLastError();
 }
 

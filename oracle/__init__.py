@@ -28,6 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
 F32, BF16 = 0, 1
 PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
 ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE, ERR_SLOT_RANGE = 1, 2, 4, 8
+FALLBACK_NONE, FALLBACK_UNIFORM = 0, 1  # the primary speculator / uniform random tokens
 E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
 FANOUT_EPS = 1e-9
 # Half-width of the inverse-CDF near-tie band (E2) on the normalised CDF.
@@ -331,6 +332,45 @@ def fanout_optimize(hist, Bf: int, Fmax: int):
                 b -= f
                 break
     return F, int(best[0][Bf]), int(hist.sum())
+
+
+def fallback_throughputs(model, h):
+    """Expected tokens per unit time of each fallback speculator for one round of a
+    batch with hit probabilities h [B] ([zh] section 2 Challenge 3 and [nl] section
+    3 C: on a miss the whole batch waits for the fallback; slow and accurate for
+    small batches, fast and weak for large ones; the formula is a reading):
+        P(any miss) = 1 - prod_b h_b
+        time(f)     = t_verify + P(any miss) * t_f
+        tokens(f)   = sum_b [h_b n_hit + (1 - h_b) n_f]
+    model: mapping with t_verify, t_primary, t_random, n_hit, n_primary, n_random.
+    Returns (primary, random)."""
+    all_hit, hit_sum = 1.0, 0.0
+    for hb in h:
+        all_hit *= float(hb)
+        hit_sum += float(hb)
+    p_miss = 1.0 - all_hit
+    miss_sum = len(h) - hit_sum
+    out = []
+    for t_f, n_f in ((model["t_primary"], model["n_primary"]), (model["t_random"], model["n_random"])):
+        tokens = hit_sum * model["n_hit"] + miss_sum * n_f
+        out.append(tokens / (model["t_verify"] + p_miss * t_f))
+    return out[0], out[1]
+
+
+def fallback_choose(model, h):
+    """FALLBACK_UNIFORM (random tokens) when its throughput is strictly higher, else
+    FALLBACK_NONE (the primary speculator)."""
+    tp, tr = fallback_throughputs(model, h)
+    return (FALLBACK_UNIFORM if tr > tp else FALLBACK_NONE), tp, tr
+
+
+def fallback_critical_batch(model, h: float, b_max: int) -> int:
+    """The smallest batch size b <= b_max whose batch of b sequences with hit
+    probability h prefers random tokens; 0 if none (b*, read from [nl] section 3 C)."""
+    for b in range(1, b_max + 1):
+        if fallback_choose(model, [h] * b)[0] == FALLBACK_UNIFORM:
+            return b
+    return 0
 
 
 @dataclass

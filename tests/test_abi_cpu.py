@@ -155,6 +155,12 @@ def test_cache_and_round_validation(ssd):
                                (2, 4, 3, None, BAD), (2, 4, 3, BAD, None)):
         assert L.ssd_cache_gather(B, K, Bf, vals, BAD, BAD, BAD, nd, None, None) == ssd.SSD_ERR_ARG
     assert L.ssd_cache_gather(1 << 28, 16, 3, BAD, BAD, BAD, BAD, BAD, None, None) == ssd.SSD_ERR_UNSUPPORTED
+    # bonus rank: missing inputs, no output, R out of range, small workspace
+    for q, acc, bon, R, ro, rh in ((None, BAD, BAD, 8, BAD, BAD), (BAD, None, BAD, 8, BAD, BAD),
+                                   (BAD, BAD, None, 8, BAD, BAD), (BAD, BAD, BAD, 8, None, None),
+                                   (BAD, BAD, BAD, 0, BAD, BAD), (BAD, BAD, BAD, 65, BAD, BAD)):
+        assert L.ssd_bonus_rank(ctypes.byref(s), q, acc, bon, R, ro, rh, ws, 1 << 30, None) == ssd.SSD_ERR_ARG
+    assert L.ssd_bonus_rank(ctypes.byref(s), BAD, BAD, BAD, 8, BAD, None, ws, 8, None) == ssd.SSD_ERR_WORKSPACE
 
 
 def test_binding_refuses_host_tensors(ssd):

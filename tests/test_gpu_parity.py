@@ -300,6 +300,54 @@ def test_cache_gather_oracle_fed():
         assert B < 100 or oerr.any()
 
 
+RANK_CASES = [
+    # (dtype, B, K, V, ld pad, R)
+    ("f32", 7, 3, 5000, 0, 16),
+    ("bf16", 9, 4, 40013, 5, 64),
+    ("bf16", 64, 8, 128256, 0, 64),
+    ("f32", 3, 1, 2, 0, 1),
+    ("bf16", 5, 16, 4097, 3, 7),
+]
+
+
+@pytest.mark.parametrize("case", RANK_CASES, ids=lambda c: "%s-B%d-K%d-V%d-pad%d-R%d" % c)
+def test_bonus_rank_oracle_fed(case):
+    """ssd_bonus_rank against the oracle: heavy ties (coarse logits), -inf entries,
+    ragged tails, unaligned rows, invalid (k, bonus); the histogram accumulates over
+    two calls."""
+    dtype, B, K, V, pad, R = case
+    _case("bonus rank %s" % (case,))
+    rng = np.random.default_rng(B * 7 + V)
+    z = np.round(rng.standard_normal((B, K + 1, V + pad)) * 4.0) / 4.0
+    z[rng.random(z.shape) < 0.03] = -np.inf
+    z = z.astype(np.float32)
+    zt = torch.from_numpy(z)
+    if dtype == "bf16":
+        zt = zt.to(torch.bfloat16)
+    zt = zt[:, :, :V]
+    z_np = to_oracle_array(zt)
+    zd = zt.cuda() if pad == 0 else torch.empty((B, K + 1, V + pad), dtype=zt.dtype, device="cuda")[:, :, :V]
+    if pad:
+        zd.copy_(zt)
+    shape = ssd.shape_of(zd, 1.0)
+    hist = torch.zeros((K + 1, R + 1), dtype=torch.int32, device="cuda")
+    ohist = np.zeros((K + 1, R + 1), np.uint32)
+    for rep in range(2):
+        acc = rng.integers(-1, K + 2, B).astype(np.int32)
+        bon = rng.integers(-2, V + 2, B).astype(np.int32)
+        top = np.argmax(z[:, :, :V], axis=2)  # some bonuses at the top of their row
+        for b in range(0, B, 3):
+            if 0 <= acc[b] <= K:
+                bon[b] = top[b, acc[b]]
+        rank = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+        ssd.ssd_bonus_rank(shape, zd, torch.as_tensor(acc, device="cuda"), torch.as_tensor(bon, device="cuda"), R,
+                           rank, hist)
+        torch.cuda.synchronize()
+        orank, ohist = oracle.bonus_rank(z_np, acc, bon, R, hist=ohist)
+        assert np.array_equal(rank.cpu().numpy(), orank), (case, rep)
+        assert np.array_equal(hist.cpu().numpy().astype(np.uint32), ohist), (case, rep)
+
+
 def test_residual_bad_len_and_greedy():
     """ssd_residual_sample with accepted lengths outside [0, K] reports the error and
     returns -1; at T = 0 it returns argmax p_k."""
@@ -399,3 +447,16 @@ def test_full_size_sampled(name, C, sig):
     nd, _ = oracle.cache_gather(values, g["hit"], g["slot"], g["fallback_tokens"])
     assert np.array_equal(g["next_draft"], nd)
     assert np.all(g["dev_err"] == 0)
+    # coverage statistics of this round: the bonus ranks below F_k exactly on a hit
+    _case("full-size %s: bonus rank" % name)
+    rank = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    hist = torch.zeros((w.K + 1, 65), dtype=torch.int32, device="cuda")
+    acc_d = torch.as_tensor(g["accept_len"], device="cuda")
+    ssd.ssd_bonus_rank(ssd.shape_of(zq, T), zq, acc_d, torch.as_tensor(g["bonus"], device="cuda"), 64, rank, hist)
+    torch.cuda.synchronize()
+    rk = rank.cpu().numpy()
+    assert np.array_equal(rk < F[g["accept_len"]], g["hit"] == 1)
+    assert int(hist.sum()) == w.B
+    for b in sample:
+        orank, _ = oracle.bonus_rank(per[int(b)][1], g["accept_len"][b:b + 1], g["bonus"][b:b + 1], 64)
+        assert rk[b] == orank[0], (name, b)

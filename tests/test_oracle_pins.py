@@ -493,3 +493,43 @@ def test_fanout_optimize_special_cases(orc):
     assert hits == sum(int(hist[k, :g[k]].sum()) for k in range(K1))
     assert F.tolist() == g.tolist()
     assert F.sum() == Bf and np.all(np.diff(F) <= 0)
+
+
+# --------------------------------------------------------------------------- fallback policy
+def _model(**kw):
+    m = dict(t_verify=1.0, t_primary=0.8, t_random=0.05, n_hit=3.0, n_primary=3.0, n_random=1.2)
+    m.update(kw)
+    return m
+
+
+def test_fallback_no_miss_is_a_tie(orc):
+    """h = 1 for every sequence: no round waits and both fallbacks deliver n_hit per
+    sequence, so the throughputs are equal (B n_hit / t_verify) and the tie keeps
+    the primary speculator."""
+    m = _model()
+    c, tp, tr = orc.fallback_choose(m, [1.0] * 17)
+    assert c == orc.FALLBACK_NONE and tp == tr == 17 * 3.0 / 1.0
+
+
+def test_fallback_closed_form_values(orc):
+    """Throughputs written out by hand for B = 2, h = (0.5, 0.75)."""
+    m = _model(t_verify=2.0, t_primary=1.0, t_random=0.25, n_hit=4.0, n_primary=3.0, n_random=1.0)
+    c, tp, tr = orc.fallback_choose(m, [0.5, 0.75])
+    p_miss = 1 - 0.375
+    assert tp == pytest.approx((1.25 * 4 + 0.75 * 3) / (2 + p_miss * 1.0), rel=1e-15)
+    assert tr == pytest.approx((1.25 * 4 + 0.75 * 1) / (2 + p_miss * 0.25), rel=1e-15)
+    assert c == (orc.FALLBACK_UNIFORM if tr > tp else orc.FALLBACK_NONE)
+
+
+def test_fallback_critical_batch_closed_form(orc):
+    """With n_primary = n_hit = n, n_random = 0 and t_random = 0, random tokens win
+    exactly when h^b < 1 - t_verify (1 - h) / (h t_primary), so
+    b* = floor(ln(1 - t_verify (1 - h) / (h t_primary)) / ln h) + 1."""
+    import math
+    for h, tv, tpri in ((0.9, 1.0, 3.0), (0.97, 0.5, 4.0), (0.8, 1.0, 10.0), (0.995, 1.0, 2.5)):
+        m = _model(t_verify=tv, t_primary=tpri, t_random=0.0, n_hit=2.0, n_primary=2.0, n_random=0.0)
+        x = math.log(1 - tv * (1 - h) / (h * tpri)) / math.log(h)
+        assert abs(x - round(x)) > 1e-6  # away from a boundary
+        assert orc.fallback_critical_batch(m, h, 5000) == math.floor(x) + 1
+    # a primary fallback that costs nothing is never beaten
+    assert orc.fallback_critical_batch(_model(t_primary=0.0), 0.9, 500) == 0
