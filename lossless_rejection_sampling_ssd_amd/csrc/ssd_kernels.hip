@@ -882,11 +882,20 @@ __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f)
 // ============================================================================ pass 2
 enum { kWResid = 0, kWP = 1, kWQprime = 2 };
 
+// The weights are kept in the units of the target row's terms tp = term(z_p, c, op)
+// (p(x) = tp * inv_p), so that no per-element scaling is needed: with tq = term(z_q,
+// c, oq) and q'(x) = tq * sc_q * (C if cached else 1),
+//   residual  max(p - q', 0) = inv_p * max(tp - tq * rho_sel, 0),  rho = sc_q / inv_p;
+//   target    p              = inv_p * tp;
+//   draft q'  (its own units)  tq * (C if cached else 1).
+// The inverse CDF is invariant to the common factor; only the reported residual mass
+// is scaled back by inv_p.
 struct WParams {
     float c;
-    float op, oq;       // offsets of the target / draft rows
-    double inv_p;       // p(x) = term(z_p, c, op) * inv_p
-    double sc_q, sc_qC; // q'(x) = term(z_q, c, oq) * (sc_qC if cached else sc_q)
+    float op, oq;        // offsets of the target / draft rows
+    double inv_p;        // p(x) = tp * inv_p
+    double rho, rhoC;    // draft-to-target unit ratio, off / on the cached ids
+    double Cd;           // C as double (tq * C is exact in fp64)
 };
 
 // Row statistics of one (b, position), loaded together with no branch in between so
@@ -913,28 +922,31 @@ __device__ __forceinline__ WParams make_wparams(float c, float C, bool with_p, c
     w.c = c;
     w.op = 0.f;
     w.inv_p = 0.0;
+    w.rho = w.rhoC = 0.0;
+    w.Cd = (double)C;
+    const RowNorm nq = row_norm(L.qm, L.qs, c);
+    w.oq = nq.o;
     if (with_p) {
         const RowNorm np = row_norm(L.pm, L.ps, c);
         w.op = np.o;
         w.inv_p = np.inv;
+        w.rho = nq.inv / L.Z / np.inv;
+        w.rhoC = w.rho * w.Cd;
     }
-    const RowNorm nq = row_norm(L.qm, L.qs, c);
-    w.oq = nq.o;
-    w.sc_q = nq.inv / L.Z;
-    w.sc_qC = w.sc_q * (double)C;
     return w;
 }
 
-// Weight of one element for the inverse-CDF scan (fp64); *pw receives p(x).
+// Weight of one element for the inverse-CDF scan (fp64, in the units above); *pw
+// receives tp.  A -inf logit (also the padding past V) has term 0 and weight 0.
 template <int MODE>
 __device__ __forceinline__ double elem_weight_t(const WParams& w, float zp, float zq, bool in_cache, double* pw) {
-    double p = 0.0;
-    if (MODE != kWQprime) p = (double)term(zp, w.c, w.op) * w.inv_p;
-    *pw = p;
-    if (MODE == kWP) return p;
-    const double q = (double)term(zq, w.c, w.oq) * (in_cache ? w.sc_qC : w.sc_q);
-    if (MODE == kWQprime) return q;
-    const double d = p - q;
+    double tp = 0.0;
+    if (MODE != kWQprime) tp = (double)term(zp, w.c, w.op);
+    *pw = tp;
+    if (MODE == kWP) return tp;
+    const double tq = (double)term(zq, w.c, w.oq);
+    if (MODE == kWQprime) return in_cache ? tq * w.Cd : tq;
+    const double d = __builtin_fma(-tq, in_cache ? w.rhoC : w.rho, tp);
     return d > 0.0 ? d : 0.0;
 }
 
@@ -951,7 +963,7 @@ __device__ inline void tile_bitmap(uint32_t* bits, int64_t t0, int my_id) {
 }
 
 // Weights of one lane's vector j of a tile from the raw vectors of the target and
-// draft rows; elements past V weigh 0.
+// draft rows.  The tile loads hold -inf past V, so those elements weigh 0.
 template <int DT, int MODE>
 __device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 rq, int64_t e0, int V,
                                             const uint32_t* bits, int64_t t0, double* w, double* p) {
@@ -965,10 +977,6 @@ __device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 r
     for (int e = 0; e < N; ++e) {
         w[e] = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f, (cbits >> e) & 1u,
                                    &p[e]);
-        if (e0 + e >= V) {
-            w[e] = 0.0;
-            p[e] = 0.0;
-        }
     }
 }
 
@@ -1098,7 +1106,6 @@ __device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int
             mode = kWP;
             Z = tot_p;
         }
-        Zused = Z;
         const double thr = u * Z;
         int gsel = -1, glast = -1;
         double gbase = 0.0, lastbase = 0.0, carry = 0.0;
@@ -1139,6 +1146,7 @@ __device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int
         const LawIn L = load_law(a, r);
         my_id = cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O);
         const WParams wp = make_wparams(a.c, a.C, mode != kWQprime, L);
+        Zused = Z * wp.inv_p;  // the residual (or target) mass in probability units
         if (mode == kWResid)
             tok = rescan_tile<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
         else if (mode == kWP)
