@@ -253,6 +253,9 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
     return __longlong_as_double((long long)(((uint64_t)lane_u32((uint32_t)(b >> 32), l) << 32) |
                                             lane_u32((uint32_t)b, l)));
 }
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+    return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | lane_u32((uint32_t)v, l);
+}
 // Sum over the wave in fp64 (fixed order).
 __device__ __forceinline__ double wave_sum_f64(double v) {
     v += dpp_f64_zero<kRowShr1>(v);

@@ -234,6 +234,7 @@ __device__ inline uint32_t wave_select_value(const uint64_t (&k)[KREG], int U, i
 // the j-th largest (0 past min(n, F)).
 __device__ inline uint64_t rank_sort_lds(TopfScratch& sc, int n, int F) {
     const int lane = lane_id();
+    n = uniform(n);
     uint64_t k[4];
     int rank[4];
 #pragma unroll
@@ -243,7 +244,8 @@ __device__ inline uint64_t rank_sort_lds(TopfScratch& sc, int n, int F) {
         rank[u] = 0;
     }
     if (n <= kWave) {
-        for (int v = 0; v < n; ++v) rank[0] += sc.surv[v] > k[0];
+        // one key per lane: the others are read from lanes, not from LDS
+        for (int v = 0; v < n; ++v) rank[0] += lane_u64(k[0], v) > k[0];
     } else {
         for (int v = 0; v < n; ++v) {
             const uint64_t x = sc.surv[v];
@@ -354,8 +356,15 @@ __device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, c
 // rank (a whole-key select first when more than kSurvivorCap keys tie there).
 template <int KREG>
 __device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, int F, TopfScratch& sc) {
-    // One histogram step usually leaves few enough keys (those in or above the bin of
-    // the F-th largest value) to rank them all; otherwise resolve the value exactly.
+    // At most one key per lane: rank them all.  Otherwise one histogram step usually
+    // leaves few enough keys (those in or above the bin of the F-th largest value) to
+    // rank them all; failing that, resolve the value exactly.
+    U = uniform(U);
+    int live = 0;
+#pragma unroll
+    for (int u = 0; u < KREG; ++u)
+        if (u < U) live += wave_popc(k[u] != 0ull);
+    if (live <= kWave) return rank_sort_lds(sc, compact_keys<KREG>(sc, k, U, 0ull), F);
     uint64_t lo = (uint64_t)wave_select_value<KREG>(k, U, F, sc.bins, true) << 32;
     int n = compact_keys<KREG>(sc, k, U, lo);
     if (n > kSurvivorCap) {
@@ -809,7 +818,10 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
         }
         stats_from_lanes(qq, f.c, mq, sq, aq);
         stats_from_lanes(pp, f.c, mp, sp, ap);
+        // Floor of the row's F-th largest value: the largest tile threshold, or the F-th
+        // largest tile maximum (F tiles hold an element at or above it) if higher.
         cs.tr = wave_max_u32(qq.tau);
+        if (F > 0 && F < nt) cs.tr = max(cs.tr, wave_select_u32(lane < nt ? ord32(qq.m) : 0u, F));
         cs.max_nc = (int)wave_max_u32((uint32_t)qq.ncand);
         if (lane < nt) sc.nc[lane] = (uint8_t)qq.ncand;
         wave_sync_lds();
