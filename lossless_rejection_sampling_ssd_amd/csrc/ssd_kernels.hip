@@ -38,6 +38,7 @@ enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange =
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
 constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
 constexpr int kStageCap = 160;     // LDS slots per wave for one tile's candidate keys (>= any cap)
+constexpr int kHotCap = 128;       // LDS slots per wave for the vectors that hold candidates
 
 int tile_elems(int dtype) { return dtype == 1 ? kTile<1> : kTile<0>; }
 int tiles_per_row(int dtype, int V) {
@@ -563,6 +564,8 @@ __device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     __shared__ uint64_t cand_stage[kWavesPerBlock][kStageCap + kWave];
+    __shared__ u32x4 hot_vec[kWavesPerBlock][kHotCap];
+    __shared__ int hot_id[kWavesPerBlock][kHotCap];
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -639,9 +642,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     opaque_regs(raw);
 
     // ---- candidate keys of this tile (draft rows of the cache): every element at or
-    // above the F-th largest lane maximum.  Only vectors whose maximum reaches the
-    // threshold in some lane are examined; keys are staged in LDS element position by
-    // element position and copied out with one coalesced store per 64 keys.
+    // above the F-th largest lane maximum.  Only the (lane, vector) pairs whose vector
+    // maximum reaches the threshold can hold one: they are few (about F), so they are
+    // compacted through LDS, one per lane, and examined there; the keys are staged in
+    // LDS and copied out with one coalesced store per 64 keys.
     const int F = a.F[i];
     uint32_t tau = 0u;
     int ncand = 0;
@@ -654,22 +658,69 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         uint64_t* out = a.cand + ((r * a.nt) + t) * a.cap;
         uint64_t* stage = cand_stage[wave];
         const int cap = a.cap;
-        const uint64_t below = (1ull << lane) - 1ull;
         int n = 0;
+        uint32_t hot = 0u;
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) {
-            if (__ballot(vmax[j] >= tauf) == 0ull) continue;
+        for (int j = 0; j < kVecPerLane; ++j) hot |= (vmax[j] >= tauf ? 1u : 0u) << j;
+        const uint32_t h = (uint32_t)__popc(hot);
+        const uint32_t hincl = wave_prefix_u32(h);
+        const int H = (int)lane_u32(hincl, kWave - 1);
+        if (H <= kHotCap) {
+            u32x4* hv = hot_vec[wave];
+            int* hid = hot_id[wave];
+            int q = (int)(hincl - h);
 #pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const float v = vec_elem<DT>(raw[j], e);
-                const int id = id0 + j * kWave * N + e;
-                const bool hit = v >= tauf && (full || id < V);
-                const uint64_t mk = __ballot(hit);
-                if (mk) {  // uniform; the store itself is unconditional (misses go to the
-                           // lane's discard slot)
-                    const int pos = n + __popcll(mk & below);
-                    stage[hit && pos < kStageCap ? pos : kStageCap + lane] = cand_key(v, (uint32_t)id);
-                    n += __popcll(mk);
+            for (int j = 0; j < kVecPerLane; ++j) {
+                if ((hot >> j) & 1u) {
+                    hv[q] = raw[j];
+                    hid[q] = id0 + j * kWave * N;
+                    ++q;
+                }
+            }
+            wave_sync_lds();
+            for (int q0 = 0; q0 < H; q0 += kWave) {
+                const int qq = q0 + lane;
+                const bool live = qq < H;
+                const u32x4 v = hv[live ? qq : 0];
+                const int e0 = hid[live ? qq : 0];
+                float x[N];
+                unpack_vec<DT>(v, x);
+                bool hit[N];
+                uint32_t cnt = 0u;
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    hit[e] = live && x[e] >= tauf && (full || e0 + e < V);
+                    cnt += hit[e] ? 1u : 0u;
+                }
+                const uint32_t cincl = wave_prefix_u32(cnt);
+                int pos = n + (int)(cincl - cnt);
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    if (hit[e]) {
+                        if (pos < kStageCap) stage[pos] = cand_key(x[e], (uint32_t)(e0 + e));
+                        ++pos;
+                    }
+                }
+                n += (int)lane_u32(cincl, kWave - 1);
+            }
+        } else {
+            // many hot vectors (a threshold at -inf, or heavy ties): element by element
+            const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+            for (int j = 0; j < kVecPerLane; ++j) {
+                if (__ballot(vmax[j] >= tauf) == 0ull) continue;
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float v = vec_elem<DT>(raw[j], e);
+                    const int id = id0 + j * kWave * N + e;
+                    const bool hit = v >= tauf && (full || id < V);
+                    const uint64_t mk = __ballot(hit);
+                    if (mk) {  // uniform; the store itself is unconditional (misses go to
+                               // the lane's discard slot)
+                        const int pos = n + __popcll(mk & below);
+                        stage[hit && pos < kStageCap ? pos : kStageCap + lane] = cand_key(v, (uint32_t)id);
+                        n += __popcll(mk);
+                    }
                 }
             }
         }
