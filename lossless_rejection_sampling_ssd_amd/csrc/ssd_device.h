@@ -387,7 +387,10 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
 }
 
 // Same for one nonzero 32-bit key per lane (0 = no key).
-__device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
+// With max_bits below 32 only the max_bits highest bits in which the keys differ are
+// resolved and the rest are left 0: a lower bound of the F-th largest key that still
+// has at least F keys at or above it.
+__device__ inline uint32_t wave_select_u32(uint32_t k, int F, int max_bits = 32) {
     const int n = wave_popc(k != 0u);
     if (n <= F) return 0u;
     uint32_t orv = k, andv = k ? k : ~0u;
@@ -395,7 +398,7 @@ __device__ inline uint32_t wave_select_u32(uint32_t k, int F) {
     andv = wave_and_u32(andv);
     uint32_t diff = orv ^ andv;
     uint32_t T = andv & ~diff;
-    while (diff) {
+    for (int it = 0; diff && it < max_bits; ++it) {
         const int bit = 31 - __clz(diff);
         diff &= ~(1u << bit);
         const uint32_t cand = T | (1u << bit);

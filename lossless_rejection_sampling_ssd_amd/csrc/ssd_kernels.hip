@@ -725,8 +725,11 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             }
         }
         wave_sync_lds();
+        // the slots a finalisation may read speculatively (up to 2F+2) hold 0 past the
+        // last key, so that it needs no per-tile count to mask them
+        const int fill = min(2 * F + 2, cap);
         if (n <= min(cap, kStageCap)) {
-            for (int q = lane; q < n; q += kWave) out[q] = stage[q];
+            for (int q = lane; q < max(n, fill); q += kWave) out[q] = q < n ? stage[q] : 0ull;
             ncand = n;
         } else {
             // More tied candidates than slots: store this tile's exact top F, found by
@@ -754,6 +757,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 if (lane == 0) out[q] = best;
                 prev = best;
             }
+            for (int q = F + lane; q < fill; q += kWave) out[q] = 0ull;
             ncand = F;
         }
     }
@@ -861,6 +865,7 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
     CandSummary cs;
     uint64_t k[kCandRegs];
     int Rg = 0;
+    int nc_lane = 0;
     if (fast) {
         const WavePartial qq = lane_partial(Pq, nt), pp = lane_partial(Pp, nt);
         if (F > 0) {
@@ -869,13 +874,13 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
         }
         stats_from_lanes(qq, f.c, mq, sq, aq);
         stats_from_lanes(pp, f.c, mp, sp, ap);
-        // Floor of the row's F-th largest value: the largest tile threshold, or the F-th
-        // largest tile maximum (F tiles hold an element at or above it) if higher.
+        // Floor of the row's F-th largest value: the largest tile threshold, or a lower
+        // bound of the F-th largest tile maximum (F tiles hold an element at or above
+        // it; its 10 leading differing bits suffice) if higher.
         cs.tr = wave_max_u32(qq.tau);
-        if (F > 0 && F < nt) cs.tr = max(cs.tr, wave_select_u32(lane < nt ? ord32(qq.m) : 0u, F));
+        if (F > 0 && F < nt) cs.tr = max(cs.tr, wave_select_u32(lane < nt ? ord32(qq.m) : 0u, F, 10));
         cs.max_nc = (int)wave_max_u32((uint32_t)qq.ncand);
-        if (lane < nt) sc.nc[lane] = (uint8_t)qq.ncand;
-        wave_sync_lds();
+        nc_lane = qq.ncand;
     } else {
         CandSummary unused;
         row_stats_wave(Pq, nt, f.c, mq, sq, aq, true, cs, sc.nc);
@@ -896,9 +901,16 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
     if (F > 0) {
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
-            mask_slots<kCandRegs>(k, nt, Rg, sc.nc, (uint64_t)cs.tr << 32);
+            // every tile's keys lie in its first Rg slots, and the slots past them hold 0
+            const uint64_t floor_key = (uint64_t)cs.tr << 32;
+#pragma unroll
+            for (int u = 0; u < kCandRegs; ++u) k[u] = k[u] >= floor_key ? k[u] : 0ull;
             key = select_sorted<kCandRegs>(k, (nt * Rg + kWave - 1) / kWave, F, sc);  // tile-major slots
         } else {
+            if (fast) {
+                if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
+                wave_sync_lds();
+            }
             key = row_topf_wave(Pq, cr, nt, f.cap, F, cs, sc);
         }
         M = finish_cache_row(key, F, mq, sq, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i], nullptr);
