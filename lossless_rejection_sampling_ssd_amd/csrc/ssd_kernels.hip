@@ -1105,91 +1105,143 @@ __device__ __forceinline__ int pass2_mode(const Pass2Args& a, int pos) {
     return a.mode == 1 ? kWQprime : (pos < a.K ? kWResid : kWP);
 }
 
-// Rescan of one tile element by element in id order: the first id whose running sum
-// (starting at base) exceeds thr, or with pick_last the last id of positive weight.
-// The caller has issued the tile loads (rp, rq).
+// The crossing tile is rescanned by the four waves of a block, wave j taking vector j
+// of the tile (ids t0 + (j*64 + lane)*N + e: vector, then lane, then element order).
+struct BonusShare {
+    double tot[kVecPass2];  // weight of each vector
+    int lastp[kVecPass2];   // last id of positive weight in each vector (-1: none)
+    int found;              // the id where the running sum crosses thr (-1: none)
+};
+
+// Phase 1, every wave: the weights of its vector, their total and last positive id,
+// published in sh.  Returns the lane's weight sum (phase 2 needs it).
 template <int DT, int MODE>
-__device__ inline int rescan_tile(const WParams& wp, const u32x4 (&rp)[kVecPass2], const u32x4 (&rq)[kVecPass2],
-                                  int64_t t0, int V, int my_id, uint32_t* bits, double base, double thr,
-                                  bool pick_last) {
+__device__ inline double rescan_vector_sums(const WParams& wp, u32x4 rp, u32x4 rq, int64_t t0, int V, int my_id,
+                                            uint32_t* bits, int j, BonusShare& sh) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int lane = lane_id();
     if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
-    double run = base;
-    int found = -1, last_pos = -1;
+    const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+    double w[N], p[N];
+    vec_weights<DT, MODE>(wp, rp, rq, e0, V, bits, t0, w, p);
+    double ls = 0.0;
+    int lastp = -1;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        ls += w[e];
+        if (w[e] > 0.0) lastp = (int)(e0 + e);
+    }
+    const double tot = wave_sum_f64(ls);
+    const int last = (int)wave_max_u32((uint32_t)(lastp + 1)) - 1;
+    if (lane == 0) {
+        sh.tot[j] = tot;
+        sh.lastp[j] = last;
+    }
+    return ls;
+}
+
+// Phase 2, after a block barrier: the vector where the running sum (from base, in
+// vector order) first exceeds thr, and run = the sum before it (-1 if none).
+__device__ __forceinline__ int crossing_vector(const BonusShare& sh, double base, double thr, double& run) {
+    run = base;
+    int jx = -1;
 #pragma unroll
     for (int j = 0; j < kVecPass2; ++j) {
-        const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
-        double w[N], p[N];
-        vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, V, bits, t0, w, p);
-        double ls = 0.0;
-#pragma unroll
-        for (int e = 0; e < N; ++e) ls += w[e];
-        const double incl = wave_prefix_f64(ls);
-        double cum = run + (incl - ls);
-        int hitpos = -1, lastp = -1;
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-            cum += w[e];
-            if (hitpos < 0 && cum > thr) hitpos = (int)(e0 + e);
-            if (w[e] > 0.0) lastp = (int)(e0 + e);
+        if (jx < 0) {
+            if (run + sh.tot[j] > thr)
+                jx = j;
+            else
+                run += sh.tot[j];
         }
-        if (!pick_last && found < 0) {
-            const uint64_t hm = __ballot(hitpos >= 0);
-            if (hm) found = (int)lane_u32((uint32_t)hitpos, uniform(__ffsll((long long)hm) - 1));
-        }
-        const uint64_t lm = __ballot(lastp >= 0);
-        if (lm) last_pos = (int)lane_u32((uint32_t)lastp, uniform(63 - __clzll(lm)));
-        run += lane_f64(incl, kWave - 1);
     }
-    return found >= 0 ? found : (last_pos >= 0 ? last_pos : (int)min<int64_t>(t0, V - 1));
+    return jx;
+}
+
+// Phase 2, the wave of the crossing vector: the first id whose running sum exceeds thr
+// (recomputing its weights), published in sh.found.
+template <int DT, int MODE>
+__device__ inline void rescan_vector_find(const WParams& wp, u32x4 rp, u32x4 rq, int64_t t0, int V,
+                                          const uint32_t* bits, int j, double ls, double run, double thr,
+                                          BonusShare& sh) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    const int lane = lane_id();
+    const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+    double w[N], p[N];
+    vec_weights<DT, MODE>(wp, rp, rq, e0, V, bits, t0, w, p);
+    const double incl = wave_prefix_f64(ls);
+    double cum = run + (incl - ls);
+    int hitpos = -1;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        cum += w[e];
+        if (hitpos < 0 && cum > thr) hitpos = (int)(e0 + e);
+    }
+    const uint64_t hm = __ballot(hitpos >= 0);
+    if (lane == 0) sh.found = hm ? (int)lane_u32((uint32_t)hitpos, uniform(__ffsll((long long)hm) - 1)) : -1;
 }
 
 // Inclusive wave scan of x (fp64, lane order).
 __device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_f64(x); }
 
-// Bonus of one group by one wave: totals over the tiles in tile order, the tile where
-// the running sum crosses u * total, the id inside it, and the cache lookup.  The tile
-// sums of the first 64 tiles, the row statistics and the cached ids are requested
+// Bonus of one group by one block of four waves: totals over the tiles in tile order
+// and the tile where the running sum crosses u * total (every wave, alike), the id
+// inside it (wave j rescans vector j of that tile), and the cache lookup (wave 0).  The
+// tile sums of the first 64 tiles, the row statistics and the cached ids are requested
 // together.
 template <int DT, bool VEC>
-__device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
-                                           double2 v0, uint32_t* bits) {
+__device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
+                                            double2 v0, uint32_t* bits, BonusShare& sh, int wave) {
     const int lane = lane_id();
     const int K = a.K;
     const int nt = a.nt;
     const double2* seg = a.seg + (int64_t)g * nt;
-    int tok = -1;
     double Zused = 0.0;
     int my_id = -1;
+    int mode = pass2_mode(a, pos);
+    bool pick_last = false;
+    double gbase = 0.0, thr = 0.0, ls = 0.0;
+    int64_t t0 = 0;
+    WParams wp{};
+    u32x4 rp = neg_inf_vec<DT>(), rq = neg_inf_vec<DT>();
     if (valid) {
         const int64_t r = (int64_t)b * (K + 1) + pos;
         const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
         const double u = (double)philox_uniform(a.seed, a.round, purpose, (uint64_t)b, (uint64_t)pos);
+        // one chunk of at most 64 tiles (the usual case): the scan that gives the total
+        // also locates the crossing
+        const double incl_w = nt <= kWave ? wave_scan_incl(v0.x) : 0.0;
         double tot_w = 0.0, tot_p = 0.0;
-        for (int g0 = 0; g0 < nt; g0 += kWave) {
-            const int j = g0 + lane;
-            double2 v = v0;
-            if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
-            tot_w += lane_f64(wave_scan_incl(v.x), kWave - 1);
-            tot_p += lane_f64(wave_scan_incl(v.y), kWave - 1);
+        if (nt <= kWave) {
+            tot_w = lane_f64(incl_w, kWave - 1);
+        } else {
+            for (int g0 = 0; g0 < nt; g0 += kWave) {
+                const int j = g0 + lane;
+                double2 v = v0;
+                if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+                tot_w += lane_f64(wave_scan_incl(v.x), kWave - 1);
+            }
         }
-        int mode = pass2_mode(a, pos);
         double Z = tot_w;
         const bool use_p = mode == kWResid && !(Z > 0.0);
         if (use_p) {
+            for (int g0 = 0; g0 < nt; g0 += kWave) {
+                const int j = g0 + lane;
+                double2 v = v0;
+                if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+                tot_p += lane_f64(wave_scan_incl(v.y), kWave - 1);
+            }
             mode = kWP;
             Z = tot_p;
         }
-        const double thr = u * Z;
+        thr = u * Z;
         int gsel = -1, glast = -1;
-        double gbase = 0.0, lastbase = 0.0, carry = 0.0;
+        double lastbase = 0.0, carry = 0.0;
         for (int g0 = 0; g0 < nt; g0 += kWave) {
             const int j = g0 + lane;
             double2 v = v0;
             if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
             const double x = use_p ? v.y : v.x;
-            const double incl = wave_scan_incl(x) + carry;
+            const double incl = (nt <= kWave && !use_p ? incl_w : wave_scan_incl(x)) + carry;
             const double excl = incl - x;
             const uint64_t cross = __ballot(j < nt && incl > thr);
             const uint64_t posm = __ballot(j < nt && x > 0.0);
@@ -1205,29 +1257,55 @@ __device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int
             }
             carry = lane_f64(incl, kWave - 1);
         }
-        bool pick_last = false;
         if (gsel < 0) {
             gsel = glast < 0 ? 0 : glast;
             gbase = lastbase;
             pick_last = true;
         }
-        // the crossing tile, the row statistics and the cached ids travel together
-        const int64_t t0 = (int64_t)gsel * kTile2<DT>;
+        // this wave's vector of the crossing tile, the row statistics and the cached ids
+        // travel together
+        t0 = (int64_t)gsel * kTile2<DT>;
+        const int64_t v0id = t0 + (int64_t)wave * kWave * ElemTraits<DT>::kPerVec;
         const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
         const char* qrow = a.q_logits + r * a.ld_bytes;
-        u32x4 rp[kVecPass2], rq[kVecPass2];
-        if (mode != kWQprime) load_tile<DT, VEC, kVecPass2>(prow, t0, a.V, lane, rp);
-        if (mode != kWP) load_tile<DT, VEC, kVecPass2>(qrow, t0, a.V, lane, rq);
+        u32x4 tp[1], tq[1];
+        tp[0] = rp;
+        tq[0] = rq;
+        if (mode != kWQprime) load_tile<DT, VEC, 1>(prow, v0id, a.V, lane, tp);
+        if (mode != kWP) load_tile<DT, VEC, 1>(qrow, v0id, a.V, lane, tq);
+        rp = tp[0];
+        rq = tq[0];
         const LawIn L = load_law(a, r);
         my_id = cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O);
-        const WParams wp = make_wparams(a.c, a.C, mode != kWQprime, L);
+        wp = make_wparams(a.c, a.C, mode != kWQprime, L);
         Zused = Z * wp.inv_p;  // the residual (or target) mass in probability units
         if (mode == kWResid)
-            tok = rescan_tile<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
+            ls = rescan_vector_sums<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits, wave, sh);
         else if (mode == kWP)
-            tok = rescan_tile<DT, kWP>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
+            ls = rescan_vector_sums<DT, kWP>(wp, rp, rq, t0, a.V, my_id, bits, wave, sh);
         else
-            tok = rescan_tile<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits, gbase, thr, pick_last);
+            ls = rescan_vector_sums<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits, wave, sh);
+    }
+    __syncthreads();
+    double run = 0.0;
+    const int jx = valid && !pick_last ? crossing_vector(sh, gbase, thr, run) : -1;
+    if (jx == wave) {
+        if (mode == kWResid)
+            rescan_vector_find<DT, kWResid>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+        else if (mode == kWP)
+            rescan_vector_find<DT, kWP>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+        else
+            rescan_vector_find<DT, kWQprime>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    int tok = -1;
+    if (valid) {
+        int last_pos = -1;
+#pragma unroll
+        for (int j = 0; j < kVecPass2; ++j) last_pos = max(last_pos, sh.lastp[j]);
+        if (last_pos < 0) last_pos = (int)min<int64_t>(t0, a.V - 1);
+        tok = (jx >= 0 && sh.found >= 0) ? sh.found : last_pos;
     }
     if (lane == 0) {
         if (a.mode == 0) {
@@ -1247,20 +1325,22 @@ __device__ __forceinline__ void bonus_wave(const Pass2Args& a, int g, int b, int
                     a.slot, a.fallback_tokens, ValueStore{a.cache_values, a.Bf, a.next_draft});
 }
 
-// One wave per group when the bonus runs as a kernel of its own.
+// One block of four waves per group when the bonus runs as a kernel of its own.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args a, int ngroups) {
+    static_assert(kVecPass2 == kWavesPerBlock, "one wave per vector of a pass-2 tile");
     __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
+    __shared__ BonusShare sh;
     const int wave = threadIdx.x / kWave;
-    const int g = blockIdx.x * kWavesPerBlock + wave;
-    if (g >= ngroups) return;
+    const int g = blockIdx.x;
+    if (g >= ngroups) return;  // uniform over the block
     const int lane = threadIdx.x % kWave;
     // the group's tile sums do not depend on the accepted length: request them first
     const double2 v0 = lane < a.nt ? a.seg[(int64_t)g * a.nt + lane] : make_double2(0.0, 0.0);
     int b, pos, verrs = 0;
     bool valid;
     pass2_group(a, g, b, pos, valid, &verrs);
-    bonus_wave<DT, VEC>(a, g, b, pos, valid, verrs, v0, bits[wave]);
+    bonus_block<DT, VEC>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave);
 }
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
@@ -1584,7 +1664,7 @@ hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hi
 }
 
 hipError_t launch_finalize_bonus(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st) {
-    const int grid = (ngroups + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int grid = ngroups;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
         finalize_bonus_kernel<decltype(DT)::value, decltype(VEC)::value><<<grid, kBlock, 0, st>>>(a, ngroups);
     });
