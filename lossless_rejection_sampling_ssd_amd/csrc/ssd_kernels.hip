@@ -240,14 +240,19 @@ __device__ inline uint64_t rank_sort_lds(TopfScratch& sc, int n, int F) {
     int rank[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int j = u * kWave + lane;
-        k[u] = j < n ? sc.surv[j] : 0ull;
+        k[u] = 0ull;
         rank[u] = 0;
     }
     if (n <= kWave) {
-        // one key per lane: the others are read from lanes, not from LDS
-        for (int v = 0; v < n; ++v) rank[0] += lane_u64(k[0], v) > k[0];
+        // one key per lane, compared with every key (LDS broadcast reads)
+        k[0] = lane < n ? sc.surv[lane] : 0ull;
+        for (int v = 0; v < n; ++v) rank[0] += sc.surv[v] > k[0];
     } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = u * kWave + lane;
+            k[u] = j < n ? sc.surv[j] : 0ull;
+        }
         for (int v = 0; v < n; ++v) {
             const uint64_t x = sc.surv[v];
 #pragma unroll
@@ -356,16 +361,38 @@ __device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, c
 // register slots: the F-th largest value by radix select, the keys at or above it by
 // rank (a whole-key select first when more than kSurvivorCap keys tie there).
 template <int KREG>
-__device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, int F, TopfScratch& sc) {
-    // At most one key per lane: rank them all.  Otherwise one histogram step usually
-    // leaves few enough keys (those in or above the bin of the F-th largest value) to
-    // rank them all; failing that, resolve the value exactly.
+__device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, int F, TopfScratch& sc,
+                                                  uint64_t floor_key = 1ull) {
+    // Keys below floor_key are dropped.  At most one key per lane: each lane places its
+    // keys after those of the lanes below it (one prefix sum), and they are ranked.
+    // Otherwise one histogram step usually leaves few enough keys (those in or above
+    // the bin of the F-th largest value) to rank them all; failing that, resolve the
+    // value exactly.
+    // Every slot at or past U holds 0, so the counting and placing loops run over all
+    // KREG slots with no test of U.
     U = uniform(U);
-    int live = 0;
+    uint32_t mine = 0u;
 #pragma unroll
-    for (int u = 0; u < KREG; ++u)
-        if (u < U) live += wave_popc(k[u] != 0ull);
-    if (live <= kWave) return rank_sort_lds(sc, compact_keys<KREG>(sc, k, U, 0ull), F);
+    for (int u = 0; u < KREG; ++u) mine += k[u] >= floor_key ? 1u : 0u;
+    const uint32_t incl = wave_prefix_u32(mine);
+    const int live = (int)lane_u32(incl, kWave - 1);
+    if (live <= kWave) {
+        // the comparisons are redone rather than kept (KREG masks would not fit in
+        // scalar registers)
+#pragma unroll
+        for (int u = 0; u < KREG; ++u) __asm__ volatile("" : "+v"(k[u]));
+        int pos = (int)(incl - mine);
+#pragma unroll
+        for (int u = 0; u < KREG; ++u) {
+            const bool keep = k[u] >= floor_key;
+            sc.surv[keep ? pos : kSurvivorCap + lane_id()] = k[u];
+            pos += keep ? 1 : 0;
+        }
+        wave_sync_lds();
+        return rank_sort_lds(sc, live, F);
+    }
+#pragma unroll
+    for (int u = 0; u < KREG; ++u) k[u] = k[u] >= floor_key ? k[u] : 0ull;
     uint64_t lo = (uint64_t)wave_select_value<KREG>(k, U, F, sc.bins, true) << 32;
     int n = compact_keys<KREG>(sc, k, U, lo);
     if (n > kSurvivorCap) {
@@ -902,10 +929,16 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
             // every tile's keys lie in its first Rg slots, and the slots past them hold 0
-            const uint64_t floor_key = (uint64_t)cs.tr << 32;
-#pragma unroll
-            for (int u = 0; u < kCandRegs; ++u) k[u] = k[u] >= floor_key ? k[u] : 0ull;
-            key = select_sorted<kCandRegs>(k, (nt * Rg + kWave - 1) / kWave, F, sc);  // tile-major slots
+            const uint64_t floor_key = cs.tr ? (uint64_t)cs.tr << 32 : 1ull;
+            const int U = uniform((nt * Rg + kWave - 1) / kWave);  // tile-major slots in use
+            if (U <= 4)
+                key = select_sorted<4>(reinterpret_cast<uint64_t(&)[4]>(k), U, F, sc, floor_key);
+            else if (U <= 8)
+                key = select_sorted<8>(reinterpret_cast<uint64_t(&)[8]>(k), U, F, sc, floor_key);
+            else if (U <= 12)
+                key = select_sorted<12>(reinterpret_cast<uint64_t(&)[12]>(k), U, F, sc, floor_key);
+            else
+                key = select_sorted<kCandRegs>(k, U, F, sc, floor_key);
         } else {
             if (fast) {
                 if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
