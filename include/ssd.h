@@ -63,7 +63,7 @@ enum { SSD_PURPOSE_ACCEPT = 0, SSD_PURPOSE_BONUS = 1, SSD_PURPOSE_DRAFT = 2, SSD
 
 enum {
     SSD_DEVERR_TOKEN_RANGE = 1,  /* a draft token outside [0, V): treated as rejected */
-    SSD_DEVERR_QPRIME_ZERO = 2,  /* q'(d) == 0 in fp32 for a tested draft token: rejected */
+    SSD_DEVERR_QPRIME_ZERO = 2,  /* q'(d) == 0 (in fp64) for a tested draft token: rejected */
     SSD_DEVERR_LEN_RANGE = 4,    /* accept_len outside [0, K]: bonus -1, miss */
     SSD_DEVERR_SLOT_RANGE = 8    /* a hit whose slot lies outside [0, Bf): next draft -1 */
 };

@@ -570,9 +570,11 @@ __device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp
         if (greedy) {
             ratio = (d == argp) ? 1.0 : 0.0;
         } else {
+            // one element per test: both probabilities in fp64 from the exact exponents
+            // (z c - o), so that a tiny p or q' does not underflow as an fp32 term would
             const RowNorm np = row_norm(mp, sp, c), nq = row_norm(mq, sq, c);
-            const double p = (double)term(pr.zp, c, np.o) * np.inv;
-            const double q = (double)term(pr.zq, c, nq.o) * nq.inv;
+            const double p = exp2((double)pr.zp * (double)c - (double)np.o) * np.inv;
+            const double q = exp2((double)pr.zq * (double)c - (double)nq.o) * nq.inv;
             const double qp = q * (in_cache ? (double)C : 1.0) / Zi;
             if (!(qp > 0.0)) {
                 err |= kErrQprimeZero;

@@ -66,7 +66,10 @@ def compare_round(g, o, K, Bf, check_stats=True, label="", values=None):
     ok = ~e_len
     assert np.array_equal(g["accept_len"][ok], o.accept_len[ok]), (label, np.nonzero(g["accept_len"] != o.accept_len))
     same_k = g["accept_len"] == o.accept_len
-    np.testing.assert_allclose(g["resid_mass"][same_k], o.resid_mass[same_k], atol=PROB_ATOL, rtol=0, err_msg=label)
+    # E3: a residual mass below 1e-5 is decided by rounding (exactly 0 in the oracle's
+    # fp64 selects the target law instead), so its value is not compared
+    cmp_z = same_k & ((o.exc & oracle.E3_DEGENERATE_RESIDUAL) == 0)
+    np.testing.assert_allclose(g["resid_mass"][cmp_z], o.resid_mass[cmp_z], atol=PROB_ATOL, rtol=0, err_msg=label)
     ok2 = ~e_any
     bad = np.nonzero((g["bonus"] != o.bonus) & ok2)[0]
     assert bad.size == 0, (label, "bonus", bad[:10], g["bonus"][bad[:10]], o.bonus[bad[:10]])

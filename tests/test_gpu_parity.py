@@ -218,6 +218,44 @@ def test_round_vs_oracle_and_chain(case):
         assert np.array_equal(g[k], g2[k]), ("determinism", label, k)
 
 
+EDGE_CASES = [
+    # (label, dtype, B, K, V, T, F, C, scale, noise, quantum)
+    # F_k at its maximum, with coarse (heavily tied) draft logits: many tied candidates
+    # per tile, the histogram select and the exact per-tile fallback
+    ("F=64 ties", "bf16", 3, 2, 50000, 1.0, [64, 0, 0], 0.5, 1.0, 0.3, 0.5),
+    ("F=64 smooth", "f32", 4, 1, 70001, 1.0, [64, 0], 0.3, 2.0, 0.5, 0.0),
+    ("peaked T=0.05", "bf16", 6, 3, 20000, 0.05, [8, 4, 2, 1], 0.5, 2.0, 0.5, 0.0),
+    ("flat T=5", "f32", 6, 3, 20000, 5.0, [8, 4, 2, 1], 0.5, 2.0, 0.5, 0.0),
+    ("large logits", "f32", 5, 2, 9000, 1.0, [6, 3, 1], 0.5, 3000.0, 20.0, 0.0),
+    ("all tied", "bf16", 4, 2, 6000, 1.0, [5, 3, 1], 0.5, 0.0, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: c[0])
+def test_round_edge_cases(case):
+    """The fused round against the oracle at the edges of the method: the largest
+    fan-out share, heavy ties, near-greedy and flat temperatures, large logits, and
+    rows where every logit is equal."""
+    label, dtype, B, K, V, T, F, C, scale, noise, quantum = case
+    _case("edge " + label)
+    g = torch.Generator().manual_seed(sum(map(ord, label)))
+    zq = torch.randn((B, K + 1, V), generator=g) * scale
+    if quantum > 0:
+        zq = torch.round(zq / quantum) * quantum
+    zp = zq + torch.randn((B, K + 1, V), generator=g) * noise
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    zq, zp = zq.to(dt), zp.to(dt)
+    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+    seed, rnd = 0xED6E + B, 5
+    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
+    draft[0, 0] = 0
+    draft[-1, -1] = V - 1
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, 1)
+    g_ = gpu_round(zp.cuda(), zq.cuda(), T, F, C, draft, seed, rnd, 1)
+    flagged = compare_round(g_, o, K, sum(F), label=label)
+    assert flagged < B, (label, flagged)  # the forced edge tokens may be flagged; the rest are compared
+
+
 def test_forced_paths():
     """All accepted (p = q, C = 1); rejection at position 0 (z_p(d_0) = -inf);
     invalid draft tokens; a bonus that cannot be cached (F = 0) misses."""
