@@ -27,7 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
 
 F32, BF16 = 0, 1
 PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
-ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE, ERR_SLOT_RANGE = 1, 2, 4, 8
+ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE, ERR_SLOT_RANGE, ERR_HIST_RANGE = 1, 2, 4, 8, 16
 FALLBACK_NONE, FALLBACK_UNIFORM = 0, 1  # the primary speculator / uniform random tokens
 E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
 FANOUT_EPS = 1e-9
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                           P, dbl, P, u64, u64, i64, dbl, P, P, P, P, P, P]
         L.orc_cache_lookup.argtypes = [i32, i32, i32, P, i32, P, P, P, i32, u64, u64, i64, P, P, P, P]
         L.orc_cache_gather.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+        L.orc_ngram_fallback.argtypes = [i32, i32, i32, P, i64, P, P, P, P, P, i32, i32, u64, u64, i64, P, P,
+                                         P, P, P]
         L.orc_bonus_rank.argtypes = [i32, i32, i32, i64, i32, P, P, P, i32, P, P]
         L.orc_round.argtypes = [i32, i32, i32, i64, i32, P, P, dbl, P, i32, dbl, P, u64, u64, i64, dbl, i32,
                                 P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
@@ -263,6 +265,32 @@ def cache_gather(values, hit, slot, fallback_tokens):
     lib().orc_cache_gather(B, K, Bf, _ptr(values), _ptr(hit), _ptr(slot), _ptr(fallback_tokens), _ptr(nd),
                            _ptr(err))
     return nd, err
+
+
+def ngram_fallback(K, V, hist, hist_len, draft, accept_len, bonus, hit, n_min, n_max, seed, round_,
+                   b_base: int = 0, next_draft=None):
+    """n-gram fallback speculator (prompt lookup over the context hist[b, :len_b] ++
+    draft[b, :k] ++ [bonus]; see ``orc_ngram_fallback`` for the reading).  hist is
+    int32 [B, ld_hist]; hit (uint8 [B]) or None (every sequence served).  Returns
+    (tokens [B, K], match_n [B], match_end [B], err [B]); next_draft, when given, is
+    updated in place for the served sequences."""
+    hist = np.ascontiguousarray(hist, dtype=np.int32)
+    B, ld = hist.shape
+    hist_len = np.ascontiguousarray(hist_len, dtype=np.int32)
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, K)
+    accept_len = np.ascontiguousarray(accept_len, dtype=np.int32)
+    bonus = np.ascontiguousarray(bonus, dtype=np.int32)
+    hit_a = None if hit is None else np.ascontiguousarray(hit, dtype=np.uint8)
+    if next_draft is not None:
+        assert next_draft.dtype == np.int32 and next_draft.shape == (B, K) and next_draft.flags.c_contiguous
+    tokens = np.zeros((B, K), dtype=np.int32)
+    mn = np.zeros(B, dtype=np.int32)
+    me = np.zeros(B, dtype=np.int32)
+    err = np.zeros(B, dtype=np.int32)
+    lib().orc_ngram_fallback(B, K, V, _ptr(hist), ld, _ptr(hist_len), _ptr(draft), _ptr(accept_len), _ptr(bonus),
+                             _ptr(hit_a), n_min, n_max, seed, round_, b_base, _ptr(tokens), _ptr(next_draft),
+                             _ptr(mn), _ptr(me), _ptr(err))
+    return tokens, mn, me, err
 
 
 def bonus_rank(zq, accept_len, bonus, R: int, hist=None):

@@ -58,6 +58,7 @@
 #define ORC_ERR_QPRIME_ZERO 2   /* q'(d) == 0 for a tested draft token */
 #define ORC_ERR_LEN_RANGE 4     /* accept_len outside [0, K] given to a step */
 #define ORC_ERR_SLOT_RANGE 8    /* a hit whose slot lies outside [0, Bf) */
+#define ORC_ERR_HIST_RANGE 16   /* a history length outside [0, ld_hist] */
 
 /* Near-tie / range exception bits (per sequence), decided from fp64 values. */
 #define ORC_E1_ACCEPT_TIE 1
@@ -626,6 +627,75 @@ void orc_bonus_rank(int B, int K, int V, int64_t ld, int dtype, const void* q_lo
         }
         if (rank_out) rank_out[b] = (int32_t)rank;
         if (hist) hist[(int64_t)k * (R + 1) + (rank < R ? rank : R)] += 1u;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* n-gram fallback speculator ([zh] section 2 Challenge 3 and [nl] section 3 C name an
+ * n-gram model, next to random tokens, as the fast, low-quality speculator that a
+ * large batch falls back to on a cache miss).  The pages describe it no further.
+ * READING (prompt lookup over the sequence's own context):
+ *   context   c = hist[b][0 .. len_b) ++ draft[b][0 .. k) ++ [bonus[b]], length L,
+ *             k = accept_len[b] (the tokens the verified round appended);
+ *   match     the largest n in [n_min, n_max] for which the last n tokens of c also
+ *             occur earlier, ending at some e <= L - 2; among those occurrences the
+ *             latest (largest e);
+ *   proposal  the K tokens that followed that occurrence, t_j = x[e + 1 + j] over
+ *             x = c ++ t (so when fewer than K tokens follow the occurrence the copy
+ *             runs on over the tokens just proposed, with period L - 1 - e);
+ *   no match  the uniform random tokens of the cache lookup's uniform fallback,
+ *             (U32(seed, round, b, j, FALLBACK) * V) >> 32.
+ * Only sequences that missed are served (all when hit is NULL); a hit gets tokens -1
+ * and leaves next_draft alone, as the cache gather already wrote it.  A length k
+ * outside [0, K] or len_b outside [0, ld_hist] is invalid input: error bit, tokens
+ * -1.  match_n gets n (0 when there is no match), match_end gets e (-1). */
+void orc_ngram_fallback(int B, int K, int V, const int32_t* hist, int64_t ld_hist,
+                        const int32_t* hist_len, const int32_t* draft, const int32_t* accept_len,
+                        const int32_t* bonus, const uint8_t* hit, int n_min, int n_max,
+                        uint64_t seed, uint64_t round, int64_t b_base, int32_t* tokens,
+                        int32_t* next_draft, int32_t* match_n, int32_t* match_end, int32_t* err) {
+    for (int b = 0; b < B; ++b) {
+        int32_t* out = tokens + (int64_t)b * K;
+        int n_found = 0, e_found = -1;
+        for (int j = 0; j < K; ++j) out[j] = -1;
+        if (hit && hit[b]) {
+            if (match_n) match_n[b] = 0;
+            if (match_end) match_end[b] = -1;
+            continue;
+        }
+        const int k = accept_len[b], len = hist_len[b];
+        int bad = 0;
+        if (k < 0 || k > K) { bad = 1; if (err) err[b] |= ORC_ERR_LEN_RANGE; }
+        if (len < 0 || (int64_t)len > ld_hist) { bad = 1; if (err) err[b] |= ORC_ERR_HIST_RANGE; }
+        if (!bad) {
+            const int L = len + k + 1;
+            int32_t* c = (int32_t*)malloc(sizeof(int32_t) * (size_t)(L + K));
+            for (int x = 0; x < len; ++x) c[x] = hist[(int64_t)b * ld_hist + x];
+            for (int x = 0; x < k; ++x) c[len + x] = draft[(int64_t)b * K + x];
+            c[L - 1] = bonus[b];
+            for (int n = n_max; n >= n_min && !n_found; --n) {
+                if (n > L - 1) continue;  /* an earlier occurrence needs n <= e + 1 <= L - 1 */
+                for (int e = L - 2; e >= n - 1; --e) {
+                    int same = 1;
+                    for (int j = 0; j < n && same; ++j) same = c[e - j] == c[L - 1 - j];
+                    if (same) { n_found = n; e_found = e; break; }
+                }
+            }
+            if (n_found) {
+                for (int j = 0; j < K; ++j) c[L + j] = c[e_found + 1 + j];
+                for (int j = 0; j < K; ++j) out[j] = c[L + j];
+            } else {
+                for (int j = 0; j < K; ++j) {
+                    uint64_t x = orc_uniform_u32(seed, round, ORC_PURPOSE_FALLBACK, b_base + b, j);
+                    out[j] = (int32_t)((x * (uint64_t)V) >> 32);
+                }
+            }
+            free(c);
+        }
+        if (match_n) match_n[b] = n_found;
+        if (match_end) match_end[b] = e_found;
+        if (next_draft)
+            for (int j = 0; j < K; ++j) next_draft[(int64_t)b * K + j] = out[j];
     }
 }
 
