@@ -7,8 +7,8 @@ top-F speculation cache with geometric fan-out, Saguaro reweighting, lossless
 verification, residual bonus sampling, cache lookup and the next draft gathered
 from a synthetic value store (one ssd_round call: two streaming HIP kernels, each
 followed by a small one).  Outside the timed rounds it also measures the coverage
-statistics pass (bonus rank within the draft row) and reports the fan-out the
-optimiser picks from them.  Inputs (seeded synthetic
+statistics pass (bonus rank within the draft row), reports the fan-out the
+optimiser picks from them, and times the n-gram fallback speculator on the misses.  Inputs (seeded synthetic
 logits, draft tokens from the library's own Saguaro sampler) are resident in HBM
 before timing; the timed loop rotates over distinct logit buffers totalling more
 than the 256 MB last-level cache so that rows come from HBM.
@@ -69,7 +69,7 @@ def main():
     import torch
 
     import lossless_rejection_sampling_ssd_amd as ssd
-    from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_logits
+    from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits
 
     w = WORKLOADS[args.workload]
     T = w.temps[-1]
@@ -176,6 +176,30 @@ def main():
     torch.cuda.synchronize()
     rank_us = r0.elapsed_time(r1) * 1e3 / nr
     rank_bytes = B * V * esize
+    # the n-gram fallback speculator on the misses of the last round, over synthetic
+    # 4096-token histories (spans repeated within each history)
+    NG_L, NG_MIN, NG_MAX = 4096, 2, 5
+    h_np_tok, h_len = make_histories(B, NG_L, V, seed=w.seed)
+    ng_hist = torch.as_tensor(h_np_tok, device=dev)
+    ng_len = torch.as_tensor(h_len, device=dev)
+    ng_tok = torch.zeros((B, K), dtype=torch.int32, device=dev)
+    ng_n = torch.zeros(B, dtype=torch.int32, device=dev)
+    d_last = bufs[(args.warmup + min(n, 64) - 1) % nbuf][2]
+
+    def ngram():
+        ssd.ssd_ngram_fallback(V, ng_hist, ng_len, d_last, outb["accept_len"], outb["bonus"], NG_MIN, NG_MAX,
+                               w.seed, 0, ng_tok, hit=outb["hit"], match_n=ng_n)
+
+    ngram()
+    torch.cuda.synchronize()
+    served = outb["hit"].cpu().numpy() == 0
+    ng_match = float((ng_n.cpu().numpy()[served] > 0).mean()) if served.any() else 0.0
+    r0.record()
+    for i in range(nr):
+        ngram()
+    r1.record()
+    torch.cuda.synchronize()
+    ngram_us = r0.elapsed_time(r1) * 1e3 / nr
     rows2 = np.where(ks < K, 2, 1).sum(axis=1).mean() if T > 0 else 0.0
     pass2_bytes = rows2 * V * esize
     round_bytes = pass1_bytes + pass2_bytes
@@ -241,6 +265,10 @@ def main():
             "predicted_hit_rate_optimized": round(hits_opt / max(total, 1), 4),
             "bonus_rank_us": round(rank_us, 2),
             "bonus_rank_GBps": round(rank_bytes / (rank_us * 1e-6) / 1e9, 1),
+            "ngram_fallback_us": round(ngram_us, 2),
+            "ngram_history": "%d-token synthetic histories, n = %d..%d, misses of the last round (%d of %d)" % (
+                NG_L, NG_MIN, NG_MAX, int(served.sum()), B),
+            "ngram_match_rate": round(ng_match, 4),
             "wall_s": round(wall, 3),
         },
         "roofline": {

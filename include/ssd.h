@@ -65,11 +65,12 @@ enum {
     SSD_DEVERR_TOKEN_RANGE = 1,  /* a draft token outside [0, V): treated as rejected */
     SSD_DEVERR_QPRIME_ZERO = 2,  /* q'(d) == 0 (in fp64) for a tested draft token: rejected */
     SSD_DEVERR_LEN_RANGE = 4,    /* accept_len outside [0, K]: bonus -1, miss */
-    SSD_DEVERR_SLOT_RANGE = 8    /* a hit whose slot lies outside [0, Bf): next draft -1 */
+    SSD_DEVERR_SLOT_RANGE = 8,   /* a hit whose slot lies outside [0, Bf): next draft -1 */
+    SSD_DEVERR_HIST_RANGE = 16   /* a history length outside [0, ld_hist]: n-gram tokens -1 */
 };
 
 /* Limits of this build. */
-enum { SSD_MAX_K = 16, SSD_MAX_F = 64 };
+enum { SSD_MAX_K = 16, SSD_MAX_F = 64, SSD_MAX_NGRAM = 16 };
 
 typedef struct {
     int32_t B;      /* sequences, >= 1 */
@@ -183,6 +184,34 @@ ssd_status ssd_cache_lookup(int32_t B, int32_t K, int32_t V, const int32_t* F_ho
 ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* values, const uint8_t* hit,
                             const int32_t* slot, const int32_t* fallback_tokens, int32_t* next_draft,
                             int32_t* dev_err, void* stream);
+
+/* ssd_ngram_fallback -- the n-gram fallback speculator ([zh] section 2 Challenge 3
+ * and [nl] section 3 C name an n-gram model, next to random tokens, as the fast,
+ * low-quality speculator a large batch falls back to on a miss; they give no rule).
+ * Reading of the pages (prompt lookup over the sequence's own context):
+ *   context   c = hist[b, 0 .. hist_len[b]) ++ draft[b, 0 .. k) ++ [bonus[b]], length
+ *             L, with k = accept_len[b] (the tokens the verified round appended);
+ *   match     the largest n in [n_min, n_max] whose last n tokens of c also occur
+ *             ending at some e <= L - 2, and the latest such e;
+ *   proposal  fallback_tokens[b, j] = c[e + 1 + (j mod (L - 1 - e))], j < K: the
+ *             tokens that followed the occurrence, the copy running on over its own
+ *             output when fewer than K follow;
+ *   no match  the uniform random draft of ssd_cache_lookup's SSD_FALLBACK_UNIFORM,
+ *             (U32(seed, round, b, j, FALLBACK) * V) >> 32.
+ * Sequences with hit[b] != 0 get fallback_tokens -1 and keep their next_draft row (the
+ * cache gather wrote it); hit NULL serves every sequence.  For every served sequence
+ * next_draft[b, :] (nullable) is set to the proposal, match_n[b] (nullable) to n (0:
+ * no match) and match_end[b] (nullable) to e (-1).  An accept_len outside [0, K]
+ * sets SSD_DEVERR_LEN_RANGE, a hist_len outside [0, ld_hist] SSD_DEVERR_HIST_RANGE;
+ * both give tokens -1.  Token values are opaque (no range check).
+ * hist [B, ld_hist] int32 (may be NULL when ld_hist == 0), hist_len [B], draft [B, K],
+ * accept_len [B], bonus [B] int32, hit [B] uint8.  1 <= n_min <= n_max <=
+ * SSD_MAX_NGRAM, 1 <= K <= SSD_MAX_K, V >= 2. */
+ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hist, int64_t ld_hist,
+                              const int32_t* hist_len, const int32_t* draft, const int32_t* accept_len,
+                              const int32_t* bonus, const uint8_t* hit, int32_t n_min, int32_t n_max,
+                              ssd_rng rng, int32_t* fallback_tokens, int32_t* next_draft, int32_t* match_n,
+                              int32_t* match_end, int32_t* dev_err, void* stream);
 
 /* Outputs of the fused round.  Required: cache_ids [B, Bf], accept_len [B], bonus
  * [B], hit [B], slot [B], fallback_tokens [B, K].  The rest are nullable. */

@@ -21,10 +21,11 @@ SSD_OK, SSD_ERR_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_HIP, SSD_ERR_WORKSPACE = 0, 1,
 SSD_F32, SSD_BF16 = 0, 1
 SSD_FALLBACK_NONE, SSD_FALLBACK_UNIFORM = 0, 1
 SSD_DEVERR_TOKEN_RANGE, SSD_DEVERR_QPRIME_ZERO, SSD_DEVERR_LEN_RANGE, SSD_DEVERR_SLOT_RANGE = 1, 2, 4, 8
-SSD_MAX_K, SSD_MAX_F = 16, 64
+SSD_DEVERR_HIST_RANGE = 16
+SSD_MAX_K, SSD_MAX_F, SSD_MAX_NGRAM = 16, 64, 16
 
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
-            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_round",
+            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
             "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
             "ssd_status_string", "ssd_last_error")
 
@@ -79,6 +80,8 @@ def _load():
     L.ssd_residual_sample.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, f32, _P, ssd_rng, _P, _P, _P,
                                       _P, sz, _P]
     L.ssd_cache_gather.argtypes = [i32, i32, i32, _P, _P, _P, _P, _P, _P, _P]
+    L.ssd_ngram_fallback.argtypes = [i32, i32, i32, _P, ctypes.c_int64, _P, _P, _P, _P, _P, i32, i32, ssd_rng,
+                                     _P, _P, _P, _P, _P, _P]
     L.ssd_cache_lookup.argtypes = [i32, i32, i32, _P, i32, _P, _P, _P, i32, ssd_rng, _P, _P, _P, _P, _P]
     L.ssd_round.argtypes = [S, _P, _P, _P, _P, i32, f32, ssd_rng, i32, ctypes.POINTER(ssd_round_out),
                             ctypes.POINTER(ssd_round_events), _P, sz, _P]
@@ -92,8 +95,8 @@ def _load():
     L.ssd_last_error.argtypes = []
     L.ssd_last_error.restype = ctypes.c_char_p
     for name in ("ssd_fanout", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight", "ssd_verify",
-                 "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_round", "ssd_bonus_rank",
-                 "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
+                 "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
+                 "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
         getattr(L, name).restype = i32
     return L
 
@@ -285,6 +288,24 @@ def ssd_cache_gather(values, hit, slot, fallback_tokens, next_draft, dev_err=Non
                                  _ptr(slot, torch.int32, "slot"), _ptr(fallback_tokens, torch.int32, "fallback_tokens"),
                                  _ptr(next_draft, torch.int32, "next_draft"), _ptr(dev_err, torch.int32),
                                  _stream(stream)), "ssd_cache_gather")
+
+
+def ssd_ngram_fallback(V, hist, hist_len, draft, accept_len, bonus, n_min, n_max, seed, round_, fallback_tokens,
+                       hit=None, next_draft=None, match_n=None, match_end=None, dev_err=None, stream=None):
+    """n-gram fallback draft [B, K] for the sequences that missed (all when hit is
+    None) from hist [B, ld_hist] (contiguous int32, row b valid up to hist_len[b])
+    and the round's accepted tokens and bonus."""
+    B, K = (int(x) for x in draft.shape)
+    ld = int(hist.shape[1])
+    _check(_lib.ssd_ngram_fallback(B, K, int(V), _ptr(hist, torch.int32, "hist") if ld > 0 else None, ld,
+                                   _ptr(hist_len, torch.int32, "hist_len"),
+                                   _ptr(draft, torch.int32, "draft"), _ptr(accept_len, torch.int32, "accept_len"),
+                                   _ptr(bonus, torch.int32, "bonus"), _ptr(hit, torch.uint8, "hit"), int(n_min),
+                                   int(n_max), ssd_rng(seed, round_),
+                                   _ptr(fallback_tokens, torch.int32, "fallback_tokens"),
+                                   _ptr(next_draft, torch.int32, "next_draft"), _ptr(match_n, torch.int32, "match_n"),
+                                   _ptr(match_end, torch.int32, "match_end"), _ptr(dev_err, torch.int32),
+                                   _stream(stream)), "ssd_ngram_fallback")
 
 
 def ssd_bonus_rank(shape, q_logits, accept_len, bonus, R, rank_out=None, rank_hist=None, ws=None, stream=None):

@@ -8,8 +8,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblrs_ssd.so")
-SOURCES = ["ssd_kernels.hip", "ssd_api.hip", "ssd_policy.cpp"]
-HEADERS = ["ssd_device.h", "ssd_kernels.h"]
+SOURCES = ["ssd_kernels.hip", "ssd_ngram.hip", "ssd_api.hip", "ssd_policy.cpp"]
+HEADERS = ["ssd_device.h", "ssd_kernels.h", "ssd_ngram.h"]
 ARCH = "gfx950"
 
 

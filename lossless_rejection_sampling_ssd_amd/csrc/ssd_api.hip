@@ -10,6 +10,7 @@
 
 #include "../../include/ssd.h"
 #include "ssd_kernels.h"
+#include "ssd_ngram.h"
 
 namespace {
 
@@ -450,6 +451,40 @@ ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* val
     hipError_t e = ssd::launch_gather(B, K, Bf, values, hit, slot, fallback_tokens, next_draft, dev_err,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "ssd_cache_gather");
+    return SSD_OK;
+}
+
+ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hist, int64_t ld_hist,
+                              const int32_t* hist_len, const int32_t* draft, const int32_t* accept_len,
+                              const int32_t* bonus, const uint8_t* hit, int32_t n_min, int32_t n_max,
+                              ssd_rng rng, int32_t* fallback_tokens, int32_t* next_draft, int32_t* match_n,
+                              int32_t* match_end, int32_t* dev_err, void* stream) {
+    if (B < 1 || K < 1 || K > SSD_MAX_K || V < 2 || ld_hist < 0) return SSD_ERR_ARG;
+    if (n_min < 1 || n_max < n_min || n_max > SSD_MAX_NGRAM) return SSD_ERR_ARG;
+    if ((ld_hist > 0 && !hist) || !hist_len || !draft || !accept_len || !bonus || !fallback_tokens)
+        return SSD_ERR_ARG;
+    ssd::NgramArgs a{};
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.hist = hist;
+    a.ld_hist = ld_hist;
+    a.hist_len = hist_len;
+    a.draft = draft;
+    a.accept_len = accept_len;
+    a.bonus = bonus;
+    a.hit = hit;
+    a.n_min = n_min;
+    a.n_max = n_max;
+    a.seed = rng.seed;
+    a.round = rng.round;
+    a.tokens = fallback_tokens;
+    a.next_draft = next_draft;
+    a.match_n = match_n;
+    a.match_end = match_end;
+    a.dev_err = dev_err;
+    hipError_t e = ssd::launch_ngram(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "ssd_ngram_fallback");
     return SSD_OK;
 }
 

@@ -134,3 +134,32 @@ def to_oracle_array(z: torch.Tensor):
     if z.dtype == torch.bfloat16:
         return z.view(torch.int16).numpy().view(np.uint16)
     raise TypeError("unsupported logit dtype %s" % z.dtype)
+
+
+def make_histories(B: int, L: int, V: int, seed: int, min_frac: float = 0.5, p_copy: float = 0.4,
+                   span=(4, 32), zipf_a: float = 1.2):
+    """Token histories for the n-gram fallback speculator: int32 ``hist [B, L]`` and
+    ragged lengths ``[B]`` in ``[min_frac L, L]`` (entries past a length are -1).
+    Each history is a run of spans of ``span`` tokens: with probability ``p_copy`` a
+    copy of an earlier span of the same history (the repeats that code, math and chat
+    text have), otherwise fresh tokens of Zipf-distributed rank mapped through a fixed
+    random permutation of the vocabulary.  numpy generator, deterministic per seed."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(V).astype(np.int32)
+    hist = np.full((B, L), -1, dtype=np.int32)
+    lens = rng.integers(int(min_frac * L), L + 1, B).astype(np.int32)
+    for b in range(B):
+        n = int(lens[b])
+        row = hist[b]
+        cur = 0
+        while cur < n:
+            w = min(int(rng.integers(span[0], span[1] + 1)), n - cur)
+            if cur >= span[0] and rng.random() < p_copy:
+                w = min(w, cur)
+                s = int(rng.integers(0, cur - w + 1))
+                row[cur:cur + w] = row[s:s + w]
+            else:
+                row[cur:cur + w] = perm[(rng.zipf(zipf_a, w) - 1) % V]
+            cur += w
+    return hist, lens

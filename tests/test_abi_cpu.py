@@ -163,6 +163,22 @@ def test_cache_and_round_validation(ssd):
     assert L.ssd_bonus_rank(ctypes.byref(s), BAD, BAD, BAD, 8, BAD, None, ws, 8, None) == ssd.SSD_ERR_WORKSPACE
 
 
+
+def test_ngram_validation(ssd):
+    """n-gram fallback: sizes, n-gram range and required pointers are checked on the
+    host; a missing history is allowed only for ld_hist = 0."""
+    L = ssd.lib()
+    rng = ssd.ssd_rng(0, 0)
+
+    def call(B=2, K=4, V=100, hist=BAD, ld=8, hl=BAD, dr=BAD, acc=BAD, bon=BAD, nmin=1, nmax=3, out=BAD):
+        return L.ssd_ngram_fallback(B, K, V, hist, ld, hl, dr, acc, bon, None, nmin, nmax, rng, out, None, None,
+                                    None, None, None)
+
+    for kw in (dict(B=0), dict(K=0), dict(K=17), dict(V=1), dict(ld=-1), dict(hist=None), dict(hl=None),
+               dict(dr=None), dict(acc=None), dict(bon=None), dict(out=None), dict(nmin=0), dict(nmin=4, nmax=3),
+               dict(nmax=17)):
+        assert call(**kw) == ssd.SSD_ERR_ARG, kw
+
 def test_binding_refuses_host_tensors(ssd):
     import torch
     z = torch.zeros(1, 2, 8)
