@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c3", help="c1..c5 (default: the headline B=64 K=8 V=128256 bf16)")
     ap.add_argument("--buffers", type=int, default=0, help="distinct logit buffers to rotate (0: >= 1 GB)")
+    ap.add_argument("--T", type=float, default=None, help="temperature (default: the workload's last)")
     ap.add_argument("--C", type=float, default=None)
     ap.add_argument("--target-sigma", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,7 +73,7 @@ def main():
     from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits
 
     w = WORKLOADS[args.workload]
-    T = w.temps[-1]
+    T = w.temps[-1] if args.T is None else args.T
     C = args.C if args.C is not None else w.Cs[len(w.Cs) // 2]
     sig = args.target_sigma
     esize = 2 if w.dtype == "bf16" else 4

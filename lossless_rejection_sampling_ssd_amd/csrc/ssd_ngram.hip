@@ -51,7 +51,10 @@ __global__ __launch_bounds__(kNgBlock) void ngram_kernel(const NgramArgs a) {
     const int K = a.K;
     int32_t* out = a.tokens + (int64_t)b * K;
     int32_t* nd = a.next_draft ? a.next_draft + (int64_t)b * K : nullptr;
-    if (a.hit && a.hit[b]) {  // the cache gather has written this sequence's draft
+    // the per-sequence scalars are independent: request them together
+    const int hit = a.hit ? a.hit[b] : 0;
+    const int k = a.accept_len[b], len = a.hist_len[b], bonus = a.bonus[b];
+    if (hit) {  // the cache gather has written this sequence's draft
         if (tid < K) out[tid] = -1;
         if (tid == 0) {
             if (a.match_n) a.match_n[b] = 0;
@@ -59,7 +62,6 @@ __global__ __launch_bounds__(kNgBlock) void ngram_kernel(const NgramArgs a) {
         }
         return;
     }
-    const int k = a.accept_len[b], len = a.hist_len[b];
     const int bad = ((k < 0 || k > K) ? kNgErrLen : 0) | ((len < 0 || (int64_t)len > a.ld_hist) ? kNgErrHist : 0);
     if (bad) {
         if (tid < K) {
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kNgBlock) void ngram_kernel(const NgramArgs a) {
         }
         return;
     }
-    const Context c{a.hist + (int64_t)b * a.ld_hist, a.draft + (int64_t)b * K, len, k, a.bonus[b]};
+    const Context c{a.hist + (int64_t)b * a.ld_hist, a.draft + (int64_t)b * K, len, k, bonus};
     const int L = len + k + 1;
     const int ncap = min(a.n_max, L - 1);  // an earlier occurrence ends at e <= L - 2
     if (tid < ncap) suffix[tid] = c.at(L - 1 - tid);
