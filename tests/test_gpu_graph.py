@@ -1,0 +1,111 @@
+"""The fused round and the n-gram fallback speculator captured in a HIP graph: the
+library issues no allocation, memset, copy or synchronisation, so a serving loop can
+capture one round and replay it on new inputs copied into the captured buffers.
+Every replay (eager copies and synchronisations between replays) must equal the eager
+calls on the same inputs, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import lossless_rejection_sampling_ssd_amd as ssd
+from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits, scaled
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def _inputs(w, buffer):
+    zq, zp = make_logits(w, buffer=buffer, device="cuda")
+    T, C = w.temps[0], w.Cs[0]
+    shape = ssd.shape_of(zq, T)
+    F = ssd.ssd_fanout(w.K, w.Bf, w.r)
+    B, K, R = w.B, w.K, w.B * (w.K + 1)
+    qm = torch.zeros(R, device="cuda")
+    qs = torch.zeros(R, dtype=torch.float64, device="cuda")
+    qa = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ssd.ssd_softmax(shape, zq, qm, qs, qa)
+    ids = torch.zeros((B, w.Bf), dtype=torch.int32, device="cuda")
+    mass = torch.zeros(R, dtype=torch.float64, device="cuda")
+    ssd.ssd_build_cache(shape, zq, qm, qs, F, ids, mass)
+    Z = torch.zeros(R, dtype=torch.float64, device="cuda")
+    d = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+    ssd.ssd_saguaro_reweight(shape, mass, C, Z, zq, qm, qs, qa, F, ids, None, w.seed, 500 + buffer, d)
+    torch.cuda.synchronize()
+    return zp, zq, d
+
+
+@pytest.mark.parametrize("wl,T", [("c3", 1.0), ("c5", 1.0), ("c2", 0.0)])
+def test_round_graph_replays_match_eager(wl, T):
+    print("\n[case] graph capture of the round, %s recipe, T=%g" % (wl, T), flush=True)
+    base = WORKLOADS[wl]
+    w = scaled(base, B=16, V=20000)
+    from dataclasses import replace
+    w = replace(w, temps=(T,))
+    F = ssd.ssd_fanout(w.K, w.Bf, w.r)
+    C = w.Cs[0]
+    fallback = ssd.SSD_FALLBACK_UNIFORM if w.fallback_uniform else ssd.SSD_FALLBACK_NONE
+    sets = [_inputs(w, b) for b in range(3)]
+    values = torch.randint(0, w.V, (w.B, w.Bf, w.K), dtype=torch.int32, device="cuda",
+                           generator=torch.Generator(device="cuda").manual_seed(7))
+    hist_np, lens_np = make_histories(w.B, 512, w.V, seed=w.seed)
+    hist = torch.as_tensor(hist_np, device="cuda")
+    lens = torch.as_tensor(lens_np, device="cuda")
+
+    # static buffers the graph reads and writes
+    zp_s = torch.empty_like(sets[0][0])
+    zq_s = torch.empty_like(sets[0][1])
+    d_s = torch.empty_like(sets[0][2])
+    shape = ssd.shape_of(zp_s, T)
+    ws = ssd.Workspace()
+    buf = ssd.RoundBuffers(w.B, w.K, w.Bf, cache_values=values)
+    ng_tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda")
+
+    def one_round():
+        ssd.ssd_round(shape, zp_s, zq_s, d_s, F, C, w.seed, 3, fallback, buf.out, ws=ws)
+        ssd.ssd_ngram_fallback(w.V, hist, lens, d_s, buf["accept_len"], buf["bonus"], 1, 4, w.seed, 3, ng_tok,
+                               hit=buf["hit"], next_draft=buf["next_draft"])
+
+    def load(j):
+        zp_s.copy_(sets[j][0])
+        zq_s.copy_(sets[j][1])
+        d_s.copy_(sets[j][2])
+
+    def snapshot():
+        out = {k: v.clone() for k, v in buf.t.items()}
+        out["ngram"] = ng_tok.clone()
+        return out
+
+    # eager reference on each input set
+    eager = []
+    for j in range(3):
+        load(j)
+        one_round()
+        torch.cuda.synchronize()
+        eager.append(snapshot())
+    assert not torch.equal(eager[0]["cache_ids"], eager[1]["cache_ids"])
+
+    # capture (after a warm-up on the capture stream), then replay in a changing order
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        load(0)
+        one_round()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_round()
+    torch.cuda.synchronize()
+    for rep, j in enumerate([1, 0, 2, 2, 1]):
+        for t in buf.t.values():  # eager work between replays
+            t.fill_(-1 if t.dtype != torch.uint8 else 255)
+        ng_tok.fill_(-5)
+        buf["dev_err"].zero_()
+        load(j)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for k, v in eager[j].items():
+            assert torch.equal(got[k], v), (rep, j, k)
