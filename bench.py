@@ -62,8 +62,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the round of this library runs on a single MI355X "
-              "(batch sharding across GPUs is described in DESIGN.md); --gpus %d is not supported" % args.gpus,
-              file=sys.stderr)
+              "(sequences would shard across GPUs with no exchange; only the one-GPU path is built); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
