@@ -429,8 +429,10 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
                 ok = 0;
                 ratio = 0.0;
             } else if (T > 0.0) {
-                double p = row_prob(load_logit(p_logits, dtype, r * ld + d), d, p_max[r], p_sum[r], p_arg[r], T);
-                double q = row_prob(load_logit(q_logits, dtype, r * ld + d), d, q_max[r], q_sum[r], q_arg[r], T);
+                const double zpd = load_logit(p_logits, dtype, r * ld + d);
+                const double zqd = load_logit(q_logits, dtype, r * ld + d);
+                double p = row_prob(zpd, d, p_max[r], p_sum[r], p_arg[r], T);
+                double q = row_prob(zqd, d, q_max[r], q_sum[r], q_arg[r], T);
                 double qp = q * (in_cache(S, F[i], d) ? C : 1.0) / Z[r];
                 if (qp <= 0.0) {
                     e |= ORC_ERR_QPRIME_ZERO;
@@ -443,7 +445,11 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
                     /* no earlier rejection: this position is tested */
                     double u = orc_uniform(seed, round, ORC_PURPOSE_ACCEPT, b_base + b, i);
                     if (fabs(u - ratio) < ORC_TIE_EPS) x_flags |= ORC_E1_ACCEPT_TIE;
-                    if (p < ORC_TINY || qp < ORC_TINY) x_flags |= ORC_E5_TINY_PROB;
+                    /* a finite logit whose probability is this small is at the edge of
+                     * the working range; a masked (-inf) logit has probability exactly 0
+                     * in any precision, so its test is exact and not flagged */
+                    if ((p < ORC_TINY && !isinf(zpd)) || (qp < ORC_TINY && !isinf(zqd)))
+                        x_flags |= ORC_E5_TINY_PROB;
                 }
             } else {
                 ratio = (d == p_arg[r]) ? 1.0 : 0.0;

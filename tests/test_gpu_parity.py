@@ -502,3 +502,51 @@ def test_full_size_sampled(name, C, sig):
     for b in sample:
         orank, _ = oracle.bonus_rank(per[int(b)][1], g["accept_len"][b:b + 1], g["bonus"][b:b + 1], 64)
         assert rk[b] == orank[0], (name, b)
+
+
+MASK_CASES = [
+    # (label, dtype, B, K, V, T, F, C, frac_shared, frac_target_only, n_finite_row0)
+    # a vocabulary mask shared by both models (banned ids)
+    ("shared mask", "bf16", 6, 3, 30000, 1.0, [10, 6, 3, 1], 0.5, 0.5, 0.0, 0),
+    # ids only the target masks: the draft proposes tokens of target probability 0
+    ("target-only mask", "f32", 6, 3, 20000, 1.0, [8, 4, 2, 1], 0.5, 0.0, 0.3, 0),
+    # a row with fewer finite ids than F_0 (the cache takes -inf ids, lower id first)
+    ("F above finite ids", "bf16", 4, 2, 9000, 0.8, [20, 4, 2], 0.4, 0.2, 0.1, 7),
+    # greedy with masks
+    ("masked greedy", "f32", 5, 3, 12000, 0.0, [6, 3, 2, 1], 0.5, 0.4, 0.2, 0),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: c[0])
+def test_round_masked_vocabulary(case):
+    """-inf logits (masked ids) in the fused round against the oracle: shared masks,
+    target-only masks (draft tokens the target forbids are rejected with ratio 0),
+    and a draft row with fewer finite ids than its cache share."""
+    label, dtype, B, K, V, T, F, C, f_shared, f_target, n_fin = case
+    _case("mask " + label)
+    g = torch.Generator().manual_seed(sum(map(ord, label)))
+    zq = torch.randn((B, K + 1, V), generator=g) * 2.0
+    zp = zq + torch.randn((B, K + 1, V), generator=g) * 0.7
+    shared = torch.rand((B, K + 1, V), generator=g) < f_shared
+    target = torch.rand((B, K + 1, V), generator=g) < f_target
+    zq[shared] = float("-inf")
+    zp[shared | target] = float("-inf")
+    # every row keeps one finite id in both models
+    zq[:, :, 123 % V] = 1.0
+    zp[:, :, 123 % V] = 1.0
+    if n_fin:
+        keep = torch.randperm(V, generator=g)[:n_fin]
+        row = torch.full((V,), float("-inf"))
+        row[keep] = torch.randn(n_fin, generator=g)
+        zq[0, 0] = row
+        zp[0, 0] = row + 0.1
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    zq, zp = zq.to(dt), zp.to(dt)
+    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+    seed, rnd = 0x3A5C + B, 2
+    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, 1)
+    values = np.random.default_rng(B).integers(0, V, (B, sum(F), K)).astype(np.int32)
+    g_ = gpu_round(zp.cuda(), zq.cuda(), T, F, C, draft, seed, rnd, 1, values=values)
+    flagged = compare_round(g_, o, K, sum(F), label=label, values=values)
+    assert flagged <= B // 2, (label, flagged)
