@@ -5,8 +5,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
-#include <string>
 
 #include "../../include/ssd.h"
 #include "ssd_kernels.h"
@@ -14,7 +14,9 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// Text of the last HIP failure of this thread; a fixed buffer, so that recording it
+// can neither allocate nor throw across the C ABI.
+thread_local char g_last_error[256];
 
 constexpr size_t kAlign = 256;
 
@@ -62,7 +64,7 @@ void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
 }
 
 ssd_status fail_hip(hipError_t e, const char* where) {
-    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
     return SSD_ERR_HIP;
 }
 
@@ -147,7 +149,7 @@ const char* ssd_status_string(ssd_status s) {
     return "unknown status";
 }
 
-const char* ssd_last_error(void) { return g_last_error.c_str(); }
+const char* ssd_last_error(void) { return g_last_error; }
 
 ssd_status ssd_fanout(int32_t K, int32_t Bf, double r, int32_t* F_host) {
     if (!F_host || K < 1 || K > SSD_MAX_K || Bf < 0 || !(r > 0.0) || !(r <= 1.0)) return SSD_ERR_ARG;
