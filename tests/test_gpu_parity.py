@@ -550,3 +550,50 @@ def test_round_masked_vocabulary(case):
     g_ = gpu_round(zp.cuda(), zq.cuda(), T, F, C, draft, seed, rnd, 1, values=values)
     flagged = compare_round(g_, o, K, sum(F), label=label, values=values)
     assert flagged <= B // 2, (label, flagged)
+
+
+def _random_round_config(i):
+    """Seeded random configuration i: dtype, shape, row padding, temperature, an
+    arbitrary fan-out (any split of B_f with 0 <= F_k <= 64, not only geometric), C
+    and the fallback mode."""
+    rng = np.random.default_rng(0xC0FFEE + i)
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    B = int(rng.integers(1, 9))
+    K = int(rng.integers(1, 11))
+    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 9000)), int(rng.integers(9000, 60000))]))
+    pad = int(rng.choice([0, 0, int(rng.integers(1, 40))]))
+    T = float(rng.choice([0.0, 0.5, 1.0, 1.0, 1.6]))
+    Fmax = min(V, 64)
+    F = [int(rng.integers(0, min(Fmax, 24) + 1)) if rng.random() < 0.8 else 0 for _ in range(K + 1)]
+    C = float(rng.choice([1.0, float(rng.uniform(0.05, 1.0))]))
+    fb = int(rng.integers(0, 2))
+    scale = float(rng.uniform(0.5, 4.0))
+    noise = float(rng.uniform(0.1, 1.5))
+    return dtype, B, K, V, pad, T, F, C, fb, scale, noise
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_round_random_configs(i):
+    """The fused round against the oracle (and against itself chained through the six
+    separate calls) over 48 seeded random configurations, row strides above V
+    included."""
+    dtype, B, K, V, pad, T, F, C, fb, scale, noise = _random_round_config(i)
+    label = "random %d: %s B=%d K=%d V=%d pad=%d T=%g F=%s C=%.3f fb=%d" % (i, dtype, B, K, V, pad, T, F, C, fb)
+    _case(label)
+    zq, zp = _rand(B, K, V, dtype, 0xAB00 + i, scale, noise, ld=V + pad if pad else None)
+    seed, rnd = 0x5EED + i, 100 + i
+    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+    Fa = np.array(F, np.int32)
+    draft, _ = oracle_draft(zp_np, zq_np, T, Fa, C, seed, rnd)
+    o = oracle.round_(zp_np, zq_np, T, Fa, C, draft, seed, rnd, fb)
+    zpd, zqd = _to_dev(zp), _to_dev(zq)
+    Bf = sum(F)
+    values = np.random.default_rng(i).integers(0, V, (B, max(Bf, 1), K)).astype(np.int32)[:, :Bf]
+    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb, values=values if Bf > 0 else None)
+    compare_round(g, o, K, Bf, label=label, values=values if Bf > 0 else None)
+    ch = _chain(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    for k in ch:
+        a, b = g[k], ch[k]
+        if k == "cache_ids":
+            a, b = a[:, :Bf], b[:, :Bf]
+        assert np.array_equal(a, b), (label, k)
