@@ -657,15 +657,23 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     // each later phase widens the elements afresh rather than keeping them live
     opaque_regs(raw);
 
+    // Lowest id of the lane holding m_lane: the lane's ids ascend with (vector, element),
+    // so it lies in the first vector whose maximum equals m_lane; only that vector's
+    // elements are compared.  (Padding past V holds -inf; it can equal m_lane only when
+    // every element of the lane is -inf, and then the id test excludes it.)
     int arg = INT_MAX;
     if (a.want_arg) {
+        int jm = kVecPerLane;
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j)
+        for (int j = kVecPerLane - 1; j >= 0; --j) jm = vmax[j] == m_lane ? j : jm;
+        u32x4 v = raw[0];
 #pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const int64_t id = tile0 + (int64_t)(j * kWave + lane) * N + e;
-                if (arg == INT_MAX && id < V && vec_elem<DT>(raw[j], e) == m_lane) arg = (int)id;
-            }
+        for (int j = 1; j < kVecPerLane; ++j) v = jm == j ? raw[j] : v;
+        const int64_t id0 = tile0 + (int64_t)(jm * kWave + lane) * N;
+        int em = N;
+#pragma unroll
+        for (int e = N - 1; e >= 0; --e) em = (vec_elem<DT>(v, e) == m_lane && id0 + e < V) ? e : em;
+        if (jm < kVecPerLane && em < N) arg = (int)(id0 + em);
     }
     double s = s_lane;
     opaque_regs(raw);
