@@ -206,7 +206,8 @@ ssd_status ssd_cache_gather(int32_t B, int32_t K, int32_t Bf, const int32_t* val
  * both give tokens -1.  Token values are opaque (no range check).
  * hist [B, ld_hist] int32 (may be NULL when ld_hist == 0), hist_len [B], draft [B, K],
  * accept_len [B], bonus [B] int32, hit [B] uint8.  1 <= n_min <= n_max <=
- * SSD_MAX_NGRAM, 1 <= K <= SSD_MAX_K, V >= 2. */
+ * SSD_MAX_NGRAM, 1 <= K <= SSD_MAX_K, V >= 2; ld_hist above 2^31 - 18 returns
+ * SSD_ERR_UNSUPPORTED. */
 ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hist, int64_t ld_hist,
                               const int32_t* hist_len, const int32_t* draft, const int32_t* accept_len,
                               const int32_t* bonus, const uint8_t* hit, int32_t n_min, int32_t n_max,

@@ -465,6 +465,8 @@ ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hi
     if (n_min < 1 || n_max < n_min || n_max > SSD_MAX_NGRAM) return SSD_ERR_ARG;
     if ((ld_hist > 0 && !hist) || !hist_len || !draft || !accept_len || !bonus || !fallback_tokens)
         return SSD_ERR_ARG;
+    // context positions (history + K + 1) are 32-bit in the kernel
+    if (ld_hist > (int64_t)INT32_MAX - SSD_MAX_K - 1) return SSD_ERR_UNSUPPORTED;
     ssd::NgramArgs a{};
     a.B = B;
     a.K = K;

@@ -178,6 +178,7 @@ def test_ngram_validation(ssd):
                dict(dr=None), dict(acc=None), dict(bon=None), dict(out=None), dict(nmin=0), dict(nmin=4, nmax=3),
                dict(nmax=17)):
         assert call(**kw) == ssd.SSD_ERR_ARG, kw
+    assert call(ld=(1 << 31) - 10) == ssd.SSD_ERR_UNSUPPORTED
 
 def test_binding_refuses_host_tensors(ssd):
     import torch
