@@ -264,6 +264,19 @@ ssd_status ssd_round(const ssd_shape* shape, const void* p_logits, const void* q
                      int32_t fallback, const ssd_round_out* out, const ssd_round_events* events,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ssd_round_devrng -- ssd_round with the round counter in device memory, for callers
+ * that capture the round in a HIP graph and replay it: the kernels read *round_dev
+ * (uint64, device memory, caller-owned) when they run, so the uniforms follow whatever
+ * the caller wrote there before the replay (for instance a captured increment after
+ * each round); the key is (seed, purpose) as for ssd_round.  Every other argument, the
+ * outputs and the errors are those of ssd_round; with *round_dev == r the results are
+ * bit-identical to ssd_round with rng = {seed, r}.  round_dev NULL returns SSD_ERR_ARG.
+ * Writing *round_dev while a round that reads it runs is a race. */
+ssd_status ssd_round_devrng(const ssd_shape* shape, const void* p_logits, const void* q_logits,
+                            const int32_t* draft, const int32_t* F_host, int32_t Bf, float C, uint64_t seed,
+                            const uint64_t* round_dev, int32_t fallback, const ssd_round_out* out,
+                            const ssd_round_events* events, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Choosing the fan-out from measured coverage.  [zh] section 2 Challenge 1 and [nl]
  * section 3 A say the fan-out solves a constrained optimisation over acceptance

@@ -25,9 +25,9 @@ SSD_DEVERR_HIST_RANGE = 16
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_NGRAM = 16, 64, 16
 
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
-            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
-            "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
-            "ssd_status_string", "ssd_last_error")
+            "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback",
+            "ssd_round", "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose",
+            "ssd_fallback_critical_batch", "ssd_status_string", "ssd_last_error")
 
 
 class SSDError(RuntimeError):
@@ -85,6 +85,8 @@ def _load():
     L.ssd_cache_lookup.argtypes = [i32, i32, i32, _P, i32, _P, _P, _P, i32, ssd_rng, _P, _P, _P, _P, _P]
     L.ssd_round.argtypes = [S, _P, _P, _P, _P, i32, f32, ssd_rng, i32, ctypes.POINTER(ssd_round_out),
                             ctypes.POINTER(ssd_round_events), _P, sz, _P]
+    L.ssd_round_devrng.argtypes = [S, _P, _P, _P, _P, i32, f32, u64, _P, i32, ctypes.POINTER(ssd_round_out),
+                                   ctypes.POINTER(ssd_round_events), _P, sz, _P]
     L.ssd_bonus_rank.argtypes = [S, _P, _P, _P, i32, _P, _P, _P, sz, _P]
     L.ssd_fanout_optimize.argtypes = [i32, i32, i32, i32, _P, _P, _P, _P]
     FM = ctypes.POINTER(ssd_fallback_model)
@@ -96,7 +98,7 @@ def _load():
     L.ssd_last_error.restype = ctypes.c_char_p
     for name in ("ssd_fanout", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight", "ssd_verify",
                  "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
-                 "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
+                 "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
         getattr(L, name).restype = i32
     return L
 
@@ -381,6 +383,21 @@ def ssd_round(shape, p_logits, q_logits, draft, F, C, seed, round_, fallback, ou
                           _ptr(draft, torch.int32, "draft"), _host_F(F), Bf, float(C), ssd_rng(seed, round_),
                           int(fallback), ctypes.byref(out), ctypes.byref(events) if events is not None else None,
                           w, nb, _stream(stream)), "ssd_round")
+
+
+def ssd_round_devrng(shape, p_logits, q_logits, draft, F, C, seed, round_dev, fallback, out: ssd_round_out,
+                     events: Optional[ssd_round_events] = None, ws=None, stream=None):
+    """ssd_round with the round counter read from round_dev (a one-element int64
+    device tensor holding the uint64 round) when the kernels run."""
+    if round_dev.numel() != 1:
+        raise ValueError("round_dev must hold one counter")
+    Bf = int(sum(F))
+    w, nb = _ws(ws, shape, Bf)
+    _check(_lib.ssd_round_devrng(ctypes.byref(shape), _logit_ptr(p_logits, "p_logits"),
+                                 _logit_ptr(q_logits, "q_logits"), _ptr(draft, torch.int32, "draft"), _host_F(F), Bf,
+                                 float(C), int(seed), _ptr(round_dev, torch.int64, "round_dev"), int(fallback),
+                                 ctypes.byref(out), ctypes.byref(events) if events is not None else None, w, nb,
+                                 _stream(stream)), "ssd_round_devrng")
 
 
 # ---------------------------------------------------------------------------- convenience

@@ -492,9 +492,12 @@ ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hi
     return SSD_OK;
 }
 
-ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
-                     const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, int32_t fallback,
-                     const ssd_round_out* out, const ssd_round_events* ev, void* ws, size_t ws_bytes, void* stream) {
+// The fused round; round_dev (nullable) replaces rng.round by a counter the kernels read
+// from device memory when they run.
+static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                             const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, const uint64_t* round_dev,
+                             int32_t fallback, const ssd_round_out* out, const ssd_round_events* ev, void* ws,
+                             size_t ws_bytes, void* stream) {
     ssd_status st = check_shape(s);
     if (st != SSD_OK) return st;
     int O[SSD_MAX_K + 2];
@@ -550,6 +553,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     f.C = C;
     f.seed = rng.seed;
     f.round = rng.round;
+    f.round_ptr = round_dev;
     f.fallback = fallback;
     f.Bf = Bf;
     f.p_max = out->p_max ? out->p_max : fstats + 0 * R;
@@ -612,6 +616,7 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     b.accept_len_out = f.accept_len;
     b.seed = rng.seed;
     b.round = rng.round;
+    b.round_ptr = round_dev;
     b.seg = at<double2>(ws, L.seg);
     b.out_tok = out->bonus;
     b.resid_mass = out->resid_mass;
@@ -632,6 +637,23 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
     e = ssd::launch_finalize_bonus(s->dtype, vec, b, s->B, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_round bonus");
     return SSD_OK;
+}
+
+ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                     const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, int32_t fallback,
+                     const ssd_round_out* out, const ssd_round_events* ev, void* ws, size_t ws_bytes, void* stream) {
+    return round_impl(s, p_logits, q_logits, draft, F_host, Bf, C, rng, nullptr, fallback, out, ev, ws, ws_bytes,
+                      stream);
+}
+
+ssd_status ssd_round_devrng(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                            const int32_t* F_host, int32_t Bf, float C, uint64_t seed, const uint64_t* round_dev,
+                            int32_t fallback, const ssd_round_out* out, const ssd_round_events* ev, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!round_dev) return SSD_ERR_ARG;
+    const ssd_rng rng{seed, 0};
+    return round_impl(s, p_logits, q_logits, draft, F_host, Bf, C, rng, round_dev, fallback, out, ev, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"

@@ -59,6 +59,7 @@ struct SeqFinal {
     const float* probe;    // [B][K][2] logits at the draft tokens, recorded by pass 1
     float C;
     uint64_t seed, round;
+    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
     int fallback;
     int Bf;
     float* p_max;
@@ -105,6 +106,7 @@ struct Pass2Args {
     const int32_t* vflag;       // mode 0: per-position test outcomes (accepted length = first rejection)
     int32_t* accept_len_out;    // with vflag: written by the bonus kernel
     uint64_t seed, round;
+    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
     double2* seg;       // [groups][nt] (weight sum, target-law sum) per wave tile
     int32_t* out_tok;   // bonus [B] or draft [B, K]
     double* resid_mass; // nullable

@@ -895,7 +895,8 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
     pr.d = i < K ? f.draft[(int64_t)b * K + i] : 0;
     pr.zp = i < K ? f.probe[((int64_t)b * K + i) * 2 + 0] : 0.f;  // valid when d_i is in range
     pr.zq = i < K ? f.probe[((int64_t)b * K + i) * 2 + 1] : 0.f;
-    pr.u = (i < K && !f.greedy) ? philox_uniform(f.seed, f.round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
+    const uint64_t round = f.round_ptr ? *f.round_ptr : f.round;
+    pr.u = (i < K && !f.greedy) ? philox_uniform(f.seed, round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
     float mp, mq;
     double sp, sq;
     int ap, aq;
@@ -993,7 +994,8 @@ __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f)
         f.bonus[b] = tok;
         if (f.resid_mass) f.resid_mass[b] = 1.0;
     }
-    lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, f.round, f.hit, f.slot, f.fallback_tokens,
+    const uint64_t round = f.round_ptr ? *f.round_ptr : f.round;
+    lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, round, f.hit, f.slot, f.fallback_tokens,
                 ValueStore{f.cache_values, f.Bf, f.next_draft});
 }
 
@@ -1236,6 +1238,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
                                             double2 v0, uint32_t* bits, BonusShare& sh, int wave) {
     const int lane = lane_id();
     const int K = a.K;
+    const uint64_t round = a.round_ptr ? *a.round_ptr : a.round;
     const int nt = a.nt;
     const double2* seg = a.seg + (int64_t)g * nt;
     double Zused = 0.0;
@@ -1249,7 +1252,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
     if (valid) {
         const int64_t r = (int64_t)b * (K + 1) + pos;
         const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
-        const double u = (double)philox_uniform(a.seed, a.round, purpose, (uint64_t)b, (uint64_t)pos);
+        const double u = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos);
         // one chunk of at most 64 tiles (the usual case): the scan that gives the total
         // also locates the crossing
         const double incl_w = nt <= kWave ? wave_scan_incl(v0.x) : 0.0;
@@ -1364,7 +1367,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
         }
     }
     if (a.mode == 0 && a.do_lookup)
-        lookup_wave(b, K, a.V, valid ? pos : -1, valid ? a.O[pos] : 0, my_id, tok, a.fallback, a.seed, a.round, a.hit,
+        lookup_wave(b, K, a.V, valid ? pos : -1, valid ? a.O[pos] : 0, my_id, tok, a.fallback, a.seed, round, a.hit,
                     a.slot, a.fallback_tokens, ValueStore{a.cache_values, a.Bf, a.next_draft});
 }
 

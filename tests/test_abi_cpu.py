@@ -146,6 +146,9 @@ def test_cache_and_round_validation(ssd):
                        ws, 1 << 30, None) == ssd.SSD_ERR_ARG
     assert L.ssd_round(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0, ctypes.byref(out), None,
                        ws, 64, None) == ssd.SSD_ERR_WORKSPACE
+    # device-side round counter: required
+    assert L.ssd_round_devrng(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, 1, None, 0, ctypes.byref(out), None,
+                              ws, 1 << 30, None) == ssd.SSD_ERR_ARG
     # fused round: a next draft with Bf > 0 needs the value store
     out.next_draft = 0x3000
     assert L.ssd_round(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0, ctypes.byref(out), None,

@@ -3,11 +3,11 @@ library issues no allocation, memset, copy or synchronisation, so a serving loop
 capture one round and replay it on new inputs copied into the captured buffers.
 Every replay (eager copies and synchronisations between replays) must equal the eager
 calls on the same inputs, bit for bit."""
-import numpy as np
+from dataclasses import replace
+
 import pytest
 import torch
 
-import oracle
 import lossless_rejection_sampling_ssd_amd as ssd
 from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits, scaled
 
@@ -38,10 +38,7 @@ def _inputs(w, buffer):
 @pytest.mark.parametrize("wl,T", [("c3", 1.0), ("c5", 1.0), ("c2", 0.0)])
 def test_round_graph_replays_match_eager(wl, T):
     print("\n[case] graph capture of the round, %s recipe, T=%g" % (wl, T), flush=True)
-    base = WORKLOADS[wl]
-    w = scaled(base, B=16, V=20000)
-    from dataclasses import replace
-    w = replace(w, temps=(T,))
+    w = replace(scaled(WORKLOADS[wl], B=16, V=20000), temps=(T,))
     F = ssd.ssd_fanout(w.K, w.Bf, w.r)
     C = w.Cs[0]
     fallback = ssd.SSD_FALLBACK_UNIFORM if w.fallback_uniform else ssd.SSD_FALLBACK_NONE
@@ -109,3 +106,75 @@ def test_round_graph_replays_match_eager(wl, T):
         got = snapshot()
         for k, v in eager[j].items():
             assert torch.equal(got[k], v), (rep, j, k)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_round_devrng_graph_advances_the_round(T):
+    """ssd_round_devrng reads the round counter from device memory: eagerly it equals
+    ssd_round at that round; captured together with an increment of the counter, each
+    replay equals the eager round at the next counter value (fresh uniforms per replay).
+    Uniform fallback tokens on a miss, so the lookup's uniforms follow the counter too."""
+    print("\n[case] graph replays with a device-side round counter (c3 recipe, B=16 V=20000, T=%g)" % T, flush=True)
+    w = replace(scaled(WORKLOADS["c3"], B=16, V=20000), temps=(T,))
+    C = w.Cs[0]
+    fb = ssd.SSD_FALLBACK_UNIFORM
+    F = ssd.ssd_fanout(w.K, w.Bf, w.r)
+    sets = [_inputs(w, b) for b in range(2)]
+    zp_s = torch.empty_like(sets[0][0])
+    zq_s = torch.empty_like(sets[0][1])
+    d_s = torch.empty_like(sets[0][2])
+    shape = ssd.shape_of(zp_s, T)
+    ws = ssd.Workspace()
+    buf = ssd.RoundBuffers(w.B, w.K, w.Bf)
+    round_t = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def load(j):
+        zp_s.copy_(sets[j][0])
+        zq_s.copy_(sets[j][1])
+        d_s.copy_(sets[j][2])
+
+    def eager(j, r):
+        load(j)
+        ssd.ssd_round(shape, zp_s, zq_s, d_s, F, C, w.seed, r, fb, buf.out, ws=ws)
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in buf.t.items()}
+
+    # eager: the device counter gives the same round as the by-value one
+    for j, r in ((0, 7), (1, 12345678901)):
+        ref = eager(j, r)
+        round_t.fill_(r)
+        ssd.ssd_round_devrng(shape, zp_s, zq_s, d_s, F, C, w.seed, round_t, fb, buf.out, ws=ws)
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(buf.t[k], v), ("eager devrng", r, k)
+
+    # expected results of the replays: inputs alternate, the round advances from 40
+    order = [0, 1, 1, 0, 1]
+    expect = [eager(j, 40 + n) for n, j in enumerate(order)]
+    # the same inputs at rounds 41 and 42 draw different uniforms
+    assert any(not torch.equal(expect[1][k], expect[2][k]) for k in ("accept_len", "bonus", "fallback_tokens"))
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        load(0)
+        ssd.ssd_round_devrng(shape, zp_s, zq_s, d_s, F, C, w.seed, round_t, fb, buf.out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssd.ssd_round_devrng(shape, zp_s, zq_s, d_s, F, C, w.seed, round_t, fb, buf.out, ws=ws)
+        round_t.add_(1)
+    torch.cuda.synchronize()
+    round_t.fill_(40)
+    for n, j in enumerate(order):
+        for t in buf.t.values():  # eager work between replays
+            t.fill_(-1 if t.dtype != torch.uint8 else 255)
+        buf["dev_err"].zero_()
+        load(j)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in expect[n].items():
+            assert torch.equal(buf.t[k], v), ("replay", n, k)
+    assert int(round_t.item()) == 40 + len(order)
