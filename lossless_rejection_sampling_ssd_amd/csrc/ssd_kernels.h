@@ -59,7 +59,6 @@ struct SeqFinal {
     const float* probe;    // [B][K][2] logits at the draft tokens, recorded by pass 1
     float C;
     uint64_t seed, round;
-    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
     int fallback;
     int Bf;
     float* p_max;
@@ -82,6 +81,7 @@ struct SeqFinal {
     const int32_t* cache_values;  // nullable [B, Bf, K]: continuation per cache slot
     int32_t* next_draft;          // [B, K] when cache_values is set
     int32_t* vflag;       // [B, K] workspace: bit 0 accepted, higher bits error bits
+    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
 };
 
 struct Pass2Args {
@@ -106,7 +106,6 @@ struct Pass2Args {
     const int32_t* vflag;       // mode 0: per-position test outcomes (accepted length = first rejection)
     int32_t* accept_len_out;    // with vflag: written by the bonus kernel
     uint64_t seed, round;
-    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
     double2* seg;       // [groups][nt] (weight sum, target-law sum) per wave tile
     int32_t* out_tok;   // bonus [B] or draft [B, K]
     double* resid_mass; // nullable
@@ -118,6 +117,7 @@ struct Pass2Args {
     uint8_t* hit;
     int32_t* slot;
     int32_t* fallback_tokens;
+    const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
 };
 
 int tile_elems(int dtype);

@@ -877,7 +877,7 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
 // Z = 1 - (1 - C) M and the lossless test of draft token d_i.  For rows of at most 64
 // tiles the tile partials, the first 2 F_i + 2 candidate slots of every tile and the
 // logits at d_i are requested together.
-template <int DT>
+template <int DT, bool DEVRNG>
 __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
     __shared__ TopfScratch sc;
     const int lane = threadIdx.x;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
     pr.d = i < K ? f.draft[(int64_t)b * K + i] : 0;
     pr.zp = i < K ? f.probe[((int64_t)b * K + i) * 2 + 0] : 0.f;  // valid when d_i is in range
     pr.zq = i < K ? f.probe[((int64_t)b * K + i) * 2 + 1] : 0.f;
-    const uint64_t round = f.round_ptr ? *f.round_ptr : f.round;
+    const uint64_t round = DEVRNG ? *f.round_ptr : f.round;
     pr.u = (i < K && !f.greedy) ? philox_uniform(f.seed, round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
     float mp, mq;
     double sp, sq;
@@ -979,6 +979,7 @@ __global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
 
 // T = 0: one wave per sequence takes the accepted length from the test outcomes, the
 // bonus (target argmax at that position) and the cache lookup.
+template <bool DEVRNG>
 __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int b = blockIdx.x * kWavesPerBlock + wave;
@@ -994,7 +995,7 @@ __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f)
         f.bonus[b] = tok;
         if (f.resid_mass) f.resid_mass[b] = 1.0;
     }
-    const uint64_t round = f.round_ptr ? *f.round_ptr : f.round;
+    const uint64_t round = DEVRNG ? *f.round_ptr : f.round;
     lookup_wave(b, K, f.V, k, f.O[k], my_id, tok, f.fallback, f.seed, round, f.hit, f.slot, f.fallback_tokens,
                 ValueStore{f.cache_values, f.Bf, f.next_draft});
 }
@@ -1233,12 +1234,12 @@ __device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_
 // inside it (wave j rescans vector j of that tile), and the cache lookup (wave 0).  The
 // tile sums of the first 64 tiles, the row statistics and the cached ids are requested
 // together.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool DEVRNG>
 __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
                                             double2 v0, uint32_t* bits, BonusShare& sh, int wave) {
     const int lane = lane_id();
     const int K = a.K;
-    const uint64_t round = a.round_ptr ? *a.round_ptr : a.round;
+    const uint64_t round = DEVRNG ? *a.round_ptr : a.round;
     const int nt = a.nt;
     const double2* seg = a.seg + (int64_t)g * nt;
     double Zused = 0.0;
@@ -1372,7 +1373,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
 }
 
 // One block of four waves per group when the bonus runs as a kernel of its own.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool DEVRNG>
 __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args a, int ngroups) {
     static_assert(kVecPass2 == kWavesPerBlock, "one wave per vector of a pass-2 tile");
     __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
@@ -1386,7 +1387,7 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     int b, pos, verrs = 0;
     bool valid;
     pass2_group(a, g, b, pos, valid, &verrs);
-    bonus_block<DT, VEC>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave);
+    bonus_block<DT, VEC, DEVRNG>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave);
 }
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
@@ -1688,15 +1689,24 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
 
 hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
     const int grid = f.B * (f.K + 1);
-    if (dtype == 1)
-        finalize_pos_kernel<1><<<grid, kWave, 0, st>>>(f);
+    const bool dev = f.round_ptr != nullptr;  // round counter in device memory
+    if (dtype == 1 && dev)
+        finalize_pos_kernel<1, true><<<grid, kWave, 0, st>>>(f);
+    else if (dtype == 1)
+        finalize_pos_kernel<1, false><<<grid, kWave, 0, st>>>(f);
+    else if (dev)
+        finalize_pos_kernel<0, true><<<grid, kWave, 0, st>>>(f);
     else
-        finalize_pos_kernel<0><<<grid, kWave, 0, st>>>(f);
+        finalize_pos_kernel<0, false><<<grid, kWave, 0, st>>>(f);
     return hipGetLastError();
 }
 
 hipError_t launch_finish_greedy(const SeqFinal& f, hipStream_t st) {
-    finish_greedy_kernel<<<(f.B + kWavesPerBlock - 1) / kWavesPerBlock, kBlock, 0, st>>>(f);
+    const int grid = (f.B + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (f.round_ptr)
+        finish_greedy_kernel<true><<<grid, kBlock, 0, st>>>(f);
+    else
+        finish_greedy_kernel<false><<<grid, kBlock, 0, st>>>(f);
     return hipGetLastError();
 }
 
@@ -1712,7 +1722,10 @@ hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hi
 hipError_t launch_finalize_bonus(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st) {
     const int grid = ngroups;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
-        finalize_bonus_kernel<decltype(DT)::value, decltype(VEC)::value><<<grid, kBlock, 0, st>>>(a, ngroups);
+        if (a.round_ptr)
+            finalize_bonus_kernel<decltype(DT)::value, decltype(VEC)::value, true><<<grid, kBlock, 0, st>>>(a, ngroups);
+        else
+            finalize_bonus_kernel<decltype(DT)::value, decltype(VEC)::value, false><<<grid, kBlock, 0, st>>>(a, ngroups);
     });
 }
 
