@@ -10,7 +10,7 @@
 // running on over its own output (token j is c[e + 1 + j mod (L - 1 - e)]).  With no
 // match the proposal is the uniform random draft of the cache lookup.
 //
-// One block of four waves per sequence.  Every candidate end e gets the length m(e)
+// One block of sixteen waves per sequence.  Every candidate end e gets the length m(e)
 // of the common suffix of c[..e] and c (at most min(n_max, L - 1, e + 1)); the
 // answer is the largest key (m, e) with m >= n_min, so the longest n wins and, among
 // equal n, the latest e.  The block scans the ends from the latest down in chunks of
@@ -27,7 +27,7 @@
 namespace ssd {
 namespace {
 
-constexpr int kNgBlock = 256;
+constexpr int kNgBlock = 1024;
 constexpr int kNgWaves = kNgBlock / kWave;
 constexpr int kNgPer = 8;                       // candidate ends per thread per chunk
 constexpr int kNgChunk = kNgBlock * kNgPer;     // ends per chunk

@@ -84,16 +84,17 @@ def test_ngram_synthetic_histories(B, K, L, V, n_min, n_max):
     _check(V, hist, lens, draft, acc, bonus, None, n_min, n_max, 0x55D5, 4, "no hit mask", with_next=False)
 
 
-@pytest.mark.parametrize("alphabet", [1, 2, 3, 5])
-def test_ngram_tiny_alphabets(alphabet):
+@pytest.mark.parametrize("alphabet,ld", [(1, 700), (2, 700), (3, 700), (5, 700), (2, 20000), (4, 20000)])
+def test_ngram_tiny_alphabets(alphabet, ld):
     """Many equal n-grams (ties on n broken by the latest end), ragged lengths from 0
-    to past one 256-end chunk, every k."""
-    _case("ngram tiny alphabet=%d" % alphabet)
-    rng = np.random.default_rng(alphabet)
-    B, K, ld, V = 96, 6, 700, 10
+    to past several 8192-end chunks (the scan stops after the chunk that reaches the
+    longest possible match), every k."""
+    _case("ngram tiny alphabet=%d ld=%d" % (alphabet, ld))
+    rng = np.random.default_rng(alphabet + ld)
+    B, K, V = 96, 6, 10
     hist = rng.integers(0, alphabet, (B, ld)).astype(np.int32)
     lens = rng.integers(0, ld + 1, B).astype(np.int32)
-    lens[:6] = [0, 1, 2, 255, 256, 257]
+    lens[:6] = [0, 1, 2, 255, 256, min(8193, ld)]
     draft = rng.integers(0, alphabet, (B, K)).astype(np.int32)
     acc = rng.integers(0, K + 1, B).astype(np.int32)
     bonus = rng.integers(0, alphabet, B).astype(np.int32)
