@@ -161,13 +161,14 @@ def main():
     RB = 64
     hist = torch.zeros((K1, RB + 1), dtype=torch.int32, device=dev)
     rank = torch.zeros(B, dtype=torch.int32, device=dev)
-    ks, hits = [], []
+    ks, hits, aprob = [], [], []
     for i in range(min(n, 64)):
         step(args.warmup + i)
         zq_i = bufs[(args.warmup + i) % nbuf][1]
         ssd.ssd_bonus_rank(shape, zq_i, outb["accept_len"], outb["bonus"], RB, rank, hist, ws=ws)
         ks.append(outb["accept_len"].cpu().numpy().copy())
         hits.append(outb["hit"].cpu().numpy().copy())
+        aprob.append(float(outb["accept_prob"].double().mean().item()))
     ks = np.stack(ks)
     hits = np.stack(hits)
     h_np = hist.cpu().numpy()
@@ -237,6 +238,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, bufs[0], T, C, F, args.cpu_seconds)
 
+    traffic = measured_traffic()
     label = "%s: B=%d K=%d V=%d %s logits, T=%g, B_f=%d, r=%g, C=%g" % (
         args.workload, B, K, V, w.dtype, T, w.Bf, w.r, C)
     rec = {
@@ -269,10 +271,12 @@ def main():
             "pass1_frac_of_copy": round(pass1_gbps / copy_gbps, 4),
             "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
             "mean_accept_len": round(float(ks.mean()), 3),
+            "mean_sum_min_p_qprime": round(float(np.mean(aprob)), 4),
             "hit_rate": round(float(hits.mean()), 4),
             "hit_rate_from_rank_hist": round(covered / max(total, 1), 4),
             "fanout_optimized": F_opt,
             "predicted_hit_rate_optimized": round(hits_opt / max(total, 1), 4),
+            "pass1_counter_GBps": (round(traffic / (pass1_avg_ms * 1e-3) / 1e9, 1) if traffic else None),
             "bonus_rank_us": round(rank_us, 2),
             "bonus_rank_GBps": round(rank_bytes / (rank_us * 1e-6) / 1e9, 1),
             "ngram_fallback_us": round(ngram_us, 2),
@@ -287,7 +291,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(pass1_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(),
+            "traffic": traffic,
             "kernel": "pass1_kernel (vocabulary pass over all 2*B*(K+1) rows)",
             "bytes_per_launch": int(pass1_bytes),
         },
@@ -341,11 +345,17 @@ def cpu_baseline(w, buf, T, C, F, seconds):
     ids, mass = oracle.build_cache(zq_np, T, Fa)
     Z, _ = oracle.saguaro(zq_np, T, Fa, ids, mass, C)
     draft, _ = oracle.draft_sample(zq_np, T, Fa, ids, Z, C, w.seed, 0)
+    _, gap = oracle.fanout(w.K, w.Bf, w.r)
     threads = oracle.num_threads()
     rounds = 0
+    exc = {name: 0 for name in ("E1", "E2", "E3", "E4", "E5")}
+    bits = {"E1": oracle.E1_ACCEPT_TIE, "E2": oracle.E2_CDF_TIE, "E3": oracle.E3_DEGENERATE_RESIDUAL,
+            "E4": oracle.E4_FANOUT_TIE, "E5": oracle.E5_TINY_PROB}
     t0 = time.perf_counter()
     while True:
-        oracle.round_(zp_np, zq_np, T, Fa, C, draft, w.seed, rounds, w.fallback_uniform)
+        o = oracle.round_(zp_np, zq_np, T, Fa, C, draft, w.seed, rounds, w.fallback_uniform, gap)
+        for name, bit in bits.items():
+            exc[name] += int(((o.exc & bit) != 0).sum())
         rounds += 1
         el = time.perf_counter() - t0
         if el >= seconds or rounds >= 50:
@@ -367,7 +377,8 @@ def cpu_baseline(w, buf, T, C, F, seconds):
                 rounds, w.B),
             "cpu_model": cpu_model(),
             "value_1_thread": round(one, 5),
-            "sample_1_thread": "one round of the first %d sequences, scaled to B=%d" % (nb, w.B)}
+            "sample_1_thread": "one round of the first %d sequences, scaled to B=%d" % (nb, w.B),
+            "oracle_exception_rows": dict(exc, rows=rounds * w.B)}
 
 
 def cpu_model():
