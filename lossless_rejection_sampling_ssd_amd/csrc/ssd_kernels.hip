@@ -877,8 +877,10 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
 // Z = 1 - (1 - C) M and the lossless test of draft token d_i.  For rows of at most 64
 // tiles the tile partials, the first 2 F_i + 2 candidate slots of every tile and the
 // logits at d_i are requested together.
+// Three waves per SIMD (at most 168 VGPRs; unbounded it takes 170 and two), so that the
+// 2,560 waves of a B=512 K=4 round are resident at once.
 template <int DT, bool DEVRNG>
-__global__ __launch_bounds__(kWave) void finalize_pos_kernel(const SeqFinal f) {
+__global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f) {
     __shared__ TopfScratch sc;
     const int lane = threadIdx.x;
     const int K = f.K, K1 = K + 1, nt = f.nt;
