@@ -190,3 +190,14 @@ def test_binding_refuses_host_tensors(ssd):
         ssd.ssd_softmax(ssd.shape_of(z, 1.0), z, torch.zeros(2), torch.zeros(2))
     with pytest.raises(TypeError):
         ssd.shape_of(torch.zeros(1, 2, 8, dtype=torch.float16), 1.0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says why,
+    before importing torch or touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
