@@ -19,9 +19,11 @@
  *    the last draft token.  fp32 or bf16 (bf16 is widened to fp32 in registers).
  *    Logits must be finite or -inf; a row needs at least one finite value.
  *    Rows are read as 16-byte vectors when the logits base is 16-byte aligned and
- *    ld * element size is a multiple of 16; otherwise element by element, which at
- *    B=64 K=8 V=128257 bf16 takes 2.2x as long per round.  With an odd vocabulary,
- *    pad the row stride (ld) to a multiple of 8 (bf16) or 4 (fp32) elements.
+ *    ld * element size is a multiple of 16; other rows as aligned 16-byte blocks
+ *    shifted into place (the allocation itself must be 16-byte aligned, as hipMalloc's
+ *    are), which at B=64 K=8 V=128257 bf16 takes 1.2x as long per round.  With an odd
+ *    vocabulary, pad the row stride (ld) to a multiple of 8 (bf16) or 4 (fp32)
+ *    elements for the full rate.
  *  - Every pointer except those named *_host is device memory owned by the caller.
  *    The library allocates nothing, keeps no state between calls and never
  *    synchronises: every call enqueues its kernels on `stream` (a hipStream_t; NULL

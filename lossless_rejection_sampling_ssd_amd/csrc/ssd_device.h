@@ -80,6 +80,21 @@ __device__ __forceinline__ u32x4 load_raw_elems(const char* row, int64_t e0, int
     v.w = w[3];
     return v;
 }
+// Bytes [m, m + 16) of the 32 bytes lo ++ hi (little-endian dwords; m in [0, 15]).
+__device__ __forceinline__ u32x4 funnel16(u32x4 lo, u32x4 hi, int m) {
+    // words wq .. wq + 4 (wq = m / 4) by a two-step rotation, all in registers
+    const bool by2 = (m & 8) != 0, by1 = (m & 4) != 0;
+    const uint32_t e0 = by2 ? lo.z : lo.x, e1 = by2 ? lo.w : lo.y, e2 = by2 ? hi.x : lo.z;
+    const uint32_t e3 = by2 ? hi.y : lo.w, e4 = by2 ? hi.z : hi.x, e5 = by2 ? hi.w : hi.y;
+    const uint32_t w[5] = {by1 ? e1 : e0, by1 ? e2 : e1, by1 ? e3 : e2, by1 ? e4 : e3, by1 ? e5 : e4};
+    u32x4 r;
+    r.x = __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)(m & 3));
+    r.y = __builtin_amdgcn_alignbyte(w[2], w[1], (uint32_t)(m & 3));
+    r.z = __builtin_amdgcn_alignbyte(w[3], w[2], (uint32_t)(m & 3));
+    r.w = __builtin_amdgcn_alignbyte(w[4], w[3], (uint32_t)(m & 3));
+    return r;
+}
+
 template <int DT>
 __device__ __forceinline__ void unpack_vec(u32x4 v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -146,9 +161,49 @@ __device__ __forceinline__ void load_tile(const char* row, int64_t t0, int V, in
             }
         }
     } else {
+        // Rows that do not start on a 16-byte boundary.  A vector's bytes start m =
+        // row mod 16 bytes into an aligned 16-byte block (the same m for every vector
+        // of the row, as vectors are 16 bytes apart), so it is two aligned blocks and a
+        // funnel shift by m.  The first load starts at most 15 bytes before the vector,
+        // never below the 16-byte-aligned allocation; a tile takes this path only when
+        // its last vector's second load ends inside the row's own data (then every
+        // vector's does), the row's last tile loads element by element.
+        constexpr int ES = ElemTraits<DT>::kBytes;
+        const uintptr_t rb = reinterpret_cast<uintptr_t>(row);
+        const int m = (int)(rb & 15u);
+        const uintptr_t row_end = rb + (uintptr_t)V * ES;
+        const int64_t e_last = t0 + (int64_t)(NV * kWave - 1) * N;
+        const uintptr_t a_last = (rb + (uintptr_t)(e_last * ES)) & ~(uintptr_t)15;
+        if (e_last + N <= V && a_last + 32 <= row_end) {  // uniform over the wave
+            // One aligned block per vector; a vector's second block is the first block
+            // of the next lane (lane 63: of lane 0 in the next vector, and after the
+            // tile's last vector one more block that lane 63 loads itself).
+            u32x4 lo[NV];
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
-            raw[j] = load_raw_elems<DT>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
+            for (int j = 0; j < NV; ++j) {
+                const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+                const uintptr_t a0 = (rb + (uintptr_t)(e0 * ES)) & ~(uintptr_t)15;
+                lo[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a0));
+            }
+            u32x4 tail = lo[NV - 1];
+            if (lane == kWave - 1) tail = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a_last + 16));
+            const int src = ((lane + 1) & (kWave - 1)) * 4;  // ds_bpermute byte address
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const u32x4 give = (j + 1 < NV && lane == 0) ? lo[j + 1 < NV ? j + 1 : j] : lo[j];
+                u32x4 hi;
+                hi.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)give.x);
+                hi.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)give.y);
+                hi.z = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)give.z);
+                hi.w = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)give.w);
+                if (j == NV - 1 && lane == kWave - 1) hi = tail;
+                raw[j] = funnel16(lo[j], hi, m);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                raw[j] = load_raw_elems<DT>(row, t0 + (int64_t)(j * kWave + lane) * N, V);
+        }
     }
 }
 

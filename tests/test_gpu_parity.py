@@ -597,3 +597,41 @@ def test_round_random_configs(i):
         if k == "cache_ids":
             a, b = a[:, :Bf], b[:, :Bf]
         assert np.array_equal(a, b), (label, k)
+
+
+UNALIGNED_CASES = [
+    # (label, dtype, B, K, V, base offset in elements): rows that do not start on a
+    # 16-byte boundary are read as two aligned vectors and a byte shift
+    ("odd vocabulary bf16", "bf16", 4, 3, 50257, 0),
+    ("odd vocabulary f32", "f32", 3, 2, 50257, 0),
+    ("shifted base bf16", "bf16", 3, 2, 128256, 1),
+    ("shifted base f32", "f32", 2, 3, 40000, 3),
+]
+
+
+@pytest.mark.parametrize("case", UNALIGNED_CASES, ids=lambda c: c[0])
+def test_round_unaligned_rows(case):
+    """The fused round on rows whose start is not 16-byte aligned (an odd row stride, or
+    a base pointer one or three elements into an allocation) against the oracle."""
+    label, dtype, B, K, V, off = case
+    _case("unaligned " + label)
+    zq, zp = _rand(B, K, V, dtype, sum(map(ord, label)), 2.0, 0.8)
+    F = [6, 4, 2, 1][:K + 1]
+    while len(F) < K + 1:
+        F.append(1)
+    T, C, seed, rnd = 1.0, 0.5, 0xA11 + B, 4
+    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
+    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
+    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, 1)
+
+    def dev(z):
+        if off == 0:
+            return z.cuda()
+        flat = torch.empty(z.numel() + off, dtype=z.dtype, device="cuda")
+        flat[:off] = float("nan")
+        flat[off:] = z.reshape(-1).cuda()
+        return flat[off:].view(z.shape)
+
+    zpd, zqd = dev(zp), dev(zq)
+    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, 1)
+    compare_round(g, o, K, sum(F), label=label)
