@@ -556,8 +556,9 @@ def test_round_masked_vocabulary(case):
 
 def _random_round_config(i):
     """Seeded random configuration i: dtype, shape, row padding, temperature, an
-    arbitrary fan-out (any split of B_f with 0 <= F_k <= 64, not only geometric), C
-    and the fallback mode."""
+    arbitrary fan-out (any split of B_f with 0 <= F_k <= 64, not only geometric), C,
+    the fallback mode and, for about a quarter of them, a fraction of ids masked
+    (-inf) in both models."""
     rng = np.random.default_rng(0xC0FFEE + i)
     dtype = "bf16" if rng.random() < 0.6 else "f32"
     B = int(rng.integers(1, 9))
@@ -571,18 +572,26 @@ def _random_round_config(i):
     fb = int(rng.integers(0, 2))
     scale = float(rng.uniform(0.5, 4.0))
     noise = float(rng.uniform(0.1, 1.5))
-    return dtype, B, K, V, pad, T, F, C, fb, scale, noise
+    mask = float(rng.uniform(0.1, 0.6)) if rng.random() < 0.25 else 0.0
+    return dtype, B, K, V, pad, T, F, C, fb, scale, noise, mask
 
 
-@pytest.mark.parametrize("i", range(48))
+@pytest.mark.parametrize("i", range(96))
 def test_round_random_configs(i):
     """The fused round against the oracle (and against itself chained through the six
-    separate calls) over 48 seeded random configurations, row strides above V
-    included."""
-    dtype, B, K, V, pad, T, F, C, fb, scale, noise = _random_round_config(i)
-    label = "random %d: %s B=%d K=%d V=%d pad=%d T=%g F=%s C=%.3f fb=%d" % (i, dtype, B, K, V, pad, T, F, C, fb)
+    separate calls) over 96 seeded random configurations, row strides above V and
+    masked vocabularies included."""
+    dtype, B, K, V, pad, T, F, C, fb, scale, noise, mask = _random_round_config(i)
+    label = "random %d: %s B=%d K=%d V=%d pad=%d T=%g F=%s C=%.3f fb=%d mask=%.2f" % (
+        i, dtype, B, K, V, pad, T, F, C, fb, mask)
     _case(label)
     zq, zp = _rand(B, K, V, dtype, 0xAB00 + i, scale, noise, ld=V + pad if pad else None)
+    if mask > 0:
+        g = torch.Generator().manual_seed(0xAB00 + i)
+        m = torch.rand((B, K + 1, V), generator=g) < mask
+        m[:, :, 0] = False  # every row keeps a finite id
+        zq[m] = float("-inf")
+        zp[m] = float("-inf")
     seed, rnd = 0x5EED + i, 100 + i
     zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
     Fa = np.array(F, np.int32)
