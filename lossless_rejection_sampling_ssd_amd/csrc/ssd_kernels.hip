@@ -554,39 +554,56 @@ __device__ __forceinline__ DraftProbe probe_draft(const int32_t* draft, const ch
 
 // Lossless test of one draft token d ~ q' against the target p: accepted when
 // u < p(d) / q'(d) with q'(d) = q(d) (C if d is cached) / Z; at T = 0 accepted when d
-// is the target argmax.  *ratio gets p/q' (0 when not testable), *err the error bits.
-__device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp, double sp, int argp, float mq,
-                                           double sq, double Zi, bool in_cache, float C, float c, int greedy,
-                                           double* ratio_out, int* err_out) {
-    const int d = pr.d;
-    int err = 0;
-    bool ok = true;
-    double ratio = 0.0;
-    if (d < 0 || d >= V) {
-        err |= kErrTokenRange;
-        ok = false;
+// is the target argmax.  Two steps, so that the exponentials (which need only the row
+// statistics) can run before the cache selection that gives Z and the membership.
+struct DraftTerms {
+    double p, q;  // p(d), q(d) in fp64 (T > 0)
+    int err;
+    bool ok;
+};
+__device__ __forceinline__ DraftTerms draft_terms(const DraftProbe& pr, int V, float mp, double sp, float mq,
+                                                  double sq, float c, int greedy) {
+    DraftTerms t{0.0, 0.0, 0, true};
+    if (pr.d < 0 || pr.d >= V) {
+        t.err |= kErrTokenRange;
+        t.ok = false;
+    } else if (!greedy) {
+        // one element per test: both probabilities in fp64 from the exact exponents
+        // (z c - o), so that a tiny p or q' does not underflow as an fp32 term would
+        const RowNorm np = row_norm(mp, sp, c), nq = row_norm(mq, sq, c);
+        t.p = exp2((double)pr.zp * (double)c - (double)np.o) * np.inv;
+        t.q = exp2((double)pr.zq * (double)c - (double)nq.o) * nq.inv;
     }
+    return t;
+}
+// *ratio gets p/q' (0 when not testable), *err the error bits.
+__device__ __forceinline__ bool draft_decide(const DraftProbe& pr, const DraftTerms& t, int argp, double Zi,
+                                             bool in_cache, float C, int greedy, double* ratio_out, int* err_out) {
+    int err = t.err;
+    bool ok = t.ok;
+    double ratio = 0.0;
     if (ok) {
         if (greedy) {
-            ratio = (d == argp) ? 1.0 : 0.0;
+            ratio = (pr.d == argp) ? 1.0 : 0.0;
         } else {
-            // one element per test: both probabilities in fp64 from the exact exponents
-            // (z c - o), so that a tiny p or q' does not underflow as an fp32 term would
-            const RowNorm np = row_norm(mp, sp, c), nq = row_norm(mq, sq, c);
-            const double p = exp2((double)pr.zp * (double)c - (double)np.o) * np.inv;
-            const double q = exp2((double)pr.zq * (double)c - (double)nq.o) * nq.inv;
-            const double qp = q * (in_cache ? (double)C : 1.0) / Zi;
+            const double qp = t.q * (in_cache ? (double)C : 1.0) / Zi;
             if (!(qp > 0.0)) {
                 err |= kErrQprimeZero;
                 ok = false;
             } else {
-                ratio = p / qp;
+                ratio = t.p / qp;
             }
         }
     }
     *ratio_out = ratio;
     *err_out = err;
     return ok && (greedy ? ratio == 1.0 : (double)pr.u < ratio);
+}
+__device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp, double sp, int argp, float mq,
+                                           double sq, double Zi, bool in_cache, float C, float c, int greedy,
+                                           double* ratio_out, int* err_out) {
+    return draft_decide(pr, draft_terms(pr, V, mp, sp, mq, sq, c, greedy), argp, Zi, in_cache, C, greedy, ratio_out,
+                        err_out);
 }
 
 // ============================================================================ pass 1
@@ -928,6 +945,8 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     }
     sq = f.greedy ? 1.0 : std_sum(mq, sq, f.c);
     sp = f.greedy ? 1.0 : std_sum(mp, sp, f.c);
+    // the draft test's exponentials need only the statistics: before the cache select
+    const DraftTerms dt = i < K ? draft_terms(pr, f.V, mp, sp, mq, sq, f.c, f.greedy) : DraftTerms{0.0, 0.0, 0, false};
     if (lane == 0) {
         f.q_max[r] = mq;
         f.q_sum[r] = sq;
@@ -971,7 +990,7 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
         const bool in_cache = __ballot(my_id >= 0 && my_id == pr.d) != 0ull;
         double ratio;
         int err;
-        const bool acc = test_draft(pr, f.V, mp, sp, ap, mq, sq, Z, in_cache, f.C, f.c, f.greedy, &ratio, &err);
+        const bool acc = draft_decide(pr, dt, ap, Z, in_cache, f.C, f.greedy, &ratio, &err);
         if (lane == 0) {
             f.vflag[(int64_t)b * K + i] = (acc ? 1 : 0) | (err << 1);
             if (f.accept_prob) f.accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
