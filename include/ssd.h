@@ -143,8 +143,10 @@ ssd_status ssd_saguaro_reweight(const ssd_shape* shape, const double* cache_mass
  * 4; [nl] section 2): for i = 0..K-1 in order, ratio_i = p_i(d_i) / q'_i(d_i) and
  * draft token d_i is accepted iff U(seed, round, b, i, ACCEPT) < ratio_i; the
  * accepted length k is the first rejected position, or K.  At T = 0, d_i is
- * accepted iff d_i = argmax p_i (p_argmax required).  accept_len [B] int32;
- * accept_prob (nullable [B, K] fp32) = min(1, ratio_i) for every i. */
+ * accepted iff d_i = argmax p_i (p_argmax required).  cache_ids is required whenever
+ * Bf > 0, at every temperature (the membership of d_i in S_i is read from it).
+ * accept_len [B] int32; accept_prob (nullable [B, K] fp32) = min(1, ratio_i) for
+ * every i. */
 ssd_status ssd_verify(const ssd_shape* shape, const void* p_logits, const void* q_logits,
                       const int32_t* draft, const float* p_max, const double* p_sum,
                       const int32_t* p_argmax, const float* q_max, const double* q_sum,
@@ -154,8 +156,8 @@ ssd_status ssd_verify(const ssd_shape* shape, const void* p_logits, const void* 
 
 /* ssd_residual_sample -- the bonus token ([zh] section 2 flow step 2 and Challenge 2:
  * the bonus comes from the residual distribution; [nl] section 3 B).  With
- * k = accept_len[b]:  k < K: w(x) = max(p_k(x) - q'_k(x), 0) (w = p_k if that sums to
- * 0 in fp32);  k = K: w = p_K.  bonus[b] = the smallest id whose running sum of w
+ * k = accept_len[b]:  k < K: w(x) = max(p_k(x) - q'_k(x), 0) (w = p_k if the fp64 sum of
+ * these weights is not above 0, which only rounding can cause);  k = K: w = p_K.  bonus[b] = the smallest id whose running sum of w
  * exceeds u * sum(w), u = U(seed, round, b, k, BONUS).  At T = 0 the bonus is
  * argmax p_k (p_argmax required).  resid_mass (nullable [B], fp64) receives sum(w).
  * The running sums that locate the bonus are kept in fp64. */

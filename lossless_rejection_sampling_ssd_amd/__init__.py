@@ -169,38 +169,53 @@ def _logit_ptr(t: torch.Tensor, name: str):
 
 class Workspace:
     """Caller-owned, zero-initialised device workspace (torch memory) for the calls
-    that need one.  Grows on demand; reuse one per stream."""
+    that need one.  Grows on demand.  Calls that overlap in time must not share one:
+    use one per stream (the calls without ``ws`` do, keyed by device and stream)."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf: Optional[torch.Tensor] = None
+        self._stream = None  # stream the buffer was allocated on
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, stream=None):
+        s = torch.cuda.current_stream() if stream is None else stream
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 1) + 256, dtype=torch.uint8,
-                                   device=self.device or torch.cuda.current_device())
+            old = self.buf
+            if old is not None and self._stream is not None and s != self._stream:
+                # kernels queued on the stream that last used it may still read the old
+                # block: the allocator must not hand it out before they finish
+                old.record_stream(s)
+            with torch.cuda.stream(s):
+                self.buf = torch.zeros(max(nbytes, 1) + 256, dtype=torch.uint8,
+                                       device=self.device if self.device is not None else s.device)
+            self._stream = s
+        elif self._stream is not None and s != self._stream:
+            self.buf.record_stream(s)  # used on another stream than it was allocated on
         base = self.buf.data_ptr()
         off = (-base) % 256
         return ctypes.c_void_p(base + off), self.buf.numel() - off
 
 
-def _ws(ws: Optional[Workspace], shape: ssd_shape, Bf: int):
+def _ws(ws: Optional[Workspace], shape: ssd_shape, Bf: int, stream=None):
     need = _lib.ssd_workspace_bytes(ctypes.byref(shape), int(Bf))
     if need == 0:
         raise SSDError(SSD_ERR_ARG, "ssd_workspace_bytes")
     if ws is None:
-        ws = _default_ws()
-    return ws.get(need)
+        ws = _default_ws(stream)
+    return ws.get(need, stream)
 
 
 _default = {}
 
 
-def _default_ws() -> Workspace:
-    dev = torch.cuda.current_device()
-    if dev not in _default:
-        _default[dev] = Workspace(dev)
-    return _default[dev]
+def _default_ws(stream=None) -> Workspace:
+    """The workspace of the calls given no ``ws``: one per (device, stream), so that
+    calls on different streams never share scratch."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    key = (s.device.index, s.cuda_stream)
+    if key not in _default:
+        _default[key] = Workspace(s.device)
+    return _default[key]
 
 
 # ---------------------------------------------------------------------------- entry points
@@ -218,13 +233,13 @@ def ssd_softmax(shape, logits, row_max, row_sum, row_argmax=None, probs=None, ws
     args = (_logit_ptr(logits, "logits"), _ptr(row_max, torch.float32, "row_max"),
             _ptr(row_sum, torch.float64, "row_sum"), _ptr(row_argmax, torch.int32, "row_argmax"),
             _ptr(probs, torch.float32, "probs"))
-    w, nb = _ws(ws, shape, 1)
+    w, nb = _ws(ws, shape, 1, stream)
     _check(_lib.ssd_softmax(ctypes.byref(shape), *args, w, nb, _stream(stream)), "ssd_softmax")
 
 
 def ssd_build_cache(shape, q_logits, q_max, q_sum, F, cache_ids, cache_mass, ws=None, stream=None):
     Bf = int(sum(F))
-    w, nb = _ws(ws, shape, Bf)
+    w, nb = _ws(ws, shape, Bf, stream)
     _check(_lib.ssd_build_cache(ctypes.byref(shape), _logit_ptr(q_logits, "q_logits"), _ptr(q_max, torch.float32),
                                 _ptr(q_sum, torch.float64), _host_F(F), Bf, _ptr(cache_ids, torch.int32, "cache_ids"),
                                 _ptr(cache_mass, torch.float64, "cache_mass"), w, nb, _stream(stream)),
@@ -236,7 +251,7 @@ def ssd_saguaro_reweight(shape, cache_mass, C, Z, q_logits=None, q_max=None, q_s
     Bf = int(sum(F)) if F is not None else 0
     w, nb = (None, 0)
     if draft is not None:
-        w, nb = _ws(ws, shape, Bf)
+        w, nb = _ws(ws, shape, Bf, stream)
     _check(_lib.ssd_saguaro_reweight(ctypes.byref(shape), _ptr(cache_mass, torch.float64), float(C),
                                      _ptr(Z, torch.float64, "Z"),
                                      _logit_ptr(q_logits, "q_logits") if q_logits is not None else None,
@@ -262,7 +277,7 @@ def ssd_verify(shape, p_logits, q_logits, draft, p_max, p_sum, p_argmax, q_max, 
 def ssd_residual_sample(shape, p_logits, q_logits, p_max, p_sum, p_argmax, q_max, q_sum, F, cache_ids, Z, C,
                         accept_len, seed, round_, bonus, resid_mass=None, dev_err=None, ws=None, stream=None):
     Bf = int(sum(F))
-    w, nb = _ws(ws, shape, Bf)
+    w, nb = _ws(ws, shape, Bf, stream)
     _check(_lib.ssd_residual_sample(ctypes.byref(shape), _logit_ptr(p_logits, "p_logits"),
                                     _logit_ptr(q_logits, "q_logits"), _ptr(p_max, torch.float32),
                                     _ptr(p_sum, torch.float64), _ptr(p_argmax, torch.int32),
@@ -317,7 +332,7 @@ def ssd_bonus_rank(shape, q_logits, accept_len, bonus, R, rank_out=None, rank_hi
     _check(_lib.ssd_bonus_rank(ctypes.byref(shape), _logit_ptr(q_logits, "q_logits"),
                                _ptr(accept_len, torch.int32, "accept_len"), _ptr(bonus, torch.int32, "bonus"),
                                int(R), _ptr(rank_out, torch.int32, "rank_out"),
-                               _ptr(rank_hist, torch.int32, "rank_hist"), *_ws(ws, shape, 1), _stream(stream)),
+                               _ptr(rank_hist, torch.int32, "rank_hist"), *_ws(ws, shape, 1, stream), _stream(stream)),
            "ssd_bonus_rank")
 
 
@@ -378,7 +393,7 @@ def make_round_out(**tensors) -> ssd_round_out:
 def ssd_round(shape, p_logits, q_logits, draft, F, C, seed, round_, fallback, out: ssd_round_out,
               events: Optional[ssd_round_events] = None, ws=None, stream=None):
     Bf = int(sum(F))
-    w, nb = _ws(ws, shape, Bf)
+    w, nb = _ws(ws, shape, Bf, stream)
     _check(_lib.ssd_round(ctypes.byref(shape), _logit_ptr(p_logits, "p_logits"), _logit_ptr(q_logits, "q_logits"),
                           _ptr(draft, torch.int32, "draft"), _host_F(F), Bf, float(C), ssd_rng(seed, round_),
                           int(fallback), ctypes.byref(out), ctypes.byref(events) if events is not None else None,
@@ -392,7 +407,7 @@ def ssd_round_devrng(shape, p_logits, q_logits, draft, F, C, seed, round_dev, fa
     if round_dev.numel() != 1:
         raise ValueError("round_dev must hold one counter")
     Bf = int(sum(F))
-    w, nb = _ws(ws, shape, Bf)
+    w, nb = _ws(ws, shape, Bf, stream)
     _check(_lib.ssd_round_devrng(ctypes.byref(shape), _logit_ptr(p_logits, "p_logits"),
                                  _logit_ptr(q_logits, "q_logits"), _ptr(draft, torch.int32, "draft"), _host_F(F), Bf,
                                  float(C), int(seed), _ptr(round_dev, torch.int64, "round_dev"), int(fallback),

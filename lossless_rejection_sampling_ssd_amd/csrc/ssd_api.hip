@@ -196,6 +196,7 @@ ssd_status ssd_softmax(const ssd_shape* s, const void* logits, float* row_max, d
     if ((st = check_ws(s, 1, ws, ws_bytes, &L)) != SSD_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
     const int K1 = s->K + 1, R = s->B * K1;
+    if (probs && R > 65535) return SSD_ERR_UNSUPPORTED;  // dense output: one grid row per logit row
     const int greedy = s->T == 0.f;
     ssd::Pass1Args a{};
     a.logits[0] = (const char*)logits;
@@ -218,7 +219,6 @@ ssd_status ssd_softmax(const ssd_shape* s, const void* logits, float* row_max, d
     e = ssd::launch_combine_stats(a, row_max, row_sum, argp, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_softmax combine");
     if (probs) {
-        if (R > 65535) return SSD_ERR_UNSUPPORTED;  // one grid row per logit row
         e = ssd::launch_probs(s->dtype, (const char*)logits, s->B, K1, s->V, a.ld_bytes, row_max, row_sum, argp, a.c,
                               greedy, nullptr, nullptr, nullptr, 0, nullptr, 1.f, probs, hs);
         if (e != hipSuccess) return fail_hip(e, "ssd_softmax probs");
@@ -277,12 +277,12 @@ ssd_status ssd_saguaro_reweight(const ssd_shape* s, const double* cache_mass, fl
         if (greedy && !q_argmax) return SSD_ERR_ARG;
         if (draft && (st = check_ws(s, Bf, ws, ws_bytes, &L)) != SSD_OK) return st;
     }
+    if (q_prime && R > 65535) return SSD_ERR_UNSUPPORTED;  // dense output: one grid row per logit row
     hipStream_t hs = (hipStream_t)stream;
     hipError_t e = ssd::launch_saguaro_z(cache_mass, R, C, Z, hs);
     if (e != hipSuccess) return fail_hip(e, "ssd_saguaro_reweight Z");
     const float c = temp_scale(s->T);
     if (q_prime) {
-        if (R > 65535) return SSD_ERR_UNSUPPORTED;  // one grid row per logit row
         e = ssd::launch_probs(s->dtype, (const char*)q_logits, s->B, K1, s->V, ld_bytes(s), q_max, q_sum, q_argmax, c,
                               greedy, cache_ids, F_host, O, Bf, Z, C, q_prime, hs);
         if (e != hipSuccess) return fail_hip(e, "ssd_saguaro_reweight q'");
@@ -332,9 +332,10 @@ ssd_status ssd_verify(const ssd_shape* s, const void* p_logits, const void* q_lo
     if ((st = check_fanout(s, F_host, Bf, O)) != SSD_OK) return st;
     const int greedy = s->T == 0.f;
     if (!draft || !accept_len || !(C > 0.f) || !(C <= 1.f)) return SSD_ERR_ARG;
+    // the membership test of d_i reads the cached ids at every temperature
+    if (Bf > 0 && !cache_ids) return SSD_ERR_ARG;
     if (greedy && !p_argmax) return SSD_ERR_ARG;
-    if (!greedy && (!p_logits || !q_logits || !p_max || !p_sum || !q_max || !q_sum || !Z || (Bf > 0 && !cache_ids)))
-        return SSD_ERR_ARG;
+    if (!greedy && (!p_logits || !q_logits || !p_max || !p_sum || !q_max || !q_sum || !Z)) return SSD_ERR_ARG;
     hipError_t e = ssd::launch_verify(s->dtype, (const char*)p_logits, (const char*)q_logits, s->B, s->K, s->V,
                                       ld_bytes(s), draft, p_max, p_sum, p_argmax, q_max, q_sum, F_host, O, Bf,
                                       cache_ids, Z, C, temp_scale(s->T), greedy, rng.seed, rng.round, accept_len,

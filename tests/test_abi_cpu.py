@@ -124,6 +124,15 @@ def test_cache_and_round_validation(ssd):
     s0 = _shape(ssd, K=3, V=100, T=0.0)
     assert L.ssd_verify(ctypes.byref(s0), BAD, BAD, BAD, BAD, BAD, None, BAD, BAD, good_F, 8, BAD, BAD, 0.5,
                         ssd.ssd_rng(0, 0), BAD, None, None, None) == ssd.SSD_ERR_ARG
+    # the cached ids are read at every temperature: required whenever Bf > 0, greedy too
+    for sv in (s0, s):
+        assert L.ssd_verify(ctypes.byref(sv), BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, good_F, 8, None, BAD, 0.5,
+                            ssd.ssd_rng(0, 0), BAD, None, None, None) == ssd.SSD_ERR_ARG
+    # dense outputs above 65535 rows are refused before anything is launched
+    big = _shape(ssd, B=20000, K=3, V=100)
+    assert L.ssd_softmax(ctypes.byref(big), BAD, BAD, BAD, None, BAD, ws, 1 << 40, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert L.ssd_saguaro_reweight(ctypes.byref(big), BAD, 0.5, BAD, BAD, BAD, BAD, None, good_F, 8, BAD, BAD,
+                                  ssd.ssd_rng(0, 0), None, None, 0, None) == ssd.SSD_ERR_UNSUPPORTED
     # residual: missing outputs, small workspace
     assert L.ssd_residual_sample(ctypes.byref(s), BAD, BAD, BAD, BAD, BAD, BAD, BAD, good_F, 8, BAD, BAD, 0.5, BAD,
                                  ssd.ssd_rng(0, 0), None, None, None, ws, 1 << 30, None) == ssd.SSD_ERR_ARG
