@@ -51,12 +51,59 @@ def parse():
     ap.add_argument("--C", type=float, default=None)
     ap.add_argument("--target-sigma", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="time the vocabulary pass with HIP events on every N-th timed round")
+    ap.add_argument("--event-every", type=int, default=0,
+                    help="time the vocabulary pass with HIP events on every N-th timed round "
+                         "(0: max(1, steps // 16), so that at least 16 launches are timed)")
+    ap.add_argument("--stream-passes", type=int, default=32,
+                    help="read-only passes over the rotating buffers for the same-run read ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="3 copies of 1 GiB instead of 5 (the count the byte-counter calibration expects)")
     return ap.parse_args()
+
+
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence: recording one writes a
+    timestamp without the system-scope cache writeback and invalidation a default
+    event performs, so timing a kernel between two of them barely disturbs the
+    kernels around it.  Loaded from the HIP runtime torch has already loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        self.made.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
 
 
 def main():
@@ -118,40 +165,58 @@ def main():
         zp, zq, d = bufs[i % nbuf]
         ssd.ssd_round(shape, zp, zq, d, F, C, w.seed, i, fallback, outb.out, events=events, ws=ws)
 
+    hev = HipEvents()
+    cur = torch.cuda.current_stream()
+    st = cur.cuda_stream
+
+    # ---- the same-run read ceiling: read-only passes over the same rotating buffers,
+    # in pass 1's access shape, each pass the 2 B (K+1) V s bytes of one round
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ns = max(1, args.stream_passes)
+    s0, s1 = hev.create(), hev.create()
+    for j in range(2):  # untimed: first touch
+        ssd.ssd_stream_read(bufs[j % nbuf][0], sink)
+        ssd.ssd_stream_read(bufs[j % nbuf][1], sink)
+    hev.record(s0, st)
+    for j in range(ns):
+        zp_j, zq_j, _ = bufs[j % nbuf]
+        ssd.ssd_stream_read(zp_j, sink)
+        ssd.ssd_stream_read(zq_j, sink)
+    hev.record(s1, st)
+    torch.cuda.synchronize()
+    stream_us = hev.ms(s0, s1) * 1e3 / ns
+    stream_gbps = pass1_bytes / (stream_us * 1e-6) / 1e9
+    log("read ceiling: %d passes of %d bytes, %.2f us each, %.1f GB/s" % (ns, pass1_bytes, stream_us, stream_gbps))
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K rounds; HIP events around the vocabulary pass of every
-    # --event-every-th round (an event pair on every round adds about 5 us to each round
-    # at B=64 K=8 V=128256, so sampling keeps the rounds undisturbed)
+    # ---- timed region: K rounds back to back; HIP events (no system fence) around the
+    # vocabulary pass of every --event-every-th round, at least 16 launches in all
     n = args.steps
-    every = max(1, args.event_every)
+    every = args.event_every if args.event_every > 0 else max(1, n // 16)
     sampled = list(range(0, n, every))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sampled]
-    for a, b in ev:  # create the underlying HIP events before the library records them
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    ev = [(hev.create(), hev.create()) for _ in sampled]
     evs = [None] * n
     for j, (a, b) in zip(sampled, ev):
-        evs[j] = ssd.ssd_round_events(a.cuda_event, b.cuda_event, None, None)
-    # the K rounds run back to back; events at 5 chunk boundaries give the repeat spread
+        evs[j] = ssd.ssd_round_events(a.value, b.value, None, None)
+    # events at 5 chunk boundaries give the spread between repeats
     nrep = 5 if n >= 5 else 1
     bounds = [n * j // nrep for j in range(nrep + 1)]
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+    marks = [hev.create() for _ in range(nrep + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    marks[0].record()
+    hev.record(marks[0], st)
     for j in range(nrep):
         for i in range(bounds[j], bounds[j + 1]):
             step(args.warmup + i, evs[i])
-        marks[j + 1].record()
+        hev.record(marks[j + 1], st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = marks[0].elapsed_time(marks[-1])
-    rep_us = [marks[j].elapsed_time(marks[j + 1]) * 1e3 / (bounds[j + 1] - bounds[j]) for j in range(nrep)]
-    pass1_ms = [a.elapsed_time(b) for a, b in ev]
+    total_ms = hev.ms(marks[0], marks[-1])
+    rep_us = [hev.ms(marks[j], marks[j + 1]) * 1e3 / (bounds[j + 1] - bounds[j]) for j in range(nrep)]
+    pass1_ms = [hev.ms(a, b) for a, b in ev]
     pass1_avg_ms = float(np.mean(pass1_ms))
     ms_per_step = total_ms / n
     rounds_per_s = 1000.0 / ms_per_step
@@ -252,11 +317,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",  # arithmetic: fp32 terms, fp64 sums; the logits themselves are config.logits
         "data": "synthetic",
         "config": {
             "workload": label,
             "logits": w.dtype,
+            "arithmetic": "fp32 per-element terms, fp64 normalisers and running sums",
             "fan_out": F,
             "next_draft_gather": True,
             "buffers": nbuf,
@@ -269,6 +335,12 @@ def main():
             "us_per_round_repeats": [round(x, 2) for x in rep_us],
             "copy_GBps_read_plus_write": round(copy_gbps, 1),
             "pass1_frac_of_copy": round(pass1_gbps / copy_gbps, 4),
+            "stream_read_us": round(stream_us, 2),
+            "stream_read_GBps": round(stream_gbps, 1),
+            "stream_read_frac_of_peak": round(stream_gbps / PEAK_HBM_GBPS, 4),
+            "pass1_frac_of_stream": round(pass1_gbps / stream_gbps, 4),
+            "pass1_us_min": round(min(pass1_ms) * 1e3, 2),
+            "pass1_us_median": round(float(np.median(pass1_ms)) * 1e3, 2),
             "pass2_and_gaps_us": round((ms_per_step - pass1_avg_ms) * 1e3, 2),
             "mean_accept_len": round(float(ks.mean()), 3),
             "mean_sum_min_p_qprime": round(float(np.mean(aprob)), 4),
@@ -292,11 +364,13 @@ def main():
             "unit": "GB/s",
             "frac": round(pass1_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "kernel": "pass1_kernel (vocabulary pass over all 2*B*(K+1) rows)",
+            "kernel": "pass1_kernel (vocabulary pass over all 2*B*(K+1) rows); the whole round's fraction is "
+                      "config.round_frac_of_peak",
             "bytes_per_launch": int(pass1_bytes),
         },
         "cpu_baseline": cpu,
     }
+    hev.close()
     print(json.dumps(rec), flush=True)
 
 

@@ -352,6 +352,17 @@ ssd_status ssd_fallback_choose(const ssd_fallback_model* model, int32_t B, const
 ssd_status ssd_fallback_critical_batch(const ssd_fallback_model* model, double h, int32_t b_max,
                                        int32_t* b_star_host);
 
+/* ---------------------------------------------------------------------------
+ * Measurement.  ssd_stream_read -- reads `bytes` of device memory at `buf` once, in
+ * the access shape of the vocabulary pass (each wave 8 KiB: eight non-temporal
+ * 16-byte loads per lane), and computes nothing from them but an XOR; the time it
+ * takes on the same buffers is the achievable read rate the round's streaming
+ * kernels are measured against.  `sink` (device, one uint32) is written only in the
+ * unlikely case that a wave's XOR equals a fixed constant (it exists so that the
+ * loads cannot be removed).  buf 16-byte aligned, bytes a positive multiple of 16.
+ * Not part of the round. */
+ssd_status ssd_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 const char* ssd_status_string(ssd_status s);
 
 /* Text of the last HIP error seen by this thread (empty if none). */

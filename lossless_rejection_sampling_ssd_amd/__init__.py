@@ -27,7 +27,7 @@ SSD_MAX_K, SSD_MAX_F, SSD_MAX_NGRAM = 16, 64, 16
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
             "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback",
             "ssd_round", "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose",
-            "ssd_fallback_critical_batch", "ssd_status_string", "ssd_last_error")
+            "ssd_fallback_critical_batch", "ssd_stream_read", "ssd_status_string", "ssd_last_error")
 
 
 class SSDError(RuntimeError):
@@ -92,13 +92,15 @@ def _load():
     FM = ctypes.POINTER(ssd_fallback_model)
     L.ssd_fallback_choose.argtypes = [FM, i32, _P, _P, _P, _P]
     L.ssd_fallback_critical_batch.argtypes = [FM, f64, i32, _P]
+    L.ssd_stream_read.argtypes = [_P, sz, _P, _P]
     L.ssd_status_string.argtypes = [i32]
     L.ssd_status_string.restype = ctypes.c_char_p
     L.ssd_last_error.argtypes = []
     L.ssd_last_error.restype = ctypes.c_char_p
     for name in ("ssd_fanout", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight", "ssd_verify",
                  "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
-                 "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch"):
+                 "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
+                 "ssd_stream_read"):
         getattr(L, name).restype = i32
     return L
 
@@ -369,6 +371,17 @@ def ssd_fallback_critical_batch(model: "ssd_fallback_model", h: float, b_max: in
     _check(_lib.ssd_fallback_critical_batch(ctypes.byref(model), float(h), int(b_max), ctypes.byref(b)),
            "ssd_fallback_critical_batch")
     return int(b.value)
+
+
+def ssd_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement: one read-only pass over the bytes of the contiguous device tensor
+    buf in the vocabulary pass's access shape (sink: a one-element int32 device
+    tensor the kernel almost never writes)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.ssd_stream_read(_logit_ptr(buf, "buf"), nbytes - nbytes % 16, _ptr(sink, torch.int32, "sink"),
+                                _stream(stream)), "ssd_stream_read")
 
 
 _ROUND_DTYPES = {"p_max": torch.float32, "p_sum": torch.float64, "p_argmax": torch.int32, "q_max": torch.float32,

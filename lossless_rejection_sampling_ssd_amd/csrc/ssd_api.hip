@@ -493,6 +493,13 @@ ssd_status ssd_ngram_fallback(int32_t B, int32_t K, int32_t V, const int32_t* hi
     return SSD_OK;
 }
 
+ssd_status ssd_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || (uintptr_t)buf % 16 != 0) return SSD_ERR_ARG;
+    hipError_t e = ssd::launch_stream_read(buf, (int64_t)(bytes / 16), sink, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "ssd_stream_read");
+    return SSD_OK;
+}
+
 // The fused round; round_dev (nullable) replaces rng.round by a counter the kernels read
 // from device memory when they run.
 static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,

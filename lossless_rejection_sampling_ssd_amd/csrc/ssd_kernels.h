@@ -166,6 +166,9 @@ struct RankArgs {
 };
 hipError_t launch_rank(int dtype, bool vec, const RankArgs& a, hipStream_t st);
 
+// Read-only stream over nvec 16-byte vectors (the same-run read ceiling).
+hipError_t launch_stream_read(const void* buf, int64_t nvec, uint32_t* sink, hipStream_t st);
+
 hipError_t launch_lookup(int B, int K, int V, const int* F, const int* O, int Bf, const int32_t* cache_ids,
                          const int32_t* accept_len, const int32_t* bonus, int fallback, uint64_t seed,
                          uint64_t round, uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* dev_err,

@@ -1675,6 +1675,34 @@ __global__ __launch_bounds__(kRankWaves * kWave) void rank_finish_kernel(const R
             if (h[i]) atomicAdd(&a.hist[i], h[i]);
 }
 
+// ============================================================================ read ceiling
+// Read-only stream over a buffer in pass 1's access shape: one wave per 8 KiB (each
+// lane eight non-temporal 16-byte loads, vector j of lane l at (j*64 + l)*16 bytes),
+// nothing computed but an XOR that keeps the loads alive.  Its rate on the same
+// buffers is the reference the vocabulary pass is judged against.
+__global__ __launch_bounds__(kBlock) void stream_read_kernel(const u32x4* __restrict__ buf, int64_t nvec,
+                                                             uint32_t* sink) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t v0 = w * (kVecPerLane * kWave) + lane;
+    u32x4 raw[kVecPerLane];
+    if (v0 + (int64_t)(kVecPerLane - 1) * kWave < nvec) {
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) raw[j] = __builtin_nontemporal_load(buf + v0 + j * kWave);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) {
+            const int64_t v = v0 + j * kWave;
+            raw[j] = v < nvec ? buf[v] : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    uint32_t x = 0u;
+#pragma unroll
+    for (int j = 0; j < kVecPerLane; ++j) x ^= raw[j].x ^ raw[j].y ^ raw[j].z ^ raw[j].w;
+    // a store that (almost) never happens, on a value that depends on every load
+    if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 // ============================================================================ launchers
 static FO make_fo(const int* F, const int* O, int K1) {
     FO fo;
@@ -1827,6 +1855,14 @@ hipError_t launch_rank(int dtype, bool vec, const RankArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int g2 = (int)std::min<int64_t>(((int64_t)a.B + kRankWaves - 1) / kRankWaves, 256);
     rank_finish_kernel<<<g2, kRankWaves * kWave, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, int64_t nvec, uint32_t* sink, hipStream_t st) {
+    constexpr int64_t per_block = (int64_t)kVecPerLane * kWave * kWavesPerBlock;
+    const int64_t grid = (nvec + per_block - 1) / per_block;
+    if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
+    stream_read_kernel<<<(unsigned)grid, kBlock, 0, st>>>(static_cast<const u32x4*>(buf), nvec, sink);
     return hipGetLastError();
 }
 

@@ -176,6 +176,13 @@ def test_cache_and_round_validation(ssd):
 
 
 
+def test_stream_read_validation(ssd):
+    L = ssd.lib()
+    for buf, nb, sink in ((None, 64, BAD), (BAD, 64, None), (BAD, 0, BAD), (BAD, 40, BAD),
+                          (ctypes.c_void_p(0x1008), 64, BAD)):
+        assert L.ssd_stream_read(buf, nb, sink, None) == ssd.SSD_ERR_ARG
+
+
 def test_ngram_validation(ssd):
     """n-gram fallback: sizes, n-gram range and required pointers are checked on the
     host; a missing history is allowed only for ld_hist = 0."""
