@@ -27,21 +27,19 @@ _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
 
 F32, BF16 = 0, 1
 PURPOSE_ACCEPT, PURPOSE_BONUS, PURPOSE_DRAFT, PURPOSE_FALLBACK = 0, 1, 2, 3
+BLOCK = 512  # ids per block of the two-level draw
 ERR_TOKEN_RANGE, ERR_QPRIME_ZERO, ERR_LEN_RANGE, ERR_SLOT_RANGE, ERR_HIST_RANGE = 1, 2, 4, 8, 16
 FALLBACK_NONE, FALLBACK_UNIFORM = 0, 1  # the primary speculator / uniform random tokens
 E1_ACCEPT_TIE, E2_CDF_TIE, E3_DEGENERATE_RESIDUAL, E4_FANOUT_TIE, E5_TINY_PROB = 1, 2, 4, 8, 16
 FANOUT_EPS = 1e-9
-# Half-width of the inverse-CDF near-tie band (E2) on the normalised CDF.  Bound of the
-# GPU path's CDF error from its arithmetic (per-element fp32 exp2 of an fp32 exponent,
-# fp32 partial sums over 8 terms, fp64 merges; worst case, first order):
-#   sampling from p_K or from q'      |dC| <= E|d| + s        ~ 2.2e-6
-#   sampling from max(p - q', 0)      |dC| <= (2 (E|d| + s) + z) / Z_r
-# with E|d| <= 2^-23 + ln2 2^-24 (2 log2 V + 1/2) the mean relative term error, s the
-# relative error of a row sum and z that of q' through Z.  The band is the parity
-# rule's cap of 1e-5: it covers the first kind of row, and residual rows with
-# Z_r >= ~0.5, with room to spare; smaller residual masses rely on the errors being far
-# below their worst case (their typical size is ~1e-8).
-CDF_TIE_EPS = 1e-5
+# Floor of the inverse-CDF near-tie band (E2) on the normalised CDF.  The band of
+# each draw is computed by the oracle (draw_bands in ssd_oracle.c) from the arithmetic
+# of the GPU path: this floor, plus the CDF shift between the temperature the GPU
+# path samples at (it applies T as an fp32 scale) and T, plus six standard deviations
+# of the random walk that independent per-term fp32 errors make of the running sum.
+# tests/test_cdf_error_model.py checks the band against a CPU model of that
+# arithmetic.
+CDF_TIE_EPS = 1e-8
 
 
 def build(force: bool = False) -> str:
@@ -87,6 +85,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.orc_philox4x64_10.argtypes = [P, P, P]
     L.orc_uniform.argtypes = [u64, u64, i32, i64, i64]
     L.orc_uniform.restype = dbl
+    L.orc_uniform2.argtypes = [u64, u64, i32, i64, i64]
+    L.orc_uniform2.restype = dbl
     L.orc_uniform_u32.argtypes = [u64, u64, i32, i64, i64]
     L.orc_uniform_u32.restype = ctypes.c_uint32
     L.orc_fanout.argtypes = [i32, i32, dbl, P, P]
@@ -155,6 +155,12 @@ def uniform(seed, round_, purpose, b, i) -> float:
     return lib().orc_uniform(seed, round_, purpose, b, i)
 
 
+def uniform2(seed, round_, purpose, b, i) -> float:
+    """The second uniform of a draw (Philox counter word 3 = 1): the id within the
+    block the first one picked."""
+    return lib().orc_uniform2(seed, round_, purpose, b, i)
+
+
 def uniform_u32(seed, round_, purpose, b, i) -> int:
     return lib().orc_uniform_u32(seed, round_, purpose, b, i)
 
@@ -205,19 +211,22 @@ def saguaro(zq, T: float, F, cache_ids, cache_mass, C: float, want_qprime: bool 
 
 def draft_sample(zq, T: float, F, cache_ids, Z, C: float, seed: int, round_: int, b_base: int = 0,
                  cdf_eps: float = None, want_gaps: bool = False):
-    """Harness step: draft tokens sampled from the reweighted draft law q'.  Returns
-    (draft, E2 flags) or, with want_gaps, (draft, flags, gaps)."""
+    """Harness step: draft tokens sampled from the reweighted draft law q' by the
+    two-level draw (see ``ssd_oracle.c``).  Returns (draft, E2 flags) or, with
+    want_gaps, (draft, flags, e2) with e2 [B, K, 4] = (gap of u1, band of u1, gap of u2,
+    band of u2): the distances of the two uniforms to the steps around the pick and
+    the E2 bands they were compared with."""
     code, B, K, V, ld = _logit_info(zq)
     F = np.ascontiguousarray(F, dtype=np.int32)
     cache_ids = np.ascontiguousarray(cache_ids, dtype=np.int32)
     Z = np.ascontiguousarray(Z, dtype=np.float64)
     d = np.zeros((B, K), dtype=np.int32)
     flags = np.zeros((B, K), dtype=np.uint8)
-    gaps = np.zeros((B, K))
+    e2 = np.zeros((B, K, 4))
     eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_draft_sample(B, K, V, ld, code, _base(zq), T, _ptr(F), int(F.sum()), _ptr(cache_ids),
-                           _ptr(Z), C, seed, round_, b_base, eps, _ptr(d), _ptr(flags), _ptr(gaps))
-    return (d, flags, gaps) if want_gaps else (d, flags)
+                           _ptr(Z), C, seed, round_, b_base, eps, _ptr(d), _ptr(flags), _ptr(e2))
+    return (d, flags, e2) if want_gaps else (d, flags)
 
 
 def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_, b_base: int = 0):
@@ -239,7 +248,10 @@ def verify(zp, zq, T, draft, pstats, qstats, F, cache_ids, Z, C, seed, round_, b
 
 
 def residual_sample(zp, zq, T, pstats, qstats, F, cache_ids, Z, C, accept_len, seed, round_,
-                    want_resid: bool = False, b_base: int = 0, cdf_eps: float = None):
+                    want_resid: bool = False, b_base: int = 0, cdf_eps: float = None, want_bands: bool = False):
+    """Bonus tokens by the two-level draw.  Returns (bonus, Z_r, weights or None, err,
+    exc), and with want_bands also e2 [B, 4] = (gap of u1, band of u1, gap of u2, band
+    of u2)."""
     code, B, K, V, ld = _logit_info(zp)
     F = np.ascontiguousarray(F, dtype=np.int32)
     pm, ps, pa = (np.ascontiguousarray(x) for x in pstats[:3])
@@ -252,11 +264,14 @@ def residual_sample(zp, zq, T, pstats, qstats, F, cache_ids, Z, C, accept_len, s
     resid = np.zeros((B, V)) if want_resid else None
     err = np.zeros(B, dtype=np.int32)
     exc = np.zeros(B, dtype=np.uint8)
+    e2 = np.zeros((B, 4))
     eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_residual_sample(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(pm), _ptr(ps), _ptr(pa),
                               _ptr(qm), _ptr(qs), _ptr(qa), _ptr(F), int(F.sum()), _ptr(cache_ids),
                               _ptr(Z), C, _ptr(accept_len), seed, round_, b_base, eps, _ptr(bonus), _ptr(zr),
-                              _ptr(resid), _ptr(err), _ptr(exc), None)
+                              _ptr(resid), _ptr(err), _ptr(exc), _ptr(e2))
+    if want_bands:
+        return bonus, zr, resid, err, exc, e2
     return bonus, zr, resid, err, exc
 
 
@@ -445,7 +460,7 @@ class RoundResult:
     fallback_tokens: np.ndarray
     err: np.ndarray
     exc: np.ndarray
-    cdf_gap: np.ndarray
+    e2: np.ndarray  # [B, 4]: gap and band of each of the bonus draw's two uniforms
 
 
 def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap=None,
@@ -467,7 +482,7 @@ def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap
         accept_len=np.zeros(B, np.int32), accept_prob=np.zeros((B, K)), bonus=np.zeros(B, np.int32),
         resid_mass=np.zeros(B), hit=np.zeros(B, np.uint8), slot=np.zeros(B, np.int32),
         fallback_tokens=np.zeros((B, K), np.int32), err=np.zeros(B, np.int32), exc=np.zeros(B, np.uint8),
-        cdf_gap=np.zeros(B))
+        e2=np.zeros((B, 4)))
     o = out
     eps = CDF_TIE_EPS if cdf_eps is None else cdf_eps
     lib().orc_round(B, K, V, ld, code, _base(zp), _base(zq), T, _ptr(F), Bf, C, _ptr(draft), seed,
@@ -475,7 +490,7 @@ def round_(zp, zq, T, F, C, draft, seed, round_idx, fallback_uniform, fanout_gap
                     _ptr(o.q_max), _ptr(o.q_sum), _ptr(o.q_arg), _ptr(o.cache_ids), _ptr(o.cache_mass),
                     _ptr(o.Z), _ptr(o.accept_len), _ptr(o.accept_prob), _ptr(o.bonus), _ptr(o.resid_mass),
                     _ptr(o.hit), _ptr(o.slot), _ptr(o.fallback_tokens), _ptr(o.err), _ptr(o.exc),
-                    _ptr(o.cdf_gap))
+                    _ptr(o.e2))
     if fanout_gap is not None and fanout_gap < FANOUT_EPS:
         o.exc |= E4_FANOUT_TIE
     return out

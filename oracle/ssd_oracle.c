@@ -120,23 +120,29 @@ void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint6
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* First output word for key (seed, purpose) and counter (round, b, i, 0). */
-static uint64_t philox_word(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
-    uint64_t ctr[4] = {round, (uint64_t)b, (uint64_t)i, 0};
+/* First output word for key (seed, purpose) and counter (round, b, i, w3). */
+static uint64_t philox_word(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i, uint64_t w3) {
+    uint64_t ctr[4] = {round, (uint64_t)b, (uint64_t)i, w3};
     uint64_t key[2] = {seed, (uint64_t)purpose};
     uint64_t out[4];
     orc_philox4x64_10(ctr, key, out);
     return out[0];
 }
 
-/* READING: one uniform per (sequence, position, purpose); the top 24 bits of the
- * first output word scaled by 2^-24, a value in [0, 1) that fp32 holds exactly. */
+/* READING: the uniforms of (sequence, position, purpose) are the top 24 bits of the
+ * first output word of counter (round, b, i, w) scaled by 2^-24, a value in [0, 1)
+ * that fp32 holds exactly; w = 0 gives the uniform of a test or of a draw's block,
+ * w = 1 the second uniform of a draw (the id within the block). */
 double orc_uniform(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
-    return (double)(philox_word(seed, round, purpose, b, i) >> 40) * (1.0 / 16777216.0);
+    return (double)(philox_word(seed, round, purpose, b, i, 0) >> 40) * (1.0 / 16777216.0);
+}
+
+double orc_uniform2(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
+    return (double)(philox_word(seed, round, purpose, b, i, 1) >> 40) * (1.0 / 16777216.0);
 }
 
 uint32_t orc_uniform_u32(uint64_t seed, uint64_t round, int purpose, int64_t b, int64_t i) {
-    return (uint32_t)(philox_word(seed, round, purpose, b, i) >> 32);
+    return (uint32_t)(philox_word(seed, round, purpose, b, i, 0) >> 32);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -325,27 +331,35 @@ void orc_saguaro(int B, int K, int V, int64_t ld, int dtype, const void* q_logit
 }
 
 /* ------------------------------------------------------------------------- */
-/* Inverse-CDF near-tie (E2).  The decision "smallest j with running sum > u * total"
- * flips only when u lies within the arithmetic error of the sums from a step of the
- * normalised CDF; cdf_eps is the half-width of that band, a parameter of the parity
- * rule (the oracle itself is exact up to fp64 rounding). */
+/* Draws.  READING (the pages fix no sampling mechanism; any exact one keeps the round
+ * lossless): a draw from weights w over ids 0..V-1 takes two uniforms of its
+ * (sequence, position, purpose), u1 (last counter word 0) and u2 (last counter word 1).  The ids are
+ * split into blocks of ORC_BLOCK consecutive ids; u1 picks the block -- the smallest
+ * block whose running sum of block masses exceeds u1 times their total -- and u2 the
+ * id within it -- the smallest id whose running sum within the block exceeds u2 times
+ * the block's mass.  Strict ">" over ascending order, so no zero weight is chosen; if
+ * rounding leaves no crossing, the last block (id) of positive mass is taken.  The
+ * law is w / sum(w) exactly as for one inverse CDF over all ids; two levels keep
+ * each decision well conditioned: a block boundary is resolved against the whole
+ * row's mass, an id boundary only against its block's. */
+#define ORC_BLOCK 512
 
-/* Inverse-CDF selection: the smallest j whose running sum of w exceeds u * total,
- * ids scanned in ascending order; if rounding leaves no such j, the largest j with
- * w_j > 0.  *gap (nullable) receives min(|C(j*) - u|, |C(j*-1) - u|) with
- * C(j) = cumsum_j / total, the distance of u to the two CDF steps around j*. */
-static int inverse_cdf(const double* w, int V, double total, double u, double* gap) {
+/* Inverse-CDF selection over n weights: the smallest j whose running sum exceeds
+ * u * total (ascending j); if rounding leaves no such j, the largest j with w_j > 0.
+ * *gap (nullable) receives min(|C(j*) - u|, |C(j*-1) - u|), C(j) = cumsum_j / total:
+ * the distance of u to the two steps around j*. */
+static int inverse_cdf(const double* w, int n, double total, double u, double* gap) {
     double target = u * total, run = 0.0, prev = 0.0;
     int pick = -1;
-    for (int j = 0; j < V; ++j) {
+    for (int j = 0; j < n; ++j) {
         prev = run;
         run += w[j];
         if (run > target) { pick = j; break; }
     }
     if (pick < 0) {
-        for (int j = V - 1; j >= 0; --j)
+        for (int j = n - 1; j >= 0; --j)
             if (w[j] > 0.0) { pick = j; break; }
-        if (pick < 0) pick = V - 1;
+        if (pick < 0) pick = n - 1;
         prev = total - w[pick];
         run = total;
     }
@@ -356,14 +370,175 @@ static int inverse_cdf(const double* w, int V, double total, double u, double* g
     return pick;
 }
 
+/* Block masses of w (ascending ids within a block), returning their sum. */
+static double block_masses(const double* w, int V, double* W) {
+    const int nb = (V + ORC_BLOCK - 1) / ORC_BLOCK;
+    double tot = 0.0;
+    for (int b = 0; b < nb; ++b) {
+        const int e = (b + 1) * ORC_BLOCK < V ? (b + 1) * ORC_BLOCK : V;
+        double m = 0.0;
+        for (int x = b * ORC_BLOCK; x < e; ++x) m += w[x];
+        W[b] = m;
+        tot += m;
+    }
+    return tot;
+}
+
+/* The two-level draw: returns the id; *blk the block; gap[0], gap[1] (nullable) the
+ * distances of u1 and u2 to the steps around the block and around the id. */
+static int draw_two_level(const double* w, int V, double u1, double u2, int* blk, double* gap) {
+    const int nb = (V + ORC_BLOCK - 1) / ORC_BLOCK;
+    double* W = (double*)malloc(sizeof(double) * nb);
+    const double tot = block_masses(w, V, W);
+    const int b = inverse_cdf(W, nb, tot, u1, gap ? &gap[0] : NULL);
+    const int x0 = b * ORC_BLOCK;
+    const int n = (x0 + ORC_BLOCK < V ? x0 + ORC_BLOCK : V) - x0;
+    const int j = inverse_cdf(w + x0, n, W[b], u2, gap ? &gap[1] : NULL);
+    free(W);
+    if (blk) *blk = b;
+    return x0 + j;
+}
+
+/* Near-tie of a draw (E2).  A decision flips only when its uniform lies within the
+ * arithmetic error of the GPU path's running sums from a step; the half-width of that
+ * band is a quantity of the parity rule, not of the method (the oracle is exact up to
+ * fp64 rounding).  draw_bands derives it per draw and per level. */
+#define ORC_CDF_SIGMAS 6.0  /* random part of the E2 band, in standard deviations */
+
+/* READING (parity rule): the GPU path applies the temperature as the fp32 scale
+ * c = fp32(log2(e) / fp32(T)), so it samples at the temperature log2(e) / c. */
+static double device_temperature(double T) {
+    const float Tf = (float)T;
+    const float c = (float)(1.4426950408889634 / (double)Tf);
+    return 1.4426950408889634 / (double)c;
+}
+
+/* Standard deviation of the relative error of one GPU term 2^e (e the exponent
+ * relative to the row maximum, in bits), for errors spread evenly within their
+ * bounds (rms = bound / sqrt 3): exp2 within one fp32 ulp (2^-23), and the one
+ * rounding of the fp32 exponent (half an ulp of e, times ln 2). */
+static double term_err(double e) {
+    const double a = 0x1p-23, b = 0x1p-24 * 0.6931471805599453 * (fabs(e) + 1.0);
+    return sqrt((a * a + b * b) / 3.0);
+}
+
+/* The laws of one draw at temperature Tx, from the widened rows zp (target) and zq
+ * (draft) and the nS cached ids S of the draft row:
+ *   mode 0: w = p (the target row: bonus after all K accepted);
+ *   mode 1: w = max(p - q', 0) (the residual after a rejection);
+ *   mode 2: w = q' (the draft sampler);
+ * with q' = q (C on S, else 1) / (1 - (1 - C) M).  Writes w, and the absolute term
+ * error bounds a = p d(e_p), c = q' d(e_q) of each id (0 where the term is not part
+ * of the law, and for the residual where p - q' cannot turn positive within them).
+ * Returns sum w. */
+static double draw_laws(int mode, const double* zp, const double* zq, int V, double Tx, const int32_t* S,
+                        int nS, double C, double* w, double* a, double* c) {
+    const double L2E = 1.4426950408889634;
+    double mp = -INFINITY, mq = -INFINITY, sp = 0.0, sq = 0.0, Z = 1.0;
+    if (mode != 2) {
+        for (int x = 0; x < V; ++x) if (zp[x] > mp) mp = zp[x];
+        for (int x = 0; x < V; ++x) sp += exp((zp[x] - mp) / Tx);
+    }
+    if (mode != 0) {
+        for (int x = 0; x < V; ++x) if (zq[x] > mq) mq = zq[x];
+        for (int x = 0; x < V; ++x) sq += exp((zq[x] - mq) / Tx);
+        double M = 0.0;
+        for (int j = 0; j < nS; ++j) M += exp((zq[S[j]] - mq) / Tx) / sq;
+        Z = 1.0 - (1.0 - C) * M;
+    }
+    double total = 0.0;
+    for (int x = 0; x < V; ++x) {
+        double p = 0.0, qp = 0.0, ea = 0.0, ec = 0.0;
+        if (mode != 2) {
+            p = exp((zp[x] - mp) / Tx) / sp;
+            ea = p > 0.0 ? p * term_err((zp[x] - mp) / Tx * L2E) : 0.0;
+        }
+        if (mode != 0) {
+            qp = exp((zq[x] - mq) / Tx) / sq * (in_cache(S, nS, x) ? C : 1.0) / Z;
+            ec = qp > 0.0 ? qp * term_err((zq[x] - mq) / Tx * L2E) : 0.0;
+        }
+        if (mode == 0) w[x] = p;
+        else if (mode == 2) w[x] = qp;
+        else {
+            w[x] = p - qp > 0.0 ? p - qp : 0.0;
+            if (!(p - qp > -(ea + ec))) ea = ec = 0.0;
+        }
+        a[x] = ea;
+        c[x] = ec;
+        total += w[x];
+    }
+    return total;
+}
+
+/* The CDF values of a draw just below and at its pick: block level (over block
+ * masses, around block b) and id level (within block b, around id j). */
+static void draw_cdf(const double* w, int V, int b, int j, double out[4]) {
+    const int nb = (V + ORC_BLOCK - 1) / ORC_BLOCK;
+    double* W = (double*)malloc(sizeof(double) * nb);
+    const double tot = block_masses(w, V, W);
+    double run = 0.0;
+    for (int k = 0; k < b; ++k) run += W[k];
+    out[0] = run / tot;
+    out[1] = (run + W[b]) / tot;
+    double r2 = 0.0;
+    for (int x = b * ORC_BLOCK; x < j; ++x) r2 += w[x];
+    out[2] = r2 / W[b];
+    out[3] = (r2 + w[j]) / W[b];
+    free(W);
+}
+
+/* Half-widths of the E2 bands of one draw (mode as for draw_laws) that picked id j in
+ * block b at temperature T: band[0] for u1 (block level), band[1] for u2 (id level).
+ * Each is
+ *   cdf_eps
+ *   + the shift of the level's normalised CDF at the two steps around the pick
+ *     between the temperature the GPU path samples at and T (both exact, in fp64);
+ *   + ORC_CDF_SIGMAS standard deviations of the GPU path's CDF error from
+ *     independent per-term errors of standard deviation term_err: a random walk over the ids
+ *     that can carry weight, sqrt(sum a^2 + c^2) over the row divided by its mass
+ *     (block level), over the block divided by the block's mass (id level).
+ * (The normalisers' own errors are means over many terms and far smaller.) */
+static void draw_bands(int mode, const double* zp, const double* zq, int V, double T, const int32_t* S, int nS,
+                       double C, int b, int j, double cdf_eps, double band[2]) {
+    double* w = (double*)malloc(sizeof(double) * V);
+    double* a = (double*)malloc(sizeof(double) * V);
+    double* c = (double*)malloc(sizeof(double) * V);
+    double cd[2][4];
+    for (int pass = 0; pass < 2; ++pass) {
+        const double Tx = pass == 0 ? T : device_temperature(T);
+        double total = draw_laws(mode, zp, zq, V, Tx, S, nS, C, w, a, c);
+        if (mode == 1 && !(total > 0.0))  /* degenerate residual: the draw falls back to p */
+            total = draw_laws(0, zp, zq, V, Tx, S, nS, C, w, a, c);
+        draw_cdf(w, V, b, j, cd[pass]);
+        if (pass == 0) {
+            double vr = 0.0, vb = 0.0, mb = 0.0;
+            const int e = (b + 1) * ORC_BLOCK < V ? (b + 1) * ORC_BLOCK : V;
+            for (int x = 0; x < V; ++x) vr += a[x] * a[x] + c[x] * c[x];
+            for (int x = b * ORC_BLOCK; x < e; ++x) {
+                vb += a[x] * a[x] + c[x] * c[x];
+                mb += w[x];
+            }
+            band[0] = cdf_eps + ORC_CDF_SIGMAS * sqrt(vr) / total;
+            band[1] = cdf_eps + ORC_CDF_SIGMAS * sqrt(vb) / mb;
+        }
+    }
+    for (int l = 0; l < 2; ++l) {
+        const double d0 = fabs(cd[1][2 * l] - cd[0][2 * l]), d1 = fabs(cd[1][2 * l + 1] - cd[0][2 * l + 1]);
+        band[l] += d0 > d1 ? d0 : d1;
+    }
+    free(c);
+    free(a);
+    free(w);
+}
+
 /* Draft tokens for a synthetic round (harness step, not part of the timed round):
  * the draft samples d_i from its Saguaro-reweighted law q'_i ([zh] section 2,
- * Challenge 2: the reweighting is applied while the draft samples) by inverse CDF
- * with u = U(seed, round, b, i, DRAFT).  At T = 0 the draft is greedy. */
+ * Challenge 2: the reweighting is applied while the draft samples) by the two-level
+ * draw with the uniforms of (b, i, DRAFT).  At T = 0 the draft is greedy. */
 void orc_draft_sample(int B, int K, int V, int64_t ld, int dtype, const void* q_logits, double T,
                       const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
                       uint64_t seed, uint64_t round, int64_t b_base, double cdf_eps, int32_t* draft,
-                      uint8_t* tie_flags /* [B,K] */, double* gaps /* nullable [B,K] */) {
+                      uint8_t* tie_flags /* [B,K] */, double* e2 /* nullable [B,K][4] */) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t bi = 0; bi < (int64_t)B * K; ++bi) {
         int b = (int)(bi / K), i = (int)(bi % K);
@@ -378,20 +553,23 @@ void orc_draft_sample(int B, int K, int V, int64_t ld, int dtype, const void* q_
         int32_t arg;
         softmax_row(z, V, T, &m, &s, &arg, NULL);
         uint8_t flag = 0;
+        double info[4] = {INFINITY, 0.0, INFINITY, 0.0};
         if (T > 0.0) {
-            double tot = 0.0;
-            for (int x = 0; x < V; ++x) {
+            for (int x = 0; x < V; ++x)
                 w[x] = row_prob(z[x], x, m, s, arg, T) * (in_cache(S, F[i], x) ? C : 1.0) / Z[r];
-                tot += w[x];
-            }
-            double u = orc_uniform(seed, round, ORC_PURPOSE_DRAFT, b_base + b, i), gap;
-            draft[bi] = inverse_cdf(w, V, tot, u, &gap);
-            if (gap < cdf_eps) flag = ORC_E2_CDF_TIE;
-            if (gaps) gaps[bi] = gap;
+            const double u1 = orc_uniform(seed, round, ORC_PURPOSE_DRAFT, b_base + b, i);
+            const double u2 = orc_uniform2(seed, round, ORC_PURPOSE_DRAFT, b_base + b, i);
+            double gap[2], band[2];
+            int blk;
+            draft[bi] = draw_two_level(w, V, u1, u2, &blk, gap);
+            draw_bands(2, NULL, z, V, T, S, F[i], C, blk, draft[bi], cdf_eps, band);
+            if (gap[0] < band[0] || gap[1] < band[1]) flag = ORC_E2_CDF_TIE;
+            info[0] = gap[0]; info[1] = band[0]; info[2] = gap[1]; info[3] = band[1];
         } else {
             draft[bi] = arg;
-            if (gaps) gaps[bi] = INFINITY;
         }
+        if (e2)
+            for (int l = 0; l < 4; ++l) e2[bi * 4 + l] = info[l];
         if (tie_flags) tie_flags[bi] = flag;
         free(w);
         free(z);
@@ -476,8 +654,8 @@ void orc_verify(int B, int K, int V, int64_t ld, int dtype, const void* p_logits
  *   k < K:  w(x) = max(p_k(x) - q'_k(x), 0), Z_r = sum w; if Z_r == 0 (only through
  *           rounding) w = p_k;
  *   k = K:  w = p_K, Z_r = sum w;
- * bonus = inverse CDF of w at u = U(seed, round, b, k, BONUS).  At T = 0 the bonus is
- * argmax p_k.  resid (nullable [B, V]) receives w, resid_mass receives Z_r. */
+ * bonus = the two-level draw from w with the uniforms of (b, k, BONUS).  At T = 0 the
+ * bonus is argmax p_k.  resid (nullable [B, V]) receives w, resid_mass receives Z_r. */
 void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
                          const void* q_logits, double T,
                          const double* p_max, const double* p_sum, const int32_t* p_arg,
@@ -485,11 +663,14 @@ void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void*
                          const int32_t* F, int Bf, const int32_t* cache_ids, const double* Z, double C,
                          const int32_t* accept_len, uint64_t seed, uint64_t round, int64_t b_base,
                          double cdf_eps, int32_t* bonus, double* resid_mass, double* resid, int32_t* err,
-                         uint8_t* exc, double* cdf_gap /* nullable [B] */) {
+                         uint8_t* exc, double* e2 /* nullable [B][4] */) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         int k = accept_len[b];
-        if (cdf_gap) cdf_gap[b] = INFINITY;
+        if (e2) {
+            e2[b * 4 + 0] = e2[b * 4 + 2] = INFINITY;
+            e2[b * 4 + 1] = e2[b * 4 + 3] = 0.0;
+        }
         if (k < 0 || k > K) {
             bonus[b] = -1;
             if (resid_mass) resid_mass[b] = 0.0;
@@ -529,10 +710,25 @@ void orc_residual_sample(int B, int K, int V, int64_t ld, int dtype, const void*
                 Zr += w[x];
             }
         }
-        double u = orc_uniform(seed, round, ORC_PURPOSE_BONUS, b_base + b, k), gap;
-        bonus[b] = inverse_cdf(w, V, Zr, u, &gap);
-        if (gap < cdf_eps) x_flags |= ORC_E2_CDF_TIE;
-        if (cdf_gap) cdf_gap[b] = gap;
+        const double u1 = orc_uniform(seed, round, ORC_PURPOSE_BONUS, b_base + b, k);
+        const double u2 = orc_uniform2(seed, round, ORC_PURPOSE_BONUS, b_base + b, k);
+        double gap[2], band[2];
+        int blk;
+        bonus[b] = draw_two_level(w, V, u1, u2, &blk, gap);
+        double* zp = (double*)malloc(sizeof(double) * V);
+        double* zq = (double*)malloc(sizeof(double) * V);
+        load_row(p_logits, dtype, ld, r, V, zp);
+        load_row(q_logits, dtype, ld, r, V, zq);
+        draw_bands(k < K ? 1 : 0, zp, zq, V, T, S, F[k], C, blk, bonus[b], cdf_eps, band);
+        free(zq);
+        free(zp);
+        if (gap[0] < band[0] || gap[1] < band[1]) x_flags |= ORC_E2_CDF_TIE;
+        if (e2) {
+            e2[b * 4 + 0] = gap[0];
+            e2[b * 4 + 1] = band[0];
+            e2[b * 4 + 2] = gap[1];
+            e2[b * 4 + 3] = band[1];
+        }
         if (resid_mass) resid_mass[b] = Zr;
         if (resid)
             for (int x = 0; x < V; ++x) resid[(int64_t)b * V + x] = w[x];
@@ -716,7 +912,7 @@ void orc_round(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
                int32_t* q_arg, int32_t* cache_ids, double* cache_mass, double* Z,
                int32_t* accept_len, double* accept_prob, int32_t* bonus, double* resid_mass,
                uint8_t* hit, int32_t* slot, int32_t* fallback_tokens, int32_t* err, uint8_t* exc,
-               double* cdf_gap) {
+               double* e2) {
     orc_softmax(B, K, V, ld, dtype, p_logits, T, p_max, p_sum, p_arg, NULL);
     orc_softmax(B, K, V, ld, dtype, q_logits, T, q_max, q_sum, q_arg, NULL);
     orc_build_cache(B, K, V, ld, dtype, q_logits, T, F, Bf, cache_ids, cache_mass);
@@ -726,7 +922,7 @@ void orc_round(int B, int K, int V, int64_t ld, int dtype, const void* p_logits,
                q_arg, F, Bf, cache_ids, Z, C, seed, round, b_base, accept_len, accept_prob, err, exc);
     orc_residual_sample(B, K, V, ld, dtype, p_logits, q_logits, T, p_max, p_sum, p_arg, q_max, q_sum,
                         q_arg, F, Bf, cache_ids, Z, C, accept_len, seed, round, b_base, cdf_eps,
-                        bonus, resid_mass, NULL, err, exc, cdf_gap);
+                        bonus, resid_mass, NULL, err, exc, e2);
     orc_cache_lookup(B, K, V, F, Bf, cache_ids, accept_len, bonus, fallback_uniform, seed, round,
                      b_base, hit, slot, fallback_tokens, err);
 }

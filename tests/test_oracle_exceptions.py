@@ -10,13 +10,16 @@ these pins do not restate the oracle's arithmetic.
 
 Bands (the parity rule of the round):
   E1  |u_i - p_i(d_i)/q'_i(d_i)| < 1e-5 at a tested position i <= min(k, K-1);
-  E2  u within CDF_TIE_EPS of one of the two normalised CDF steps around the
-      sampled id (draft sampler and bonus);
+  E2  a uniform of a draw within its band of one of the two normalised CDF steps
+      around its pick, at the block level (u1) or the id level (u2); the band is
+      derived per draw from the arithmetic of the GPU path, at least CDF_TIE_EPS
+      (draft sampler and bonus);
   E3  residual mass Z_r < 1e-5 after a rejection (k < K);
   E5  a tested p_i(d_i) or q'_i(d_i) below 1e-30 from a finite logit.
 A final test compiles mutated copies of ssd_oracle.c (a wrong band, the
 min(1, ratio) slip, flags after the first rejection, the -inf exemption dropped,
-one side of the CDF gap dropped) and checks that each one fails a pin here.
+one side of the CDF gap dropped, the band's random part dropped, the levels' uniforms
+swapped) and checks that each one fails a pin here.
 """
 import os
 
@@ -28,21 +31,22 @@ ACCEPT, BONUS, DRAFT = 0, 1, 2
 
 
 # --------------------------------------------------------------------------- helpers
-def u_np(seed, rnd, purpose, b, i):
+def u_np(seed, rnd, purpose, b, i, w3=0):
     """U(seed, rnd, b, i, purpose) from numpy's Philox4x64-10: the first output word
-    of counter (rnd, b, i, 0) under key (seed, purpose), top 24 bits times 2^-24
-    (numpy increments the counter before producing a block)."""
+    of counter (rnd, b, i, w3) under key (seed, purpose), top 24 bits times 2^-24
+    (numpy increments the counter before producing a block); w3 = 1 gives a draw's
+    second uniform."""
     assert rnd >= 1
     g = np.random.Philox(key=np.array([seed, purpose], np.uint64),
-                         counter=np.array([rnd - 1, b, i, 0], np.uint64))
+                         counter=np.array([rnd - 1, b, i, w3], np.uint64))
     return (int(g.random_raw(1)[0]) >> 40) / 2.0**24
 
 
-def us_over_rounds(seed, purpose, b, i, r0, n):
+def us_over_rounds(seed, purpose, b, i, r0, n, w3=0):
     """u for rounds r0 .. r0+n-1 at (b, i): consecutive numpy Philox blocks advance
     counter word 0, which is the round."""
     g = np.random.Philox(key=np.array([seed, purpose], np.uint64),
-                         counter=np.array([r0 - 1, b, i, 0], np.uint64))
+                         counter=np.array([r0 - 1, b, i, w3], np.uint64))
     w0 = g.random_raw(4 * n)[0::4]
     return (w0 >> np.uint64(40)).astype(np.float64) / 2.0**24
 
@@ -65,13 +69,17 @@ def softmax64(row):
     return e / e.sum()
 
 
-def find_round(lo, hi, purpose, bs, i=0, r0=1, n=200000):
-    """The first round r >= r0 whose uniforms at (b, i) lie in (lo, hi) for every b
-    in bs."""
+def find_round(lo, hi, purpose, bs, i=0, r0=1, n=200000, w3=0, also=None):
+    """The first round r >= r0 whose uniforms (counter word w3) at (b, i) lie in
+    (lo, hi) for every b in bs, and, with also = (w3', lo', hi'), whose uniforms of
+    word w3' lie in (lo', hi')."""
     ok = np.ones(n, bool)
     for b in bs:
-        u = us_over_rounds(SEED, purpose, b, i, r0, n)
+        u = us_over_rounds(SEED, purpose, b, i, r0, n, w3)
         ok &= (u > lo) & (u < hi)
+        if also is not None:
+            u = us_over_rounds(SEED, purpose, b, i, r0, n, also[0])
+            ok &= (u > also[1]) & (u < also[2])
     hits = np.nonzero(ok)[0]
     assert hits.size, "no round found"
     return r0 + int(hits[0])
@@ -209,104 +217,153 @@ def check_e5_band(orc):
     assert not np.any(exc & orc.E1_ACCEPT_TIE)
 
 
-# --------------------------------------------------------------------------- E2: inverse CDF
-def _e2_deltas(eps):
-    return [(0.5 * eps, True), (-0.5 * eps, True), (0.9 * eps, True), (-0.9 * eps, True),
-            (1.1 * eps, False), (-1.1 * eps, False), (2.5 * eps, False), (-2.5 * eps, False)]
+# --------------------------------------------------------------------------- E2: the draws
+# A draw takes u1 (last counter word 0) for its block of 512 ids and u2 (word 1) for
+# the id within the block.  Each case puts one CDF step at a distance delta from the
+# uniform of one level: at the id level V = 2 or 3 (a single block), at the block level
+# V = 1024 with mass on id 0 (block 0) and id 1023 (block 1) only, so that the id level
+# has one id per block and nothing to decide.  delta is a multiple of the band the
+# oracle reports for the draw (probed at delta = 0); the gap it reports must equal
+# |step - u| recomputed here from the fp32 logits, the band must lie in the range the
+# arithmetic of the GPU path gives for such rows (a few fp32 ulps, about 3e-7), and
+# the flag must fire exactly for |delta| below the band.
+E2_FACTORS = [(0.5, True), (-0.5, True), (0.9, True), (-0.9, True),
+              (1.1, False), (-1.1, False), (2.5, False), (-2.5, False)]
+LEVELS = {"id": (2, 1), "block": (1024, 0)}  # level -> (V, counter word of its uniform)
+
+
+def _u_of(rnd, purpose, b, i, w3):
+    return u_np(SEED, rnd, purpose, b, i, w3)
+
+
+def _round_for_level(purpose, w3, i=0, lo=0.4, hi=0.9):
+    """A round whose uniform of the tested level lies in (lo, hi) and whose other
+    uniform lies in (0.1, 0.9), away from the steps 0 and 1 of a one-entry level."""
+    return find_round(lo, hi, purpose, [0], i=i, w3=w3, also=(1 - w3, 0.1, 0.9))
+
+
+def _check_e2_info(info, level, t, u, flag):
+    """info = (gap of u1, band of u1, gap of u2, band of u2) of one draw."""
+    lv = 0 if level == "block" else 1
+    gap, band = info[2 * lv], info[2 * lv + 1]
+    assert abs(gap - abs(t - u)) < 1e-12, (level, gap, t, u)
+    assert 5e-8 < band < 2e-6, (level, band)
+    assert info[2 * (1 - lv)] > 0.09 and info[2 * (1 - lv) + 1] < 1e-5, info
+    assert (gap < band) == flag, (level, gap, band, flag)
+
+
+def _draft_row(V, t, cached, C):
+    """Draft logits over V ids whose reweighted law holds t on id 0 and 1 - t on id
+    V - 1 (the rest masked); cached: id 0 is the cached top-1 (F_0 = 1) with weight C.
+    Returns the row and q'(0) recomputed in fp64 from its fp32 logits."""
+    z = np.full(V, -np.inf, np.float32)
+    z[V - 1] = 0.0
+    if not cached:
+        z[0] = logit_for(t)
+        return z, p0_of(z[0])
+    q = t / (C + (1.0 - C) * t)  # q'(0) = C q / (1 - (1 - C) q), q > 1/2: id 0 is the top-1
+    z[0] = logit_for(q)
+    q = p0_of(z[0])
+    return z, C * q / (1.0 - (1.0 - C) * q)
 
 
 def check_e2_draft_sampler(orc):
-    """Draft sampler, V = 2: q'(0) = u + delta puts the CDF step at distance |delta|
-    from u, on either side; flagged iff |delta| < CDF_TIE_EPS.  Each case is drawn
-    once with id 0 uncached (q' = q) and once cached (F_0 = 1, C = 0.5, where id 0
-    holds the larger logit), so that q' differs from q."""
-    eps = orc.CDF_TIE_EPS
+    """Draft sampler at both levels, each case drawn once with id 0 uncached (q' = q)
+    and once cached (F_0 = 1, C = 0.5), so that q' differs from q."""
     C = 0.5
-    for cached in (False, True):
-        for delta, flag in _e2_deltas(eps):
-            rnd = find_round(0.4, 0.9, DRAFT, [0])
-            u = u_np(SEED, rnd, DRAFT, 0, 0)
-            t = u + delta
-            zq = np.zeros((1, 2, 2), np.float32)
-            if not cached:
-                zq[0, 0, 0] = logit_for(t)
-                qp0 = p0_of(zq[0, 0, 0])
-            else:  # q'(0) = C q / (1 - (1 - C) q), q > 1/2 so that id 0 is the top-1
-                q = t / (C + (1.0 - C) * t)
-                zq[0, 0, 0] = logit_for(q)
-                q = p0_of(zq[0, 0, 0])
-                qp0 = C * q / (1.0 - (1.0 - C) * q)
-            assert abs(qp0 - t) < 2e-8, (qp0, t)
+    for level, (V, w3) in LEVELS.items():
+        rnd = _round_for_level(DRAFT, w3)
+        u = _u_of(rnd, DRAFT, 0, 0, w3)
+        for cached in (False, True):
             F = np.array([1 if cached else 0, 0], np.int32)
-            ids, mass = orc.build_cache(zq, 1.0, F)
-            Z, _ = orc.saguaro(zq, 1.0, F, ids, mass, C)
-            d, flags = orc.draft_sample(zq, 1.0, F, ids, Z, C, SEED, rnd)
-            assert d[0, 0] == (0 if u < qp0 else 1), (cached, delta, d)
-            assert bool(flags[0, 0]) == flag, (cached, delta, flags)
+
+            def draw(t):
+                zq = np.zeros((1, 2, V), np.float32)
+                zq[0, 0], qp0 = _draft_row(V, t, cached, C)
+                ids, mass = orc.build_cache(zq, 1.0, F)
+                Z, _ = orc.saguaro(zq, 1.0, F, ids, mass, C)
+                d, flags, e2 = orc.draft_sample(zq, 1.0, F, ids, Z, C, SEED, rnd, want_gaps=True)
+                return qp0, d[0, 0], bool(flags[0, 0]), e2[0, 0]
+
+            band = draw(u)[3][2 * w3 + 1]
+            for f, flag in E2_FACTORS:
+                qp0, d, got, info = draw(u + f * band)
+                assert abs(qp0 - u - f * band) < 0.05 * band, (level, cached, f, qp0, u)
+                assert d == (0 if u < qp0 else V - 1), (level, cached, f, d)
+                assert got == flag, (level, cached, f, info)
+                _check_e2_info(info, level, qp0, u, flag)
 
 
 def check_e2_bonus_all_accepted(orc):
-    """Bonus after all K accepted (w = p_K, Z_r = 1), V = 2: p_K(0) = u + delta."""
-    eps = orc.CDF_TIE_EPS
-    deltas = _e2_deltas(eps)
-    B = len(deltas)
+    """Bonus after all K = 1 accepted (w = p_K) at both levels: p_K(0) = u + delta on
+    id 0 and the rest on id V - 1."""
     K = 1
-    rnd = find_round(0.2, 0.8, BONUS, list(range(B)), i=K)
-    zq = np.zeros((B, K + 1, 2), np.float32)
-    zp = np.zeros((B, K + 1, 2), np.float32)
-    want_b = []
-    for b, (delta, flag) in enumerate(deltas):
-        u = u_np(SEED, rnd, BONUS, b, K)
-        zp[b, K, 0] = logit_for(u + delta)
-        assert abs(p0_of(zp[b, K, 0]) - u - delta) < 2e-8
-        want_b.append(0 if u < p0_of(zp[b, K, 0]) else 1)
-    want_f = [f for _, f in deltas]
-    _bonus_check(orc, zq, zp, np.full(B, K, np.int32), rnd, want_b, want_f)
+    for level, (V, w3) in LEVELS.items():
+        rnd = _round_for_level(BONUS, w3, i=K, lo=0.2, hi=0.8)
+        u = _u_of(rnd, BONUS, 0, K, w3)
+
+        def draw(t):
+            zq = np.zeros((1, K + 1, V), np.float32)
+            zp = np.zeros((1, K + 1, V), np.float32)
+            zp[0, K], p0 = _draft_row(V, t, False, 1.0)
+            return (p0,) + _bonus(orc, zq, zp, np.full(1, K, np.int32), rnd)
+
+        band = draw(u)[4][2 * w3 + 1]
+        for f, flag in E2_FACTORS:
+            p0, bonus, got, zr, info = draw(u + f * band)
+            assert abs(p0 - u - f * band) < 0.05 * band
+            assert bonus == (0 if u < p0 else V - 1), (level, f, bonus)
+            assert got == flag, (level, f, info)
+            _check_e2_info(info, level, p0, u, flag)
 
 
 def check_e2_bonus_residual(orc):
-    """Bonus after a rejection at position 0 (w = max(p - q, 0)), V = 3: q =
-    softmax([0, 0, 2]) and p chosen so that w = (w0, 0.2, 0) with
-    w0 / (w0 + 0.2) = u + delta, i.e. the first CDF step at distance |delta| from u."""
-    eps = orc.CDF_TIE_EPS
-    deltas = _e2_deltas(eps)
-    B = len(deltas)
-    rnd = find_round(0.2, 0.55, BONUS, list(range(B)))
-    zq = np.zeros((B, 2, 3), np.float32)
-    zp = np.zeros((B, 2, 3), np.float32)
-    zq[:, 0, 2] = 2.0
-    q = softmax64(zq[0, 0])
-    want_b = []
-    for b, (delta, flag) in enumerate(deltas):
-        u = u_np(SEED, rnd, BONUS, b, 0)
-        t = u + delta
-        w1 = 0.2
-        w0 = t * w1 / (1.0 - t)
-        p0, p1 = q[0] + w0, q[1] + w1
-        p2 = 1.0 - p0 - p1
-        assert p2 < q[2]
-        zp[b, 0] = np.array([np.log(p0 / p2), np.log(p1 / p2), 0.0], np.float32)
-        p = softmax64(zp[b, 0])
-        w = np.maximum(p - q, 0.0)
-        c0 = w[0] / w.sum()
-        assert w[2] == 0.0 and abs(c0 - t) < 2e-7, (b, c0, t)
-        want_b.append(0 if u < c0 else 1)
-    want_f = [f for _, f in deltas]
-    _bonus_check(orc, zq, zp, np.zeros(B, np.int32), rnd, want_b, want_f)
+    """Bonus after a rejection at position 0 (w = max(p - q, 0)) at both levels: ids
+    (a, b, c) = (0, 1, 2) of V = 3 (id level) or (0, 1023, 512) of V = 1024 (block
+    level, a and b in different blocks, c beside b's block); q puts logits (0, 0, 2)
+    on them and p is chosen so that w = (w_a, 0.2, 0) with w_a / (w_a + 0.2) = u +
+    delta, i.e. the first CDF step of the level at distance |delta| from u."""
+    for level, V, w3 in (("id", 3, 1), ("block", 1024, 0)):
+        ia, ib, ic = (0, 1, 2) if V == 3 else (0, 1023, 512)
+        rnd = _round_for_level(BONUS, w3, lo=0.2, hi=0.55)
+        u = _u_of(rnd, BONUS, 0, 0, w3)
+        zq = np.full((1, 2, V), -np.inf, np.float32)
+        zq[0, :, [ia, ib, ic]] = np.array([0.0, 0.0, 2.0], np.float32)[:, None]
+        q = softmax64(zq[0, 0, [ia, ib, ic]])
+
+        def draw(t):
+            w1 = 0.2
+            w0 = t * w1 / (1.0 - t)
+            p0, p1 = q[0] + w0, q[1] + w1
+            p2 = 1.0 - p0 - p1
+            assert p2 < q[2]
+            zp = np.full((1, 2, V), -np.inf, np.float32)
+            zp[0, :, [ia, ib, ic]] = np.array([np.log(p0 / p2), np.log(p1 / p2), 0.0], np.float32)[:, None]
+            w = np.maximum(softmax64(zp[0, 0, [ia, ib, ic]]) - q, 0.0)
+            assert w[2] == 0.0
+            return (w[0] / w.sum(),) + _bonus(orc, zq, zp, np.zeros(1, np.int32), rnd)
+
+        band = draw(u)[4][2 * w3 + 1]
+        for f, flag in E2_FACTORS:
+            c0, bonus, got, zr, info = draw(u + f * band)
+            assert abs(c0 - u - f * band) < 0.05 * band, (level, f, c0, u)
+            assert bonus == (ia if u < c0 else ib), (level, f, bonus)
+            assert got == flag, (level, f, info)
+            _check_e2_info(info, level, c0, u, flag)
 
 
-def _bonus_check(orc, zq, zp, acc, rnd, want_b, want_f):
+def _bonus(orc, zq, zp, acc, rnd):
+    """(bonus, E2 flag, Z_r, (gap, band) info) of one sequence at T = 1, C = 1."""
     T, C = 1.0, 1.0
     K = zq.shape[1] - 1
     F = np.zeros(K + 1, np.int32)
     ps, qs = orc.softmax(zp, T), orc.softmax(zq, T)
     ids, mass = orc.build_cache(zq, T, F)
     Z, _ = orc.saguaro(zq, T, F, ids, mass, C)
-    bonus, zr, _, err, exc = orc.residual_sample(zp, zq, T, ps, qs, F, ids, Z, C, acc, SEED, rnd)
-    assert bonus.tolist() == want_b, (bonus, want_b)
-    got = (exc & orc.E2_CDF_TIE) != 0
-    assert got.tolist() == want_f, (got, want_f)
-    assert not np.any(exc & orc.E3_DEGENERATE_RESIDUAL)
+    bonus, zr, _, err, exc, e2 = orc.residual_sample(zp, zq, T, ps, qs, F, ids, Z, C, acc, SEED, rnd,
+                                                     want_bands=True)
+    assert not np.any(exc & orc.E3_DEGENERATE_RESIDUAL) and not np.any(err)
+    return int(bonus[0]), bool(exc[0] & orc.E2_CDF_TIE), float(zr[0]), e2[0]
 
 
 # --------------------------------------------------------------------------- E3: residual mass
@@ -355,8 +412,8 @@ def test_exception_pin(orc, check):
 
 
 def test_band_constants(orc):
-    """The bands the pins above bracket: E1 and E3 at 1e-5 (the parity rule), E2 at the
-    derived CDF_TIE_EPS, which the rule caps at 1e-5."""
+    """The bands the pins above bracket: E1 and E3 at 1e-5 (the parity rule); the floor
+    CDF_TIE_EPS of the per-draw E2 bands is capped by the rule at 1e-5."""
     assert 0 < orc.CDF_TIE_EPS <= 1e-5
 
 
@@ -376,6 +433,14 @@ MUTANTS = [
     ("E2 gap on one side only", "*gap = a < c ? a : c;", "*gap = a;"),
     ("E2 gap unnormalised", "double a = fabs(run / total - u), c = fabs(prev / total - u);",
      "double a = fabs(run - u), c = fabs(prev - u);"),
+    ("E2 band without its random part", "#define ORC_CDF_SIGMAS 6.0", "#define ORC_CDF_SIGMAS 0.0"),
+    ("E2 draft uniforms swapped", "draft[bi] = draw_two_level(w, V, u1, u2, &blk, gap);",
+     "draft[bi] = draw_two_level(w, V, u2, u1, &blk, gap);"),
+    ("E2 bonus uniforms swapped", "bonus[b] = draw_two_level(w, V, u1, u2, &blk, gap);",
+     "bonus[b] = draw_two_level(w, V, u2, u1, &blk, gap);"),
+    ("E2 second uniform from counter word 0", "philox_word(seed, round, purpose, b, i, 1)",
+     "philox_word(seed, round, purpose, b, i, 0)"),
+    ("E2 blocks of 1024 ids", "#define ORC_BLOCK 512", "#define ORC_BLOCK 1024"),
 ]
 
 
@@ -397,35 +462,3 @@ def test_mutants_fail_a_pin(orc, tmp_path, name, old, new):
     finally:
         orc._lib = saved
     assert failed, "mutant '%s' passes every pin" % name
-
-
-def test_e2_band_mutation_fails_a_pin(orc):
-    """The E2 band is a parameter of the oracle's calls: a band 1.2x too wide or 0.8x
-    too narrow fails a pin."""
-    saved = orc.CDF_TIE_EPS
-    for scale in (1.2, 0.8):
-        orc.CDF_TIE_EPS = saved * scale
-        try:
-            with pytest.raises(AssertionError):
-                for check in (check_e2_draft_sampler, check_e2_bonus_all_accepted, check_e2_bonus_residual):
-                    # the cases are rebuilt around the true band
-                    _with_band(check, orc, saved)
-        finally:
-            orc.CDF_TIE_EPS = saved
-
-
-def _with_band(check, orc, true_eps):
-    """Runs an E2 check whose cases sit around true_eps while the oracle is called
-    with whatever orc.CDF_TIE_EPS holds."""
-    used = orc.CDF_TIE_EPS
-
-    class View:
-        def __getattr__(self, k):
-            if k == "CDF_TIE_EPS":
-                return true_eps
-            return getattr(orc, k)
-
-    v = View()
-    # residual_sample / draft_sample read orc.CDF_TIE_EPS as their default band
-    assert orc.CDF_TIE_EPS == used
-    check(v)

@@ -53,6 +53,10 @@ def test_uniform_definition_and_ks(orc):
             assert u == (w0 >> 40) / 2.0**24
             assert orc.uniform_u32(seed, rnd, orc.PURPOSE_ACCEPT, b, i) == w0 >> 32
             us.append(u)
+            # a draw's second uniform: last counter word 1
+            bg = np.random.Philox(key=np.array([seed, orc.PURPOSE_BONUS], dtype=np.uint64),
+                                  counter=np.array([rnd - 1, b, i, 1], dtype=np.uint64))
+            assert orc.uniform2(seed, rnd, orc.PURPOSE_BONUS, b, i) == (int(bg.random_raw(1)[0]) >> 40) / 2.0**24
     from scipy import stats
     assert stats.kstest(us, "uniform").pvalue > 1e-3
 
@@ -224,12 +228,28 @@ def _setup(orc, rng, B, K, V, T, C, Bf=12, r=0.7, scale=2.0, corr_noise=0.8):
     return zp, zq, F, ids, mass, Z, qp, ps, qs
 
 
+def _u_np(seed, rnd, purpose, b, i, w3):
+    bg = np.random.Philox(key=np.array([seed, purpose], dtype=np.uint64),
+                          counter=np.array([rnd - 1, b, i, w3], dtype=np.uint64))
+    return (int(bg.random_raw(1)[0]) >> 40) / 2.0**24
+
+
+def _two_level(w, u1, u2, block=512):
+    """The two-level draw with numpy's searchsorted: the block of 512 ids from the
+    running block masses at u1, then the id within it from its running sums at u2."""
+    W = np.array([w[s:s + block].sum() for s in range(0, w.shape[0], block)])
+    b = int(np.searchsorted(np.cumsum(W), u1 * W.sum(), side="right"))
+    wb = w[b * block:(b + 1) * block]
+    return b * block + int(np.searchsorted(np.cumsum(wb), u2 * W[b], side="right"))
+
+
 @pytest.mark.parametrize("T", [0.8, 1.0])
 def test_residual_invariants_and_searchsorted(orc, T):
     """P5 / P9: w >= 0 and sums to Z_r; after a rejection w(d_k) = 0 and bonus != d_k;
-    the bonus equals np.searchsorted(cumsum(w), u * Z_r, 'right')."""
+    the bonus equals the two-level draw by np.searchsorted (blocks of 512 ids, V = 1100:
+    two whole blocks and a ragged one) with the uniforms from numpy's Philox."""
     rng = np.random.default_rng(8)
-    B, K, V, C = 64, 3, 50, 0.4
+    B, K, V, C = 64, 3, 1100, 0.4
     zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, T, C)
     seed, rnd = 99, 3
     d, _ = orc.draft_sample(zq, T, F, ids, Z, C, seed, rnd)
@@ -252,11 +272,11 @@ def test_residual_invariants_and_searchsorted(orc, T):
             assert bonus[b] != d[b, k]
         else:
             np.testing.assert_allclose(w, p[b, K], atol=1e-15)
-        u = orc.uniform(seed, rnd, orc.PURPOSE_BONUS, b, k)
-        j = int(np.searchsorted(np.cumsum(w), u * zr[b], side="right"))
+        j = _two_level(w, _u_np(seed, rnd, orc.PURPOSE_BONUS, b, k, 0), _u_np(seed, rnd, orc.PURPOSE_BONUS, b, k, 1))
         if not (exc2[b] & orc.E2_CDF_TIE):
             assert bonus[b] == j
     assert n_rej > 10
+    assert len(set((bonus // 512).tolist())) == 3
 
 
 def test_residual_greedy_and_bad_len(orc):
@@ -274,18 +294,18 @@ def test_residual_greedy_and_bad_len(orc):
 
 
 def test_draft_sampler_searchsorted(orc):
-    """P9 for the draft sampler: d_i = searchsorted(cumsum(q'_i), u, 'right')."""
+    """P9 for the draft sampler: d_i is the two-level draw from q'_i by np.searchsorted
+    (V = 1300: two whole blocks of 512 and a ragged one)."""
     rng = np.random.default_rng(10)
-    B, K, V, T, C = 20, 3, 40, 1.0, 0.5
+    B, K, V, T, C = 20, 3, 1300, 1.0, 0.5
     zp, zq, F, ids, mass, Z, qp, ps, qs = _setup(orc, rng, B, K, V, T, C)
     d, flags = orc.draft_sample(zq, T, F, ids, Z, C, 5, 6)
     for b in range(B):
         for i in range(K):
-            u = orc.uniform(5, 6, orc.PURPOSE_DRAFT, b, i)
-            c = np.cumsum(qp[b, i])
-            j = int(np.searchsorted(c, u * c[-1], side="right"))
+            j = _two_level(qp[b, i], _u_np(5, 6, orc.PURPOSE_DRAFT, b, i, 0), _u_np(5, 6, orc.PURPOSE_DRAFT, b, i, 1))
             if not flags[b, i]:
                 assert d[b, i] == j
+    assert len(set((d // 512).ravel().tolist())) == 3
     dg, _ = orc.draft_sample(zq, 0.0, F, ids, Z, C, 5, 6)
     assert np.array_equal(dg, np.argmax(zq[:, :K], -1))
 
