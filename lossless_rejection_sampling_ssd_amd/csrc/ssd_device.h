@@ -29,6 +29,12 @@ template <int DT> constexpr int kTile = kVecPerLane * kWave * ElemTraits<DT>::kP
 // the arithmetic of early waves overlaps the loads of later ones.
 constexpr int kVecPass2 = 4;
 template <int DT> constexpr int kTile2 = kVecPass2 * kWave * ElemTraits<DT>::kPerVec;
+// A draw picks a block of kDrawBlock consecutive ids first, then the id inside it; a
+// pass-2 tile holds whole blocks, a block whole wave vectors (1 bf16, 2 fp32).
+constexpr int kDrawBlock = 512;
+template <int DT> constexpr int kVecPerBlock = kDrawBlock / (kWave * ElemTraits<DT>::kPerVec);
+template <int DT> constexpr int kBlocksPerTile2 = kVecPass2 / kVecPerBlock<DT>;
+static_assert(kTile2<0> % kDrawBlock == 0 && kTile2<1> % kDrawBlock == 0, "tiles hold whole draw blocks");
 
 // ---------------------------------------------------------------------------- loads
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -375,10 +381,11 @@ __device__ __forceinline__ void merge_partial(float& m, double& s, float m2, dou
 // ---------------------------------------------------------------------------- Philox
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round two 64x64->128
 // products with the published multipliers, key bumped by the published Weyl
-// constants; returns the first output word.
+// constants; returns the first output word of counter (round, b, i, w3) under key
+// (seed, purpose).
 __device__ __forceinline__ uint64_t philox_word0(uint64_t seed, uint64_t round, uint32_t purpose,
-                                                 uint64_t b, uint64_t i) {
-    uint64_t c0 = round, c1 = b, c2 = i, c3 = 0;
+                                                 uint64_t b, uint64_t i, uint64_t w3 = 0) {
+    uint64_t c0 = round, c1 = b, c2 = i, c3 = w3;
     uint64_t k0 = seed, k1 = purpose;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
@@ -397,10 +404,11 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t seed, uint64_t round, 
     }
     return c0;
 }
-// u in [0, 1) with 24 random bits, exact in fp32.
+// u in [0, 1) with 24 random bits, exact in fp32.  w3 = 0: the uniform of a test or
+// of a draw's block; w3 = 1: a draw's second uniform (the id inside the block).
 __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t round, uint32_t purpose, uint64_t b,
-                                                uint64_t i) {
-    return (float)(uint32_t)(philox_word0(seed, round, purpose, b, i) >> 40) * (1.0f / 16777216.0f);
+                                                uint64_t i, uint64_t w3 = 0) {
+    return (float)(uint32_t)(philox_word0(seed, round, purpose, b, i, w3) >> 40) * (1.0f / 16777216.0f);
 }
 __device__ __forceinline__ uint32_t philox_u32(uint64_t seed, uint64_t round, uint32_t purpose, uint64_t b,
                                                uint64_t i) {

@@ -17,8 +17,11 @@
 //  pass 2      only the rows the bonus needs (target row k, plus draft row k when
 //              k < K, k = the first rejected position) are read again; each wave sums
 //              the residual max(p - q', 0) of its tile.
-//  bonus       one wave per sequence locates the tile where the running sum crosses
-//              u * sum, rescans that tile for the bonus id and does the cache lookup.
+//  bonus       one block per sequence draws the bonus in two levels: the 512-id block
+//              where the running sum of block weights crosses u1 * sum (tile sums
+//              locate its tile, a rescan of that tile the block), then the id of
+//              that block where the block's own running sum crosses u2 times its
+//              weight; then the cache lookup.
 //              At T = 0 pass 2 does not run and a per-sequence kernel takes the argmax.
 // Normalisers, cached masses, Z and every running sum that decides an integer are
 // kept in fp64; per-element terms are fp32 exp2 of an exactly formed exponent.  The
@@ -1207,25 +1210,66 @@ __device__ inline double rescan_vector_sums(const WParams& wp, u32x4 rp, u32x4 r
     return ls;
 }
 
-// Phase 2, after a block barrier: the vector where the running sum (from base, in
-// vector order) first exceeds thr, and run = the sum before it (-1 if none).
-__device__ __forceinline__ int crossing_vector(const BonusShare& sh, double base, double thr, double& run) {
-    run = base;
+// Phase 2, after a block barrier, block level: the draw block of the tile where the
+// running sum of block weights (from base, in id order) first exceeds thr (-1: none).
+template <int DT>
+__device__ __forceinline__ int crossing_block(const BonusShare& sh, double base, double thr) {
+    constexpr int VPB = kVecPerBlock<DT>;
+    double run = base;
+    int bx = -1;
+#pragma unroll
+    for (int k = 0; k < kBlocksPerTile2<DT>; ++k) {
+        double wb = 0.0;
+#pragma unroll
+        for (int v = 0; v < VPB; ++v) wb += sh.tot[k * VPB + v];
+        if (bx < 0) {
+            if (run + wb > thr)
+                bx = k;
+            else
+                run += wb;
+        }
+    }
+    return bx;
+}
+
+// The last draw block of the tile holding a positive weight (-1: none).
+template <int DT>
+__device__ __forceinline__ int last_positive_block(const BonusShare& sh) {
+    int bx = -1;
+#pragma unroll
+    for (int j = 0; j < kVecPass2; ++j)
+        if (sh.lastp[j] >= 0) bx = j / kVecPerBlock<DT>;
+    return bx;
+}
+
+// Id level inside block bx: thr = u2 times the block's weight, the vector of the block
+// where the running sum from the block's first id first exceeds it (-1: none) and
+// run = the sum before that vector.
+template <int DT>
+__device__ __forceinline__ int crossing_vector_in_block(const BonusShare& sh, int bx, double u2, double& run,
+                                                        double& thr) {
+    constexpr int VPB = kVecPerBlock<DT>;
+    double wb = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPB; ++v) wb += sh.tot[bx * VPB + v];
+    thr = u2 * wb;
+    run = 0.0;
     int jx = -1;
 #pragma unroll
-    for (int j = 0; j < kVecPass2; ++j) {
+    for (int v = 0; v < VPB; ++v) {
         if (jx < 0) {
-            if (run + sh.tot[j] > thr)
-                jx = j;
+            if (run + sh.tot[bx * VPB + v] > thr)
+                jx = bx * VPB + v;
             else
-                run += sh.tot[j];
+                run += sh.tot[bx * VPB + v];
         }
     }
     return jx;
 }
 
-// Phase 2, the wave of the crossing vector: the first id whose running sum exceeds thr
-// (recomputing its weights), published in sh.found.
+// Phase 2, the wave of the crossing vector: the first id whose running sum (run before
+// the vector, then the vector's ids in order) exceeds thr, recomputing its weights;
+// published in sh.found.
 template <int DT, int MODE>
 __device__ inline void rescan_vector_find(const WParams& wp, u32x4 rp, u32x4 rq, int64_t t0, int V,
                                           const uint32_t* bits, int j, double ls, double run, double thr,
@@ -1250,10 +1294,15 @@ __device__ inline void rescan_vector_find(const WParams& wp, u32x4 rp, u32x4 rq,
 // Inclusive wave scan of x (fp64, lane order).
 __device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_f64(x); }
 
-// Bonus of one group by one block of four waves: totals over the tiles in tile order
-// and the tile where the running sum crosses u * total (every wave, alike), the id
-// inside it (wave j rescans vector j of that tile), and the cache lookup (wave 0).  The
-// tile sums of the first 64 tiles, the row statistics and the cached ids are requested
+// Bonus (or draft token) of one group by one block of four waves, a draw in two
+// levels.  Block level, uniform u1: totals over the tiles in tile order and the tile
+// where the running sum crosses u1 * total (every wave, alike), then inside it the
+// draw block (512 ids) where the running sum of block weights crosses (wave j
+// recomputes the weights of vector j of that tile).  Id level, uniform u2: the id of
+// that block whose running sum from the block's first id crosses u2 times the block's
+// weight.  Strict ">" in id order; with no crossing (rounding only) the last block,
+// then the last id, of positive weight.  Wave 0 then does the cache lookup.  The tile
+// sums of the first 64 tiles, the row statistics and the cached ids are requested
 // together.
 template <int DT, bool VEC, bool DEVRNG>
 __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
@@ -1267,14 +1316,15 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
     int my_id = -1;
     int mode = pass2_mode(a, pos);
     bool pick_last = false;
-    double gbase = 0.0, thr = 0.0, ls = 0.0;
+    double gbase = 0.0, thr = 0.0, ls = 0.0, u2 = 0.0;
     int64_t t0 = 0;
     WParams wp{};
     u32x4 rp = neg_inf_vec<DT>(), rq = neg_inf_vec<DT>();
     if (valid) {
         const int64_t r = (int64_t)b * (K + 1) + pos;
         const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
-        const double u = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos);
+        const double u = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos, 0);
+        u2 = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos, 1);
         // one chunk of at most 64 tiles (the usual case): the scan that gives the total
         // also locates the crossing
         const double incl_w = nt <= kWave ? wave_scan_incl(v0.x) : 0.0;
@@ -1354,26 +1404,37 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
         else
             ls = rescan_vector_sums<DT, kWQprime>(wp, rp, rq, t0, a.V, my_id, bits, wave, sh);
     }
+    if (threadIdx.x == 0) sh.found = -1;
     __syncthreads();
-    double run = 0.0;
-    const int jx = valid && !pick_last ? crossing_vector(sh, gbase, thr, run) : -1;
+    double run = 0.0, thr2 = 0.0;
+    int bx = -1, jx = -1;
+    if (valid) {
+        bx = pick_last ? -1 : crossing_block<DT>(sh, gbase, thr);
+        if (bx < 0) bx = last_positive_block<DT>(sh);
+        if (bx >= 0) jx = crossing_vector_in_block<DT>(sh, bx, u2, run, thr2);
+    }
     if (jx == wave) {
         if (mode == kWResid)
-            rescan_vector_find<DT, kWResid>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+            rescan_vector_find<DT, kWResid>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr2, sh);
         else if (mode == kWP)
-            rescan_vector_find<DT, kWP>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+            rescan_vector_find<DT, kWP>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr2, sh);
         else
-            rescan_vector_find<DT, kWQprime>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr, sh);
+            rescan_vector_find<DT, kWQprime>(wp, rp, rq, t0, a.V, bits, wave, ls, run, thr2, sh);
     }
     __syncthreads();
     if (wave != 0) return;
     int tok = -1;
     if (valid) {
+        // fallbacks: the last positive id of the crossing vector, else of the block
         int last_pos = -1;
+        if (jx >= 0) {
+            last_pos = sh.lastp[jx];
+        } else if (bx >= 0) {
 #pragma unroll
-        for (int j = 0; j < kVecPass2; ++j) last_pos = max(last_pos, sh.lastp[j]);
+            for (int v = 0; v < kVecPerBlock<DT>; ++v) last_pos = max(last_pos, sh.lastp[bx * kVecPerBlock<DT> + v]);
+        }
         if (last_pos < 0) last_pos = (int)min<int64_t>(t0, a.V - 1);
-        tok = (jx >= 0 && sh.found >= 0) ? sh.found : last_pos;
+        tok = sh.found >= 0 ? sh.found : last_pos;
     }
     if (lane == 0) {
         if (a.mode == 0) {

@@ -3,7 +3,8 @@ the fp64 oracle on the same bits, and compare under the parity rules:
  - integer outputs bit-exact, except on sequences the oracle flags with its own fp64
    values: E1 (|u - p/q'| < 1e-5 at a tested position) and E5 (a tested p or q'
    below 1e-30 from a finite logit) exclude everything from the accepted length on;
-   E2 (u * Z within oracle.CDF_TIE_EPS * Z of a CDF step around the sampled id) and
+   E2 (a uniform of a draw within its per-draw band of a CDF step around its pick, at
+   the block or the id level) and
    E3 (residual mass below 1e-5) exclude the bonus, hit, slot and fallback tokens;
  - probabilities within 1e-5 absolute; row sums within 1e-5 relative; row maxima
    exact (they are input values)."""
