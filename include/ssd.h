@@ -39,9 +39,17 @@
  *    reading it, in a later kernel of the same call.  One workspace serves any
  *    number of calls on one stream; two calls that overlap in time must not share it.
  *  - Uniforms are counter-based: Philox4x64-10 (Salmon et al., SC'11) with key
- *    (seed, purpose) and counter (round, b, i, 0); u = (word0 >> 40) * 2^-24 and
- *    u32 = word0 >> 32.  Purposes: SSD_PURPOSE_*.  Results are reproducible from
- *    (seed, round).
+ *    (seed, purpose) and counter (round, b, i, w); u = (word0 >> 40) * 2^-24 and
+ *    u32 = word0 >> 32.  w = 0 for a test, a fallback token or a draw's first
+ *    uniform u1, w = 1 for a draw's second uniform u2.  Purposes: SSD_PURPOSE_*.
+ *    Results are reproducible from (seed, round).
+ *  - A draw from weights w over ids 0..V-1 (the draft sampler and the bonus) takes
+ *    two steps over blocks of 512 consecutive ids: u1 picks the block, the smallest
+ *    one whose running sum of block weights exceeds u1 times the total; u2 picks the
+ *    id inside it, the smallest one whose running sum from the block's first id
+ *    exceeds u2 times the block's weight.  The law is w / sum(w), as for one inverse
+ *    CDF over all ids; each decision is resolved against its own level's mass.  If
+ *    rounding leaves no crossing, the last block (id) of positive weight is taken.
  */
 #ifndef SSD_H
 #define SSD_H
@@ -128,9 +136,8 @@ ssd_status ssd_build_cache(const ssd_shape* shape, const void* q_logits, const f
  * renormalised:  Z_k = 1 - (1 - C) M_k,  q'_k(x) = q_k(x) (C if x in S_k else 1) / Z_k.
  * Z [B*(K+1)] (fp64) is always written.  The rest is optional (pass NULL to skip):
  *  - q_prime [B, K+1, V] fp32 dense receives q';
- *  - draft [B, K] receives draft tokens sampled from q'_i by inverse CDF with
- *    u = U(seed, round, b, i, DRAFT) (the smallest id whose running sum of q'_i
- *    exceeds u times the total), or argmax z_q at T = 0.
+ *  - draft [B, K] receives draft tokens drawn from q'_i (the two-step draw above,
+ *    with the uniforms of (b, i, DRAFT)), or argmax z_q at T = 0.
  * Both optional outputs need q_logits, q_max, q_sum, q_argmax (T = 0), F_host, Bf,
  * cache_ids; draft also needs ws. */
 ssd_status ssd_saguaro_reweight(const ssd_shape* shape, const double* cache_mass, float C, double* Z,
@@ -157,9 +164,9 @@ ssd_status ssd_verify(const ssd_shape* shape, const void* p_logits, const void* 
 /* ssd_residual_sample -- the bonus token ([zh] section 2 flow step 2 and Challenge 2:
  * the bonus comes from the residual distribution; [nl] section 3 B).  With
  * k = accept_len[b]:  k < K: w(x) = max(p_k(x) - q'_k(x), 0) (w = p_k if the fp64 sum of
- * these weights is not above 0, which only rounding can cause);  k = K: w = p_K.  bonus[b] = the smallest id whose running sum of w
- * exceeds u * sum(w), u = U(seed, round, b, k, BONUS).  At T = 0 the bonus is
- * argmax p_k (p_argmax required).  resid_mass (nullable [B], fp64) receives sum(w).
+ * these weights is not above 0, which only rounding can cause);  k = K: w = p_K.
+ * bonus[b] is drawn from w (the two-step draw above, with the uniforms of
+ * (b, k, BONUS)).  At T = 0 the bonus is argmax p_k (p_argmax required).  resid_mass (nullable [B], fp64) receives sum(w).
  * The running sums that locate the bonus are kept in fp64. */
 ssd_status ssd_residual_sample(const ssd_shape* shape, const void* p_logits, const void* q_logits,
                                const float* p_max, const double* p_sum, const int32_t* p_argmax,
