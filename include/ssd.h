@@ -292,6 +292,25 @@ ssd_status ssd_round_devrng(const ssd_shape* shape, const void* p_logits, const 
                             const uint64_t* round_dev, int32_t fallback, const ssd_round_out* out,
                             const ssd_round_events* events, void* ws, size_t ws_bytes, void* stream);
 
+/* ssd_round_noalloc -- ssd_round for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace: the round's scratch is a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until the
+ * process ends.  The first call on a GPU looks up that GPU's copy
+ * (hipGetSymbolAddress, with the stream's device current); no call allocates or frees
+ * anything.  A shape whose ssd_workspace_bytes(shape, Bf) exceeds the array returns
+ * SSD_ERR_WORKSPACE (text in ssd_last_error()) before any launch.  The array keeps
+ * the last call's contents; the round writes every part of it it reads, so nothing
+ * needs clearing.  Every call on one GPU uses the same array: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads) race and
+ * must not be made.  Arguments, outputs, results and errors are otherwise those of
+ * ssd_round (bit-identical for the same inputs). */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+ssd_status ssd_round_noalloc(const ssd_shape* shape, const void* p_logits, const void* q_logits,
+                             const int32_t* draft, const int32_t* F_host, int32_t Bf, float C, ssd_rng rng,
+                             int32_t fallback, const ssd_round_out* out, const ssd_round_events* events,
+                             void* stream);
+
 /* ---------------------------------------------------------------------------
  * Choosing the fan-out from measured coverage.  [zh] section 2 Challenge 1 and [nl]
  * section 3 A say the fan-out solves a constrained optimisation over acceptance

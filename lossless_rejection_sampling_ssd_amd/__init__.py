@@ -23,10 +23,11 @@ SSD_FALLBACK_NONE, SSD_FALLBACK_UNIFORM = 0, 1
 SSD_DEVERR_TOKEN_RANGE, SSD_DEVERR_QPRIME_ZERO, SSD_DEVERR_LEN_RANGE, SSD_DEVERR_SLOT_RANGE = 1, 2, 4, 8
 SSD_DEVERR_HIST_RANGE = 16
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_NGRAM = 16, 64, 16
+SSD_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 EXPORTED = ("ssd_fanout", "ssd_workspace_bytes", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight",
             "ssd_verify", "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback",
-            "ssd_round", "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose",
+            "ssd_round", "ssd_round_devrng", "ssd_round_noalloc", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose",
             "ssd_fallback_critical_batch", "ssd_stream_read", "ssd_status_string", "ssd_last_error")
 
 
@@ -87,6 +88,8 @@ def _load():
                             ctypes.POINTER(ssd_round_events), _P, sz, _P]
     L.ssd_round_devrng.argtypes = [S, _P, _P, _P, _P, i32, f32, u64, _P, i32, ctypes.POINTER(ssd_round_out),
                                    ctypes.POINTER(ssd_round_events), _P, sz, _P]
+    L.ssd_round_noalloc.argtypes = [S, _P, _P, _P, _P, i32, f32, ssd_rng, i32, ctypes.POINTER(ssd_round_out),
+                                    ctypes.POINTER(ssd_round_events), _P]
     L.ssd_bonus_rank.argtypes = [S, _P, _P, _P, i32, _P, _P, _P, sz, _P]
     L.ssd_fanout_optimize.argtypes = [i32, i32, i32, i32, _P, _P, _P, _P]
     FM = ctypes.POINTER(ssd_fallback_model)
@@ -99,7 +102,7 @@ def _load():
     L.ssd_last_error.restype = ctypes.c_char_p
     for name in ("ssd_fanout", "ssd_softmax", "ssd_build_cache", "ssd_saguaro_reweight", "ssd_verify",
                  "ssd_residual_sample", "ssd_cache_lookup", "ssd_cache_gather", "ssd_ngram_fallback", "ssd_round",
-                 "ssd_round_devrng", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
+                 "ssd_round_devrng", "ssd_round_noalloc", "ssd_bonus_rank", "ssd_fanout_optimize", "ssd_fallback_choose", "ssd_fallback_critical_batch",
                  "ssd_stream_read"):
         getattr(L, name).restype = i32
     return L
@@ -426,6 +429,19 @@ def ssd_round_devrng(shape, p_logits, q_logits, draft, F, C, seed, round_dev, fa
                                  float(C), int(seed), _ptr(round_dev, torch.int64, "round_dev"), int(fallback),
                                  ctypes.byref(out), ctypes.byref(events) if events is not None else None, w, nb,
                                  _stream(stream)), "ssd_round_devrng")
+
+
+def ssd_round_noalloc(shape, p_logits, q_logits, draft, F, C, seed, round_, fallback, out: ssd_round_out,
+                      events: Optional[ssd_round_events] = None, stream=None):
+    """ssd_round with its scratch in the library's static per-GPU array (no workspace,
+    nothing allocated); calls that overlap in time on one GPU race."""
+    st = _lib.ssd_round_noalloc(ctypes.byref(shape), _logit_ptr(p_logits, "p_logits"),
+                                _logit_ptr(q_logits, "q_logits"), _ptr(draft, torch.int32, "draft"), _host_F(F),
+                                int(sum(F)), float(C), ssd_rng(seed, round_), int(fallback), ctypes.byref(out),
+                                ctypes.byref(events) if events is not None else None, _stream(stream))
+    if st == SSD_ERR_WORKSPACE:
+        raise SSDError(st, "ssd_round_noalloc", _lib.ssd_last_error().decode())
+    _check(st, "ssd_round_noalloc")
 
 
 # ---------------------------------------------------------------------------- convenience

@@ -1,12 +1,15 @@
 // ssd_api.hip -- the C ABI (include/ssd.h): host-side validation, workspace layout
-// and kernel launches.  No allocation, no synchronisation, no state.
+// and kernel launches.  No allocation, no synchronisation; the only state is the
+// per-GPU address of the no-allocation round's static scratch array.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ssd.h"
 #include "ssd_kernels.h"
@@ -127,11 +130,54 @@ void fill_fo(ssd::Pass2Args& a, const int32_t* F, const int* O, int K1) {
 
 int zeros_F[SSD_MAX_K + 1] = {0};
 
+// Scratch of ssd_round_noalloc: one copy per GPU, looked up once per device.  In host
+// code `scratch` names a host-side stand-in, never the device memory: only the
+// address hipGetSymbolAddress returns (kept in g_scratch) is handed to kernels.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
 void set_ws(ssd::Pass1Args& a, void* ws, const Layout& L) {
     a.nt = L.nt;
     a.cap = L.cap;
     a.part = at<ssd::WavePartial>(ws, L.part);
     a.cand = at<uint64_t>(ws, L.cand);
+}
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The device address of this GPU's copy of `scratch` (the device of `stream`, or the
+// current one for the null stream), looked up on the first call on that GPU.
+ssd_status scratch_for(hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "ssd_round_noalloc device");
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return fail_hip(e, "ssd_round_noalloc device");
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "ssd_round_noalloc device");
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (e != hipSuccess) return fail_hip(e, "ssd_round_noalloc scratch lookup");
+            if (e2 != hipSuccess) return fail_hip(e2, "ssd_round_noalloc device");
+            if (!p || ((uintptr_t)p % kAlign) != 0) {
+                snprintf(g_last_error, sizeof(g_last_error), "ssd_round_noalloc: scratch address %p unusable", p);
+                return SSD_ERR_HIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SSD_OK;
 }
 
 }  // namespace
@@ -502,13 +548,13 @@ ssd_status ssd_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* 
 
 // The fused round; round_dev (nullable) replaces rng.round by a counter the kernels read
 // from device memory when they run.
-static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
-                             const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, const uint64_t* round_dev,
-                             int32_t fallback, const ssd_round_out* out, const ssd_round_events* ev, void* ws,
-                             size_t ws_bytes, void* stream) {
+// Argument checks of the fused round (everything but the workspace); O receives the
+// fan-out offsets.
+static ssd_status round_check(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                              const int32_t* F_host, int32_t Bf, float C, int32_t fallback, const ssd_round_out* out,
+                              int* O) {
     ssd_status st = check_shape(s);
     if (st != SSD_OK) return st;
-    int O[SSD_MAX_K + 2];
     if ((st = check_fanout(s, F_host, Bf, O)) != SSD_OK) return st;
     if (!p_logits || !q_logits || !draft || !out || !(C > 0.f) || !(C <= 1.f)) return SSD_ERR_ARG;
     if (fallback != SSD_FALLBACK_NONE && fallback != SSD_FALLBACK_UNIFORM) return SSD_ERR_ARG;
@@ -516,6 +562,16 @@ static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const voi
         !out->fallback_tokens)
         return SSD_ERR_ARG;
     if (out->next_draft && Bf > 0 && !out->cache_values) return SSD_ERR_ARG;
+    return SSD_OK;
+}
+
+static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                             const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, const uint64_t* round_dev,
+                             int32_t fallback, const ssd_round_out* out, const ssd_round_events* ev, void* ws,
+                             size_t ws_bytes, void* stream) {
+    int O[SSD_MAX_K + 2];
+    ssd_status st = round_check(s, p_logits, q_logits, draft, F_host, Bf, C, fallback, out, O);
+    if (st != SSD_OK) return st;
     Layout L;
     if ((st = check_ws(s, Bf, ws, ws_bytes, &L)) != SSD_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
@@ -652,6 +708,26 @@ ssd_status ssd_round(const ssd_shape* s, const void* p_logits, const void* q_log
                      const ssd_round_out* out, const ssd_round_events* ev, void* ws, size_t ws_bytes, void* stream) {
     return round_impl(s, p_logits, q_logits, draft, F_host, Bf, C, rng, nullptr, fallback, out, ev, ws, ws_bytes,
                       stream);
+}
+
+ssd_status ssd_round_noalloc(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,
+                             const int32_t* F_host, int32_t Bf, float C, ssd_rng rng, int32_t fallback,
+                             const ssd_round_out* out, const ssd_round_events* ev, void* stream) {
+    int O[SSD_MAX_K + 2];
+    ssd_status st = round_check(s, p_logits, q_logits, draft, F_host, Bf, C, fallback, out, O);
+    if (st != SSD_OK) return st;
+    Layout L;
+    layout_for(s, Bf, &L);
+    if (L.total > SSD_NOALLOC_SCRATCH_BYTES) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "ssd_round_noalloc: the round needs %zu bytes of scratch, the static array holds %zu", L.total,
+                 (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+        return SSD_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    if ((st = scratch_for((hipStream_t)stream, &ws)) != SSD_OK) return st;
+    return round_impl(s, p_logits, q_logits, draft, F_host, Bf, C, rng, nullptr, fallback, out, ev, ws,
+                      SSD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 ssd_status ssd_round_devrng(const ssd_shape* s, const void* p_logits, const void* q_logits, const int32_t* draft,

@@ -155,6 +155,22 @@ def test_cache_and_round_validation(ssd):
                        ws, 1 << 30, None) == ssd.SSD_ERR_ARG
     assert L.ssd_round(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0, ctypes.byref(out), None,
                        ws, 64, None) == ssd.SSD_ERR_WORKSPACE
+    # no-allocation round: the round's own checks come first; a shape whose scratch
+    # exceeds the static array is refused before any HIP call, with both sizes
+    assert L.ssd_round_noalloc(ctypes.byref(s), BAD, BAD, None, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 0,
+                               ctypes.byref(out), None, None) == ssd.SSD_ERR_ARG
+    assert L.ssd_round_noalloc(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, ssd.ssd_rng(0, 0), 9,
+                               ctypes.byref(out), None, None) == ssd.SSD_ERR_ARG
+    huge = _shape(ssd, B=1024, K=8, V=128256, dtype=ssd.SSD_BF16)
+    hF = _F([20, 14, 10, 7, 5, 3, 2, 2, 1])
+    need = L.ssd_workspace_bytes(ctypes.byref(huge), 64)
+    assert need > ssd.SSD_NOALLOC_SCRATCH_BYTES
+    assert L.ssd_round_noalloc(ctypes.byref(huge), BAD, BAD, BAD, hF, 64, 0.5, ssd.ssd_rng(0, 0), 0,
+                               ctypes.byref(out), None, None) == ssd.SSD_ERR_WORKSPACE
+    msg = L.ssd_last_error().decode()
+    assert str(need) in msg and str(ssd.SSD_NOALLOC_SCRATCH_BYTES) in msg, msg
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", open(HEADER).read())
+    assert m and int(m.group(1)) << 20 == ssd.SSD_NOALLOC_SCRATCH_BYTES
     # device-side round counter: required
     assert L.ssd_round_devrng(ctypes.byref(s), BAD, BAD, BAD, good_F, 8, 0.5, 1, None, 0, ctypes.byref(out), None,
                               ws, 1 << 30, None) == ssd.SSD_ERR_ARG
