@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import lossless_rejection_sampling_ssd_amd as ssd
-from lossless_rejection_sampling_ssd_amd.workloads import to_oracle_array
+from parity_cases import oracle_draft  # noqa: F401  (the harness's draft sampler)
 
 PROB_ATOL = 1e-5
 SUM_RTOL = 1e-5
@@ -21,14 +21,6 @@ SUM_RTOL = 1e-5
 
 def dev(t):
     return t.to("cuda")
-
-
-def oracle_draft(zp_np, zq_np, T, F, C, seed, rnd, b_base=0):
-    """Draft tokens sampled by the oracle from its own q' (harness step)."""
-    ids, mass = oracle.build_cache(zq_np, T, F)
-    Z, _ = oracle.saguaro(zq_np, T, F, ids, mass, C)
-    d, flags = oracle.draft_sample(zq_np, T, F, ids, Z, C, seed, rnd, b_base)
-    return d, flags
 
 
 def gpu_round(zp, zq, T, F, C, draft, seed, rnd, fallback, ws=None, values=None):

@@ -1,14 +1,28 @@
 """Parity of the HIP path (called through the C ABI) with the fp64 oracle on seeded
 synthetic inputs.  Each test prints what names its case before the GPU step."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import lossless_rejection_sampling_ssd_amd as ssd
-from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_logits, scaled, to_oracle_array
+from lossless_rejection_sampling_ssd_amd.workloads import to_oracle_array
 
 from gpu_helpers import PROB_ATOL, SUM_RTOL, compare_round, gpu_round, oracle_draft
+import parity_cases as pc
+from parity_cases import rand_logits as _rand
+
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "flag_counts.json")) as _fh:
+    FLAGS = json.load(_fh)["cases"]
+
+
+def _check_flags(label, flagged):
+    """The number of sequences the oracle flagged equals the stored count
+    (tests/golden/flag_counts.json, written from the oracle alone)."""
+    assert flagged == FLAGS[label]["flagged"], (label, flagged, FLAGS[label])
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -16,21 +30,6 @@ pytestmark = [pytest.mark.gpu,
 
 def _case(msg):
     print("\n[case] " + msg, flush=True)
-
-
-def _rand(B, K, V, dtype, seed, scale=2.0, noise=0.8, ld=None):
-    g = torch.Generator().manual_seed(seed)
-    zq = torch.randn((B, K + 1, V), generator=g) * scale
-    zp = zq + torch.randn((B, K + 1, V), generator=g) * noise
-    dt = torch.float32 if dtype == "f32" else torch.bfloat16
-    zq, zp = zq.to(dt), zp.to(dt)
-    if ld is not None and ld > V:
-        def pad(z):
-            o = torch.full((B, K + 1, ld), float("nan"), dtype=dt)
-            o[:, :, :V] = z
-            return o[:, :, :V]
-        zq, zp = pad(zq), pad(zp)
-    return zq, zp
 
 
 def _to_dev(z):
@@ -218,46 +217,17 @@ def test_round_vs_oracle_and_chain(case):
         assert np.array_equal(g[k], g2[k]), ("determinism", label, k)
 
 
-EDGE_CASES = [
-    # (label, dtype, B, K, V, T, F, C, scale, noise, quantum)
-    # F_k at its maximum, with coarse (heavily tied) draft logits: many tied candidates
-    # per tile, the histogram select and the exact per-tile fallback
-    ("F=64 ties", "bf16", 3, 2, 50000, 1.0, [64, 0, 0], 0.5, 1.0, 0.3, 0.5),
-    ("F=64 smooth", "f32", 4, 1, 70001, 1.0, [64, 0], 0.3, 2.0, 0.5, 0.0),
-    ("peaked T=0.05", "bf16", 6, 3, 20000, 0.05, [8, 4, 2, 1], 0.5, 2.0, 0.5, 0.0),
-    ("flat T=5", "f32", 6, 3, 20000, 5.0, [8, 4, 2, 1], 0.5, 2.0, 0.5, 0.0),
-    ("large logits", "f32", 5, 2, 9000, 1.0, [6, 3, 1], 0.5, 3000.0, 20.0, 0.0),
-    ("all tied", "bf16", 4, 2, 6000, 1.0, [5, 3, 1], 0.5, 0.0, 0.0, 0.0),
-    # more than 64 tiles per row (pass 1: 4096 bf16 / 2048 fp32 elements per tile):
-    # the finalisation's general path and the bonus's multi-chunk scans
-    ("V=300k bf16", "bf16", 3, 2, 300001, 1.0, [12, 6, 3], 0.5, 2.0, 0.5, 0.0),
-    ("V=200k f32", "f32", 2, 3, 200003, 0.8, [9, 5, 3, 2], 0.6, 2.0, 0.5, 0.0),
-]
-
-
-@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: c[0])
-def test_round_edge_cases(case):
+@pytest.mark.parametrize("label", [c[0] for c in pc.EDGE_CASES])
+def test_round_edge_cases(label):
     """The fused round against the oracle at the edges of the method: the largest
     fan-out share, heavy ties, near-greedy and flat temperatures, large logits, and
-    rows where every logit is equal."""
-    label, dtype, B, K, V, T, F, C, scale, noise, quantum = case
+    rows where every logit is equal; the first and the last draft token forced to
+    ids 0 and V - 1."""
     _case("edge " + label)
-    g = torch.Generator().manual_seed(sum(map(ord, label)))
-    zq = torch.randn((B, K + 1, V), generator=g) * scale
-    if quantum > 0:
-        zq = torch.round(zq / quantum) * quantum
-    zp = zq + torch.randn((B, K + 1, V), generator=g) * noise
-    dt = torch.float32 if dtype == "f32" else torch.bfloat16
-    zq, zp = zq.to(dt), zp.to(dt)
-    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
-    seed, rnd = 0xED6E + B, 5
-    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
-    draft[0, 0] = 0
-    draft[-1, -1] = V - 1
-    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, 1)
-    g_ = gpu_round(zp.cuda(), zq.cuda(), T, F, C, draft, seed, rnd, 1)
-    flagged = compare_round(g_, o, K, sum(F), label=label)
-    assert flagged < B, (label, flagged)  # the forced edge tokens may be flagged; the rest are compared
+    c = pc.edge_case(label)
+    o = c.oracle_round()
+    g_ = gpu_round(c.zp.cuda(), c.zq.cuda(), c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback)
+    _check_flags(label, compare_round(g_, o, c.K, sum(c.F), label=label))
 
 
 def test_forced_paths():
@@ -424,59 +394,37 @@ def test_residual_bad_len_and_greedy():
 
 # ----------------------------------------------------------------------------- workloads
 def test_c1_rounds():
-    """The single-sequence workload: every round with its own logits and counter."""
-    w = WORKLOADS["c1"]
-    F, gap = oracle.fanout(w.K, w.Bf, w.r)
+    """The single-sequence workload: all of its rounds, each with its own logits and
+    counter."""
     flagged = 0
-    n = 300
     ws = ssd.Workspace()
-    for rnd in range(n):
+    for rnd in range(pc.C1_ROUNDS):
         if rnd % 100 == 0:
             _case("c1 round %d" % rnd)
-        zq, zp = make_logits(w, buffer=rnd)
-        zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
-        draft, _ = oracle_draft(zp_np, zq_np, 1.0, F, 0.5, w.seed, rnd)
-        o = oracle.round_(zp_np, zq_np, 1.0, F, 0.5, draft, w.seed, rnd, False, gap)
-        g = gpu_round(zp.cuda(), zq.cuda(), 1.0, F.tolist(), 0.5, draft, w.seed, rnd, 0, ws=ws)
-        flagged += compare_round(g, o, w.K, w.Bf, label="c1 round %d" % rnd)
-    assert flagged <= max(1, n // 100)
+        c = pc.c1_case(rnd)
+        o = c.oracle_round()
+        g = gpu_round(c.zp.cuda(), c.zq.cuda(), c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, ws=ws)
+        flagged += compare_round(g, o, c.K, sum(c.F), label=c.label)
+    _check_flags("c1 rounds", flagged)
+    assert flagged <= max(1, pc.C1_ROUNDS // 1000)
 
 
-@pytest.mark.parametrize("name,C,sig,V", [("c3", 0.5, None, None), ("c4", 0.2, 1.65, None), ("c4", 0.8, 0.3, None),
-                                          ("c5", 0.5, None, None), ("c3", 0.5, None, 128257)])
-def test_full_size_sampled(name, C, sig, V):
-    """The workload at its full size in the launch configuration the benchmark
-    times; the oracle recomputes a sample of sequences one by one (their uniforms
-    keep the global sequence index).  V = 128257: the headline shape with an odd
-    vocabulary, so every row after the first starts off a 16-byte boundary."""
-    w = WORKLOADS[name] if V is None else scaled(WORKLOADS[name], V=V)
-    T = w.temps[0]
-    _case("full-size %s C=%g sigma=%s: generate" % (name, C, sig))
-    zq, zp = make_logits(w, target_sigma=sig, device="cuda")
-    F, gap = oracle.fanout(w.K, w.Bf, w.r)
-    rng = np.random.default_rng(w.seed)
-    sample = np.sort(rng.choice(w.B, size=6, replace=False))
-    seed, rnd = w.seed, 1
-    draft = rng.integers(0, w.V, size=(w.B, w.K)).astype(np.int32)
-    zp_h, zq_h = zp.cpu(), zq.cpu()
-    per = {}
-    for b in sample:
-        zp_np = to_oracle_array(zp_h[b:b + 1])
-        zq_np = to_oracle_array(zq_h[b:b + 1])
-        d, _ = oracle_draft(zp_np, zq_np, T, F, C, seed, rnd, b_base=int(b))
-        draft[b] = d[0]
-        per[int(b)] = (zp_np, zq_np)
-    _case("full-size %s: GPU round" % name)
-    values = rng.integers(0, w.V, size=(w.B, w.Bf, w.K)).astype(np.int32)
-    g = gpu_round(zp, zq, T, F.tolist(), C, draft, seed, rnd, int(w.fallback_uniform), values=values)
-    _case("full-size %s: oracle on %s" % (name, sample.tolist()))
-    for b in sample:
-        zp_np, zq_np = per[int(b)]
-        o = oracle.round_(zp_np, zq_np, T, F, C, draft[b:b + 1], seed, rnd, w.fallback_uniform, gap, int(b))
-        K1 = w.K + 1
-        gb = {k: (v[b * K1:(b + 1) * K1] if v.ndim == 1 and v.shape[0] == w.B * K1 else v[b:b + 1])
-              for k, v in g.items()}
-        compare_round(gb, o, w.K, w.Bf, label="%s b=%d" % (name, b), values=values[b:b + 1])
+@pytest.mark.parametrize("label", [c[0] for c in pc.FULL_CASES])
+def test_full_size_whole_batch(label):
+    """A workload's whole batch at its full size, in the launch configuration the
+    benchmark times, against the oracle sequence by sequence (c4 at three of its
+    (target spread, C) points, c2 on its own recipe at each temperature).  c3 odd V:
+    V = 128257, so every row after the first starts off a 16-byte boundary.  At most
+    max(1, 1e-3 B) sequences may be flagged; the count must equal the stored one."""
+    _case("full-size %s: inputs and oracle" % label)
+    c = pc.full_case(label)
+    w, F = c.w, np.array(c.F)
+    o = c.oracle_round()
+    _case("full-size %s: GPU round" % label)
+    g = gpu_round(c.zp.cuda(), c.zq.cuda(), c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, values=c.values)
+    flagged = compare_round(g, o, w.K, w.Bf, label=label, values=c.values)
+    _check_flags(label, flagged)
+    assert flagged <= max(1, w.B // 1000), (label, flagged)
     # properties that hold for every sequence
     assert np.all((g["accept_len"] >= 0) & (g["accept_len"] <= w.K))
     assert np.all((g["bonus"] >= 0) & (g["bonus"] < w.V))
@@ -484,130 +432,54 @@ def test_full_size_sampled(name, C, sig, V):
     for b in range(w.B):
         k = g["accept_len"][b]
         S = g["cache_ids"][b, O[k]:O[k + 1]]
-        h = g["bonus"][b] in S
-        assert g["hit"][b] == h
-        if not h and w.fallback_uniform:
-            assert np.all((g["fallback_tokens"][b] >= 0) & (g["fallback_tokens"][b] < w.V))
-    nd, _ = oracle.cache_gather(values, g["hit"], g["slot"], g["fallback_tokens"])
-    assert np.array_equal(g["next_draft"], nd)
+        assert g["hit"][b] == (g["bonus"][b] in S)
     assert np.all(g["dev_err"] == 0)
-    # coverage statistics of this round: the bonus ranks below F_k exactly on a hit
-    _case("full-size %s: bonus rank" % name)
+    # coverage statistics of this round: the bonus ranks below F_k exactly on a hit,
+    # and every rank equals the oracle's
+    _case("full-size %s: bonus rank" % label)
+    zq = c.zq.cuda()
     rank = torch.zeros(w.B, dtype=torch.int32, device="cuda")
     hist = torch.zeros((w.K + 1, 65), dtype=torch.int32, device="cuda")
     acc_d = torch.as_tensor(g["accept_len"], device="cuda")
-    ssd.ssd_bonus_rank(ssd.shape_of(zq, T), zq, acc_d, torch.as_tensor(g["bonus"], device="cuda"), 64, rank, hist)
+    ssd.ssd_bonus_rank(ssd.shape_of(zq, c.T), zq, acc_d, torch.as_tensor(g["bonus"], device="cuda"), 64, rank, hist)
     torch.cuda.synchronize()
     rk = rank.cpu().numpy()
     assert np.array_equal(rk < F[g["accept_len"]], g["hit"] == 1)
     assert int(hist.sum()) == w.B
-    for b in sample:
-        orank, _ = oracle.bonus_rank(per[int(b)][1], g["accept_len"][b:b + 1], g["bonus"][b:b + 1], 64)
-        assert rk[b] == orank[0], (name, b)
+    orank, _ = oracle.bonus_rank(c.zq_np, g["accept_len"], g["bonus"], 64)
+    assert np.array_equal(rk, orank), label
 
 
-MASK_CASES = [
-    # (label, dtype, B, K, V, T, F, C, frac_shared, frac_target_only, n_finite_row0)
-    # a vocabulary mask shared by both models (banned ids)
-    ("shared mask", "bf16", 6, 3, 30000, 1.0, [10, 6, 3, 1], 0.5, 0.5, 0.0, 0),
-    # ids only the target masks: the draft proposes tokens of target probability 0
-    ("target-only mask", "f32", 6, 3, 20000, 1.0, [8, 4, 2, 1], 0.5, 0.0, 0.3, 0),
-    # a row with fewer finite ids than F_0 (the cache takes -inf ids, lower id first)
-    ("F above finite ids", "bf16", 4, 2, 9000, 0.8, [20, 4, 2], 0.4, 0.2, 0.1, 7),
-    # greedy with masks
-    ("masked greedy", "f32", 5, 3, 12000, 0.0, [6, 3, 2, 1], 0.5, 0.4, 0.2, 0),
-]
-
-
-@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: c[0])
-def test_round_masked_vocabulary(case):
+@pytest.mark.parametrize("label", [c[0] for c in pc.MASK_CASES])
+def test_round_masked_vocabulary(label):
     """-inf logits (masked ids) in the fused round against the oracle: shared masks,
     target-only masks (draft tokens the target forbids are rejected with ratio 0),
     and a draft row with fewer finite ids than its cache share."""
-    label, dtype, B, K, V, T, F, C, f_shared, f_target, n_fin = case
     _case("mask " + label)
-    g = torch.Generator().manual_seed(sum(map(ord, label)))
-    zq = torch.randn((B, K + 1, V), generator=g) * 2.0
-    zp = zq + torch.randn((B, K + 1, V), generator=g) * 0.7
-    shared = torch.rand((B, K + 1, V), generator=g) < f_shared
-    target = torch.rand((B, K + 1, V), generator=g) < f_target
-    zq[shared] = float("-inf")
-    zp[shared | target] = float("-inf")
-    # every row keeps one finite id in both models
-    zq[:, :, 123 % V] = 1.0
-    zp[:, :, 123 % V] = 1.0
-    if n_fin:
-        keep = torch.randperm(V, generator=g)[:n_fin]
-        row = torch.full((V,), float("-inf"))
-        row[keep] = torch.randn(n_fin, generator=g)
-        zq[0, 0] = row
-        zp[0, 0] = row + 0.1
-    dt = torch.float32 if dtype == "f32" else torch.bfloat16
-    zq, zp = zq.to(dt), zp.to(dt)
-    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
-    seed, rnd = 0x3A5C + B, 2
-    draft, _ = oracle_draft(zp_np, zq_np, T, np.array(F, np.int32), C, seed, rnd)
-    o = oracle.round_(zp_np, zq_np, T, np.array(F, np.int32), C, draft, seed, rnd, 1)
-    values = np.random.default_rng(B).integers(0, V, (B, sum(F), K)).astype(np.int32)
-    g_ = gpu_round(zp.cuda(), zq.cuda(), T, F, C, draft, seed, rnd, 1, values=values)
-    flagged = compare_round(g_, o, K, sum(F), label=label, values=values)
-    assert flagged <= B // 2, (label, flagged)
+    c = pc.mask_case(label)
+    o = c.oracle_round()
+    g_ = gpu_round(c.zp.cuda(), c.zq.cuda(), c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, values=c.values)
+    _check_flags(label, compare_round(g_, o, c.K, sum(c.F), label=label, values=c.values))
 
 
-def _random_round_config(i):
-    """Seeded random configuration i: dtype, shape, row padding, temperature, an
-    arbitrary fan-out (any split of B_f with 0 <= F_k <= 64, not only geometric), C,
-    the fallback mode and, for about a quarter of them, a fraction of ids masked
-    (-inf) in both models."""
-    rng = np.random.default_rng(0xC0FFEE + i)
-    dtype = "bf16" if rng.random() < 0.6 else "f32"
-    B = int(rng.integers(1, 9))
-    K = int(rng.integers(1, 11))
-    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 9000)), int(rng.integers(9000, 60000))]))
-    pad = int(rng.choice([0, 0, int(rng.integers(1, 40))]))
-    T = float(rng.choice([0.0, 0.5, 1.0, 1.0, 1.6]))
-    Fmax = min(V, 64)
-    F = [int(rng.integers(0, min(Fmax, 24) + 1)) if rng.random() < 0.8 else 0 for _ in range(K + 1)]
-    C = float(rng.choice([1.0, float(rng.uniform(0.05, 1.0))]))
-    fb = int(rng.integers(0, 2))
-    scale = float(rng.uniform(0.5, 4.0))
-    noise = float(rng.uniform(0.1, 1.5))
-    mask = float(rng.uniform(0.1, 0.6)) if rng.random() < 0.25 else 0.0
-    return dtype, B, K, V, pad, T, F, C, fb, scale, noise, mask
-
-
-@pytest.mark.parametrize("i", range(96))
+@pytest.mark.parametrize("i", range(pc.N_RANDOM))
 def test_round_random_configs(i):
     """The fused round against the oracle (and against itself chained through the six
     separate calls) over 96 seeded random configurations, row strides above V and
     masked vocabularies included."""
-    dtype, B, K, V, pad, T, F, C, fb, scale, noise, mask = _random_round_config(i)
-    label = "random %d: %s B=%d K=%d V=%d pad=%d T=%g F=%s C=%.3f fb=%d mask=%.2f" % (
-        i, dtype, B, K, V, pad, T, F, C, fb, mask)
-    _case(label)
-    zq, zp = _rand(B, K, V, dtype, 0xAB00 + i, scale, noise, ld=V + pad if pad else None)
-    if mask > 0:
-        g = torch.Generator().manual_seed(0xAB00 + i)
-        m = torch.rand((B, K + 1, V), generator=g) < mask
-        m[:, :, 0] = False  # every row keeps a finite id
-        zq[m] = float("-inf")
-        zp[m] = float("-inf")
-    seed, rnd = 0x5EED + i, 100 + i
-    zp_np, zq_np = to_oracle_array(zp), to_oracle_array(zq)
-    Fa = np.array(F, np.int32)
-    draft, _ = oracle_draft(zp_np, zq_np, T, Fa, C, seed, rnd)
-    o = oracle.round_(zp_np, zq_np, T, Fa, C, draft, seed, rnd, fb)
-    zpd, zqd = _to_dev(zp), _to_dev(zq)
-    Bf = sum(F)
-    values = np.random.default_rng(i).integers(0, V, (B, max(Bf, 1), K)).astype(np.int32)[:, :Bf]
-    g = gpu_round(zpd, zqd, T, F, C, draft, seed, rnd, fb, values=values if Bf > 0 else None)
-    compare_round(g, o, K, Bf, label=label, values=values if Bf > 0 else None)
-    ch = _chain(zpd, zqd, T, F, C, draft, seed, rnd, fb)
+    c = pc.random_case(i)
+    _case(c.label)
+    zpd, zqd = _to_dev(c.zp), _to_dev(c.zq)
+    Bf = sum(c.F)
+    o = c.oracle_round()
+    g = gpu_round(zpd, zqd, c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, values=c.values)
+    _check_flags(c.label, compare_round(g, o, c.K, Bf, label=c.label, values=c.values))
+    ch = _chain(zpd, zqd, c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback)
     for k in ch:
         a, b = g[k], ch[k]
         if k == "cache_ids":
             a, b = a[:, :Bf], b[:, :Bf]
-        assert np.array_equal(a, b), (label, k)
+        assert np.array_equal(a, b), (c.label, k)
 
 
 UNALIGNED_CASES = [
