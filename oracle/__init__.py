@@ -56,10 +56,16 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library; LRS_ORACLE_LIB names another build of ssd_oracle.c to load
+    instead (the sanitizer test's instrumented one)."""
     global _lib
     if _lib is None:
-        build()
-        _lib = load_library(_LIB_PATH)
+        other = os.environ.get("LRS_ORACLE_LIB")
+        if other:
+            _lib = load_library(other)
+        else:
+            build()
+            _lib = load_library(_LIB_PATH)
     return _lib
 
 
