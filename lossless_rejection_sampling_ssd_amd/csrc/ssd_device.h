@@ -360,6 +360,10 @@ __device__ __forceinline__ int lanes_below(bool p) {
 // single rounding and partial sums under different offsets merge exactly by
 // ldexp.  o(-inf) = 0 (such a partial has no mass).
 __device__ __forceinline__ float offset_of(float m, float c) { return m == -INFINITY ? 0.f : rintf(m * c); }
+// max(a, b, c) for non-NaN operands, as one v_maximum3_f32 (no canonicalisation).
+__device__ __forceinline__ float fmax3_nan(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 __device__ __forceinline__ float term(float z, float c, float o) { return __builtin_amdgcn_exp2f(fmaf(z, c, -o)); }
 
 // Sum of 2^{z c - o(M)} for the union of two partials (m1, s1), (m2, s2) whose sums are
@@ -453,6 +457,36 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
 // With max_bits below 32 only the max_bits highest bits in which the keys differ are
 // resolved and the rest are left 0: a lower bound of the F-th largest key that still
 // has at least F keys at or above it.
+// The F-th largest of the nonzero keys the wave holds in R registers per lane (0 when at
+// most F are nonzero), by the same most-significant-bit-first search over the bits
+// where the keys differ.
+template <int R>
+__device__ inline uint32_t wave_select_regs_u32(const uint32_t (&k)[R], int F) {
+    int n = 0;
+    uint32_t orv = 0u, andv = ~0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        n += wave_popc(k[r] != 0u);
+        orv |= k[r];
+        andv &= k[r] ? k[r] : ~0u;
+    }
+    if (n <= F) return 0u;
+    orv = wave_or_u32(orv);
+    andv = wave_and_u32(andv);
+    uint32_t diff = orv ^ andv;
+    uint32_t T = andv & ~diff;
+    for (int it = 0; diff && it < 32; ++it) {
+        const int bit = 31 - __clz(diff);
+        diff &= ~(1u << bit);
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) cnt += wave_popc(k[r] >= cand);
+        if (cnt >= F) T = cand;
+    }
+    return T;
+}
+
 __device__ inline uint32_t wave_select_u32(uint32_t k, int F, int max_bits = 32) {
     const int n = wave_popc(k != 0u);
     if (n <= F) return 0u;

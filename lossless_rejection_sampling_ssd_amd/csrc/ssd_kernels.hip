@@ -8,8 +8,8 @@
 //              (4096 bf16 / 2048 fp32 elements); waves never wait for each other.  Per
 //              tile: the softmax partial (max, sum of 2^{z c - o}), the lowest-id argmax
 //              and, for draft rows of the cache, every element at or above the F-th
-//              largest lane maximum of the tile (a lower bound of the tile's F-th
-//              largest value) as a candidate key.
+//              largest lane maximum of its block of four tiles (a lower bound of the
+//              row's F-th largest value) as a candidate key.
 //  finalise    one wave per (sequence, position i): softmax statistics of both rows,
 //              cache ids S_i (top F_i draft ids, ties to the lower id), M_i, the Saguaro
 //              normaliser Z_i and the lossless test of draft token d_i, whose outcome
@@ -412,9 +412,9 @@ __device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, in
 }
 
 // Top F of one draft row from its tiles' candidate keys, by one wave.  The largest
-// tile threshold bounds the row's F-th largest value from below (that tile alone has
-// F elements at or above it), so only keys at or above it can be in the row's top F,
-// and every such key is in its tile's list.  Keys are distinct (they carry the id).
+// tile threshold bounds the row's F-th largest value from below (that tile's block of
+// four tiles alone has F elements at or above it), so only keys at or above it can be
+// in the row's top F, and every such key is in its tile's list.  Keys are distinct (they carry the id).
 // Returns lane j = the j-th largest key (0 past F).  cs and sc.nc come from
 // row_stats_wave.
 __device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F,
@@ -610,11 +610,12 @@ __device__ __forceinline__ bool test_draft(const DraftProbe& pr, int V, float mp
 }
 
 // ============================================================================ pass 1
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool GREEDY>
 __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     __shared__ uint64_t cand_stage[kWavesPerBlock][kStageCap + kWave];
     __shared__ u32x4 hot_vec[kWavesPerBlock][kHotCap];
     __shared__ int hot_id[kWavesPerBlock][kHotCap];
+    __shared__ uint32_t lane_key[kWavesPerBlock][kWave];
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -629,7 +630,12 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     const int model = (y % per) / nblk, blk = (y % per) % nblk;
     const int i = pr % a.K1, b = pr / a.K1;
     const int t = blk * kWavesPerBlock + wave;
-    if (t >= a.nt) return;
+    const int F = a.F[i];
+    // draft rows of the cache: the block's waves meet at a barrier, so a wave past the
+    // row's last tile stays (with no data) until then
+    const bool topf = model == a.topf_model && F > 0;  // uniform over the block
+    const bool tile_ok = t < a.nt;
+    if (!tile_ok && !topf) return;
     const int64_t r = (int64_t)b * a.K1 + i;
     const char* row = a.logits[model] + r * a.ld_bytes;
     const int64_t tile0 = (int64_t)t * kTile<DT>;
@@ -639,15 +645,24 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     // The tile stays in its raw 16-byte vectors (32 registers for bf16, not 64) and is
     // widened element by element in each use.
     u32x4 raw[kVecPerLane];
-    load_tile<DT, VEC, kVecPerLane>(row, tile0, V, lane, raw);
+    if (tile_ok) {
+        load_tile<DT, VEC, kVecPerLane>(row, tile0, V, lane, raw);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVecPerLane; ++j) raw[j] = neg_inf_vec<DT>();
+    }
 
     // One pass over the lane's vectors: the maximum of each vector and, unless greedy,
     // the sum of 2^{z c - o} with o the offset of the running maximum; when the maximum
     // grows the partial sum moves to the new offset exactly (ldexp by o_old - o_new).
+    // Maxima use the NaN-propagating maximum (v_maximum3_f32), which needs no operand
+    // canonicalisation; logits are never NaN, and a zero maximum may come out as +0 where
+    // fmax could give -0 (equal in every later comparison).  While the running maximum is
+    // -inf the offset is -3e38 instead of 0: every term so far is exactly 0, and the
+    // first finite maximum rescales that zero sum (ldexp by a saturated exponent).
     float vmax[kVecPerLane];  // maximum of each of the lane's vectors
     float m = -INFINITY;
     float s32 = 0.f, o = 0.f;
-    const bool want_sum = !a.greedy;
 #pragma unroll
     for (int j = 0; j < kVecPerLane; ++j) {
         float x[N];
@@ -655,11 +670,12 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         for (int e = 0; e < N; ++e) x[e] = vec_elem<DT>(raw[j], e);
         float vm = x[0];
 #pragma unroll
-        for (int e = 1; e < N; ++e) vm = fmaxf(vm, x[e]);
+        for (int e = 1; e < N; e += 2)
+            vm = e + 1 < N ? fmax3_nan(vm, x[e], x[e + 1]) : __builtin_elementwise_maximum(vm, x[e]);
         vmax[j] = vm;
-        m = fmaxf(m, vm);
-        if (want_sum) {
-            const float on = offset_of(m, c);
+        m = __builtin_elementwise_maximum(m, vm);
+        if (!GREEDY) {
+            const float on = rintf(__builtin_elementwise_maximum(m * c, -3e38f));
             s32 = ldexpf(s32, (int)(o - on));
             o = on;
             float tt[N];
@@ -670,6 +686,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
 #pragma unroll
                 for (int e = 0; e < w; ++e) tt[e] += tt[e + w];
             s32 += tt[0];
+            // each vector's sum completes here: left free, the compiler sinks every
+            // vector's terms below the loop and keeps all widened elements live at once
+            // (137 VGPRs instead of 67)
+            __asm__ volatile("" : "+v"(s32), "+v"(o));
         }
     }
     const float m_lane = m;
@@ -699,16 +719,25 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     opaque_regs(raw);
 
     // ---- candidate keys of this tile (draft rows of the cache): every element at or
-    // above the F-th largest lane maximum.  Only the (lane, vector) pairs whose vector
-    // maximum reaches the threshold can hold one: they are few (about F), so they are
-    // compacted through LDS, one per lane, and examined there; the keys are staged in
-    // LDS and copied out with one coalesced store per 64 keys.
-    const int F = a.F[i];
+    // above tau, the F-th largest of the block's 256 lane maxima (its four tiles are
+    // consecutive tiles of one row).  F lanes of the row hold an element at or above
+    // tau, so the row's F-th largest value is at least tau and every element of the
+    // row's top F is kept by its tile.  Only the (lane, vector) pairs whose vector
+    // maximum reaches tau can hold one: they are few, so they are compacted through
+    // LDS, one per lane, and examined there; the keys are staged in LDS and copied out
+    // with one coalesced store per 64 keys.
     uint32_t tau = 0u;
     int ncand = 0;
-    if (model == a.topf_model && F > 0) {
-        const bool lane_valid = tile0 + (int64_t)lane * N < V;
-        tau = wave_select_u32(lane_valid ? ord32(m_lane) : 0u, F);
+    if (topf) {
+        const bool lane_valid = tile_ok && tile0 + (int64_t)lane * N < V;
+        lane_key[wave][lane] = lane_valid ? ord32(m_lane) : 0u;
+        __syncthreads();
+        uint32_t k4[kWavesPerBlock];
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) k4[w] = lane_key[w][lane];
+        tau = wave_select_regs_u32<kWavesPerBlock>(k4, F);
+    }
+    if (topf && tile_ok) {
         const float tauf = tau ? unord32(tau) : -INFINITY;
         const int id0 = (int)tile0 + lane * N;
         const bool full = tile0 + kTile<DT> <= V;
@@ -782,11 +811,9 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             }
         }
         wave_sync_lds();
-        // the slots a finalisation may read speculatively (up to 2F+2) hold 0 past the
-        // last key, so that it needs no per-tile count to mask them
-        const int fill = min(2 * F + 2, cap);
+        // only the keys are stored: a reader masks the slots past the tile's count
         if (n <= min(cap, kStageCap)) {
-            for (int q = lane; q < max(n, fill); q += kWave) out[q] = q < n ? stage[q] : 0ull;
+            for (int q = lane; q < n; q += kWave) out[q] = stage[q];
             ncand = n;
         } else {
             // More tied candidates than slots: store this tile's exact top F, found by
@@ -814,10 +841,11 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 if (lane == 0) out[q] = best;
                 prev = best;
             }
-            for (int q = F + lane; q < fill; q += kWave) out[q] = 0ull;
             ncand = F;
         }
     }
+
+    if (!tile_ok) return;  // a wave past the row's last tile: nothing to record
 
     // ---- logit at the draft token of this row, if it falls in this tile
     if (a.draft && i < a.K1 - 1) {
@@ -963,17 +991,28 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (F > 0) {
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
-            // every tile's keys lie in its first Rg slots, and the slots past them hold 0
+            // every tile's keys lie in its first Rg slots; the slots past a tile's count
+            // hold stale values and are cleared
             const uint64_t floor_key = cs.tr ? (uint64_t)cs.tr << 32 : 1ull;
             const int U = uniform((nt * Rg + kWave - 1) / kWave);  // tile-major slots in use
-            if (U <= 4)
-                key = select_sorted<4>(reinterpret_cast<uint64_t(&)[4]>(k), U, F, sc, floor_key);
-            else if (U <= 8)
-                key = select_sorted<8>(reinterpret_cast<uint64_t(&)[8]>(k), U, F, sc, floor_key);
-            else if (U <= 12)
-                key = select_sorted<12>(reinterpret_cast<uint64_t(&)[12]>(k), U, F, sc, floor_key);
-            else
+            if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
+            wave_sync_lds();
+            if (U <= 4) {
+                auto& k4 = reinterpret_cast<uint64_t(&)[4]>(k);
+                mask_slots<4>(k4, nt, Rg, sc.nc, floor_key);
+                key = select_sorted<4>(k4, U, F, sc, floor_key);
+            } else if (U <= 8) {
+                auto& k8 = reinterpret_cast<uint64_t(&)[8]>(k);
+                mask_slots<8>(k8, nt, Rg, sc.nc, floor_key);
+                key = select_sorted<8>(k8, U, F, sc, floor_key);
+            } else if (U <= 12) {
+                auto& k12 = reinterpret_cast<uint64_t(&)[12]>(k);
+                mask_slots<12>(k12, nt, Rg, sc.nc, floor_key);
+                key = select_sorted<12>(k12, U, F, sc, floor_key);
+            } else {
+                mask_slots<kCandRegs>(k, nt, Rg, sc.nc, floor_key);
                 key = select_sorted<kCandRegs>(k, U, F, sc, floor_key);
+            }
         } else {
             if (fast) {
                 if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
@@ -1793,7 +1832,10 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
     const int64_t grid = ((int64_t)a.B * a.K1 + kXcds - 1) / kXcds * kXcds * a.nmodel * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
-        pass1_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
+        if (a.greedy)
+            pass1_kernel<decltype(DT)::value, decltype(VEC)::value, true><<<(unsigned)grid, kBlock, 0, st>>>(a);
+        else
+            pass1_kernel<decltype(DT)::value, decltype(VEC)::value, false><<<(unsigned)grid, kBlock, 0, st>>>(a);
     });
 }
 
