@@ -53,6 +53,10 @@ int tiles_per_row2(int dtype, int V) {
     return (V + t - 1) / t;
 }
 int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }  // <= 144 = cand_cap(64) <= kStageCap
+// Candidate slots per tile that the finalisation reads before it knows the tile's count
+// (pass 1 writes 0 past the keys up to there): with the block threshold a tile holds
+// at most about F + 6 keys.  A row with more in some tile takes the general path.
+__host__ __device__ __forceinline__ int spec_slots(int F, int cap) { return min(min(2 * F + 2, F + 8), cap); }
 
 // ============================================================================ shared pieces
 // Row normalisation from the exchanged statistics (row max m, row sum
@@ -811,9 +815,10 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             }
         }
         wave_sync_lds();
-        // only the keys are stored: a reader masks the slots past the tile's count
+        // the slots a finalisation reads before it knows the count hold 0 past the keys
+        const int fill = spec_slots(F, cap);
         if (n <= min(cap, kStageCap)) {
-            for (int q = lane; q < n; q += kWave) out[q] = stage[q];
+            for (int q = lane; q < max(n, fill); q += kWave) out[q] = q < n ? stage[q] : 0ull;
             ncand = n;
         } else {
             // More tied candidates than slots: store this tile's exact top F, found by
@@ -841,6 +846,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                 if (lane == 0) out[q] = best;
                 prev = best;
             }
+            for (int q = F + lane; q < fill; q += kWave) out[q] = 0ull;
             ncand = F;
         }
     }
@@ -957,7 +963,7 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (fast) {
         const WavePartial qq = lane_partial(Pq, nt), pp = lane_partial(Pp, nt);
         if (F > 0) {
-            Rg = min(min(2 * F + 2, f.cap), kWave * kCandRegs / nt);
+            Rg = min(spec_slots(F, f.cap), kWave * kCandRegs / nt);
             gather_slots<kCandRegs>(cr, f.cap, nt, Rg, k);
         }
         stats_from_lanes(qq, f.c, mq, sq, aq);
@@ -991,28 +997,17 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (F > 0) {
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
-            // every tile's keys lie in its first Rg slots; the slots past a tile's count
-            // hold stale values and are cleared
+            // every tile's keys lie in its first Rg slots, and the slots past them hold 0
             const uint64_t floor_key = cs.tr ? (uint64_t)cs.tr << 32 : 1ull;
             const int U = uniform((nt * Rg + kWave - 1) / kWave);  // tile-major slots in use
-            if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
-            wave_sync_lds();
-            if (U <= 4) {
-                auto& k4 = reinterpret_cast<uint64_t(&)[4]>(k);
-                mask_slots<4>(k4, nt, Rg, sc.nc, floor_key);
-                key = select_sorted<4>(k4, U, F, sc, floor_key);
-            } else if (U <= 8) {
-                auto& k8 = reinterpret_cast<uint64_t(&)[8]>(k);
-                mask_slots<8>(k8, nt, Rg, sc.nc, floor_key);
-                key = select_sorted<8>(k8, U, F, sc, floor_key);
-            } else if (U <= 12) {
-                auto& k12 = reinterpret_cast<uint64_t(&)[12]>(k);
-                mask_slots<12>(k12, nt, Rg, sc.nc, floor_key);
-                key = select_sorted<12>(k12, U, F, sc, floor_key);
-            } else {
-                mask_slots<kCandRegs>(k, nt, Rg, sc.nc, floor_key);
+            if (U <= 4)
+                key = select_sorted<4>(reinterpret_cast<uint64_t(&)[4]>(k), U, F, sc, floor_key);
+            else if (U <= 8)
+                key = select_sorted<8>(reinterpret_cast<uint64_t(&)[8]>(k), U, F, sc, floor_key);
+            else if (U <= 12)
+                key = select_sorted<12>(reinterpret_cast<uint64_t(&)[12]>(k), U, F, sc, floor_key);
+            else
                 key = select_sorted<kCandRegs>(k, U, F, sc, floor_key);
-            }
         } else {
             if (fast) {
                 if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
