@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--T", type=float, default=None, help="temperature (default: the workload's last)")
     ap.add_argument("--C", type=float, default=None)
     ap.add_argument("--target-sigma", type=float, default=None)
+    ap.add_argument("--r", type=float, default=None, help="fan-out ratio r (default: the workload's)")
+    ap.add_argument("--Bf", type=int, default=None, help="cache budget B_f (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=0,
                     help="time the vocabulary pass with HIP events on every N-th timed round "
@@ -122,6 +124,9 @@ def main():
     from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits
 
     w = WORKLOADS[args.workload]
+    if args.r is not None or args.Bf is not None:
+        import dataclasses
+        w = dataclasses.replace(w, r=w.r if args.r is None else args.r, Bf=w.Bf if args.Bf is None else args.Bf)
     T = w.temps[-1] if args.T is None else args.T
     C = args.C if args.C is not None else w.Cs[len(w.Cs) // 2]
     sig = args.target_sigma
@@ -306,6 +311,8 @@ def main():
     traffic = measured_traffic()
     label = "%s: B=%d K=%d V=%d %s logits, T=%g, B_f=%d, r=%g, C=%g" % (
         args.workload, B, K, V, w.dtype, T, w.Bf, w.r, C)
+    if sig is not None:
+        label += ", target sigma=%g" % sig
     rec = {
         "metric": "verify+cache rounds/sec and achieved HBM GB/s (% of peak), B=64 V=128256 K=8",
         "value": round(rounds_per_s, 2),
@@ -345,6 +352,10 @@ def main():
             "mean_accept_len": round(float(ks.mean()), 3),
             "mean_sum_min_p_qprime": round(float(np.mean(aprob)), 4),
             "hit_rate": round(float(hits.mean()), 4),
+            # P(some sequence of the batch misses in a round): measured over the replayed
+            # rounds, and 1 - prod_b h_b from each sequence's own hit rate over them
+            "p_any_miss_measured": round(float((hits == 0).any(axis=1).mean()), 4),
+            "p_any_miss_from_h": round(float(1.0 - np.prod(hits.mean(axis=0))), 6),
             "hit_rate_from_rank_hist": round(covered / max(total, 1), 4),
             "fanout_optimized": F_opt,
             "predicted_hit_rate_optimized": round(hits_opt / max(total, 1), 4),
