@@ -749,49 +749,47 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         uint64_t* stage = cand_stage[wave];
         const int cap = a.cap;
         int n = 0;
-        uint32_t hot = 0u;
+        // hot (lane, vector) pairs, counted per vector with a ballot (scalar masks)
+        int H = 0;
 #pragma unroll
-        for (int j = 0; j < kVecPerLane; ++j) hot |= (vmax[j] >= tauf ? 1u : 0u) << j;
-        const uint32_t h = (uint32_t)__popc(hot);
-        const uint32_t hincl = wave_prefix_u32(h);
-        const int H = (int)lane_u32(hincl, kWave - 1);
+        for (int j = 0; j < kVecPerLane; ++j) H += __popcll(__ballot(vmax[j] >= tauf));
+        H = uniform(H);
         if (H <= kHotCap) {
+            // compacted vector-major: the hot lanes of vector j follow those of vectors
+            // below j, in lane order
             u32x4* hv = hot_vec[wave];
             int* hid = hot_id[wave];
-            int q = (int)(hincl - h);
+            int q0 = 0;
 #pragma unroll
             for (int j = 0; j < kVecPerLane; ++j) {
-                if ((hot >> j) & 1u) {
-                    hv[q] = raw[j];
-                    hid[q] = id0 + j * kWave * N;
-                    ++q;
+                const bool me = vmax[j] >= tauf;
+                const uint64_t mj = __ballot(me);
+                if (mj) {  // uniform
+                    const int q = q0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mj >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mj, 0u));
+                    if (me) {
+                        hv[q] = raw[j];
+                        hid[q] = id0 + j * kWave * N;
+                    }
+                    q0 += __popcll(mj);
                 }
             }
             wave_sync_lds();
-            for (int q0 = 0; q0 < H; q0 += kWave) {
-                const int qq = q0 + lane;
-                const bool live = qq < H;
-                const u32x4 v = hv[live ? qq : 0];
-                const int e0 = hid[live ? qq : 0];
-                float x[N];
-                unpack_vec<DT>(v, x);
-                bool hit[N];
-                uint32_t cnt = 0u;
-#pragma unroll
-                for (int e = 0; e < N; ++e) {
-                    hit[e] = live && x[e] >= tauf && (full || e0 + e < V);
-                    cnt += hit[e] ? 1u : 0u;
-                }
-                const uint32_t cincl = wave_prefix_u32(cnt);
-                int pos = n + (int)(cincl - cnt);
-#pragma unroll
-                for (int e = 0; e < N; ++e) {
-                    if (hit[e]) {
-                        if (pos < kStageCap) stage[pos] = cand_key(x[e], (uint32_t)(e0 + e));
-                        ++pos;
-                    }
-                }
-                n += (int)lane_u32(cincl, kWave - 1);
+            // one element per lane: element e of hot vector q is lane (q N + e) mod 64
+            const uint32_t* hw = reinterpret_cast<const uint32_t*>(hv);
+            for (int p0 = 0; p0 < H * N; p0 += kWave) {
+                const int pp = p0 + lane;
+                const bool live = pp < H * N;
+                const int q = live ? pp / N : 0, e = pp % N;
+                const uint32_t w = hw[q * 4 + (DT == 1 ? e >> 1 : e)];
+                const float x = DT == 1 ? __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
+                const int id = hid[q] + e;
+                const bool hit = live && x >= tauf && (full || id < V);
+                const uint64_t mk = __ballot(hit);
+                const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+                if (hit && pos < kStageCap) stage[pos] = cand_key(x, (uint32_t)id);
+                n += __popcll(mk);
             }
         } else {
             // many hot vectors (a threshold at -inf, or heavy ties): element by element
