@@ -648,6 +648,9 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
 
     // The tile stays in its raw 16-byte vectors (32 registers for bf16, not 64) and is
     // widened element by element in each use.
+    // the draft token of this row is requested with the tile, not after it
+    const bool has_draft = a.draft && i < a.K1 - 1;
+    const int d_tok = has_draft ? a.draft[(int64_t)b * (a.K1 - 1) + i] : -1;
     u32x4 raw[kVecPerLane];
     if (tile_ok) {
         load_tile<DT, VEC, kVecPerLane>(row, tile0, V, lane, raw);
@@ -852,8 +855,8 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     if (!tile_ok) return;  // a wave past the row's last tile: nothing to record
 
     // ---- logit at the draft token of this row, if it falls in this tile
-    if (a.draft && i < a.K1 - 1) {
-        const int d = a.draft[(int64_t)b * (a.K1 - 1) + i];
+    if (has_draft) {
+        const int d = d_tok;
         const int64_t off = (int64_t)d - tile0;
         if (d >= 0 && d < V && off >= 0 && off < kTile<DT>) {  // uniform
             const int owner = (int)((off / N) % kWave), jd = (int)(off / (N * kWave)), ed = (int)(off % N);
