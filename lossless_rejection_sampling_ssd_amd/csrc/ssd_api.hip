@@ -28,7 +28,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Workspace regions (byte offsets).  Every region is written by one kernel of a call
 // and read by a later kernel of the same call; nothing persists between calls.
 //   part   [B][2][K+1][nt]        WavePartial, one per wave tile
-//   cand   [B][K+1][nt][cap]      top-F candidate keys of the draft rows' tiles
+//   cand   [B][K+1][nu][4 cap]    top-F candidate keys of the draft rows, per unit of four
+//                                 tiles (nu = ceil(nt / 4))
 //   seg    [max(B, B K)][nt2]     (weight sum, target-law sum) per pass-2 tile
 //   stats  [B (K+1)]              fp64 p_sum q_sum cache_mass Z, fp32 p_max q_max,
 //                                 int32 p_arg (for outputs the caller leaves NULL)
@@ -51,7 +52,8 @@ void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     L->part = off;
     off = align_up(off + (size_t)R * 2 * nt * sizeof(ssd::WavePartial));
     L->cand = off;
-    off = align_up(off + (size_t)R * nt * cap * sizeof(uint64_t));
+    // keys per unit of four tiles (one pass-1 block), 4 cap slots each
+    off = align_up(off + (size_t)R * ((nt + 3) / 4) * 4 * cap * sizeof(uint64_t));
     L->seg = off;
     off = align_up(off + (size_t)groups * nt2 * 16);
     L->stats = off;

@@ -57,6 +57,9 @@ int cand_cap(int Fmax) { return ((2 * Fmax + 16) + 7) / 8 * 8; }  // <= 144 = ca
 // (pass 1 writes 0 past the keys up to there): with the block threshold a tile holds
 // at most about F + 6 keys.  A row with more in some tile takes the general path.
 __host__ __device__ __forceinline__ int spec_slots(int F, int cap) { return min(min(2 * F + 2, F + 8), cap); }
+// Candidate keys are stored per unit: the four tiles of one pass-1 block (one row, one
+// threshold), contiguously, in a region of kWavesPerBlock * cap slots.
+__host__ __device__ __forceinline__ int units_per_row(int nt) { return (nt + kWavesPerBlock - 1) / kWavesPerBlock; }
 
 // ============================================================================ shared pieces
 // Row normalisation from the exchanged statistics (row max m, row sum
@@ -116,9 +119,9 @@ struct CandSummary {
 // Softmax statistics of one row from its nt tile partials, by one wave in a fixed
 // order (lane-sequential, then a butterfly); every lane returns the same values.
 // With with_cands, the same single read of the partials also fills the candidate
-// summary cs (per-tile counts to nc, which holds kMaxMergeTiles entries).
+// summary cs (per-unit counts to nc, which holds kMaxMergeTiles entries).
 __device__ __forceinline__ void row_stats_wave(const WavePartial* P, int nt, float c, float& m, double& s, int& arg,
-                                               bool with_cands, CandSummary& cs, uint8_t* nc) {
+                                               bool with_cands, CandSummary& cs, uint16_t* nc) {
     const int lane = lane_id();
     m = -INFINITY;
     s = 0.0;
@@ -131,7 +134,7 @@ __device__ __forceinline__ void row_stats_wave(const WavePartial* P, int nt, flo
         if (with_cands) {
             tr = max(tr, q.tau);
             max_nc = max(max_nc, q.ncand);
-            if (t < kMaxMergeTiles) nc[t] = (uint8_t)q.ncand;
+            if ((t & 3) == 0 && (t >> 2) < kMaxMergeTiles) nc[t >> 2] = (uint16_t)q.ncand;
         }
     }
     wave_stats(m, s, arg, c, m, s, arg);
@@ -155,7 +158,7 @@ struct TopfScratch {
     uint64_t rank[kWave];                 // the top F, placed by rank
     uint32_t bins[256 + kWave];           // value histogram of the select (+ one discard
                                           // bin per lane)
-    uint8_t nc[kMaxMergeTiles];           // candidates per tile
+    uint16_t nc[kMaxMergeTiles];          // candidates per unit (four tiles)
 };
 
 // The largest 32-bit value part T such that at least F of the nonzero keys among the
@@ -340,7 +343,7 @@ __device__ __forceinline__ void gather_slots(const uint64_t* cand, int cap, int 
 // Keeps the gathered slots that hold a candidate (s < the tile's count, from nc) at
 // or above floor_key; clears the rest.
 template <int KREG>
-__device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, const uint8_t* nc,
+__device__ __forceinline__ void mask_slots(uint64_t (&k)[KREG], int nt, int R, const uint16_t* nc,
                                            uint64_t floor_key) {
     const int lane = lane_id();
     int t = lane / R, sl = lane % R;
@@ -415,22 +418,24 @@ __device__ __forceinline__ uint64_t select_sorted(uint64_t (&k)[KREG], int U, in
     return rank_sort_lds(sc, n, F);
 }
 
-// Top F of one draft row from its tiles' candidate keys, by one wave.  The largest
-// tile threshold bounds the row's F-th largest value from below (that tile's block of
-// four tiles alone has F elements at or above it), so only keys at or above it can be
-// in the row's top F, and every such key is in its tile's list.  Keys are distinct (they carry the id).
-// Returns lane j = the j-th largest key (0 past F).  cs and sc.nc come from
-// row_stats_wave.
-__device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const uint64_t* cand, int nt, int cap, int F,
-                                                  const CandSummary& cs, TopfScratch& sc) {
+// Top F of one draft row from its units' candidate keys (unit u: tiles 4u..4u+3, its
+// count in the partial of tile 4u, stored at unit u of cand with stride capU), by one
+// wave.  The largest threshold bounds the row's F-th largest value from below (that
+// unit alone has F elements at or above it), so only keys at or above it can be in the
+// row's top F, and every such key is in its unit's list.  Keys are distinct (they carry
+// the id).  Returns lane j = the j-th largest key (0 past F).  cs and sc.nc (per unit)
+// come from row_stats_wave.
+__device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const uint64_t* cand, int nt, int capU,
+                                                  int F, const CandSummary& cs, TopfScratch& sc) {
     const int lane = lane_id();
     const uint64_t floor_key = (uint64_t)cs.tr << 32;
     const int R = cs.max_nc;
-    if (nt <= kMaxMergeTiles && (int64_t)nt * R <= (int64_t)kWave * kCandRegs) {
+    const int nu = units_per_row(nt);
+    if (nu <= kMaxMergeTiles && (int64_t)nu * R <= (int64_t)kWave * kCandRegs) {
         uint64_t k[kCandRegs];
-        gather_slots<kCandRegs>(cand, cap, nt, R, k);
-        mask_slots<kCandRegs>(k, nt, R, sc.nc, floor_key);
-        return select_sorted<kCandRegs>(k, (nt * R + kWave - 1) / kWave, F, sc);
+        gather_slots<kCandRegs>(cand, capU, nu, R, k);
+        mask_slots<kCandRegs>(k, nu, R, sc.nc, floor_key);
+        return select_sorted<kCandRegs>(k, (nu * R + kWave - 1) / kWave, F, sc);
     }
 
     // Rows with more candidates than register slots: exact selection by F rounds of a
@@ -439,8 +444,8 @@ __device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const ui
     uint64_t key = 0ull, prev = ~0ull;
     for (int r = 0; r < F; ++r) {
         uint64_t best = 0ull;
-        for (int c0 = 0; c0 < nt; c0 += kWave) {
-            const int nc = c0 + lane < nt ? P[c0 + lane].ncand : 0;
+        for (int c0 = 0; c0 < nu; c0 += kWave) {
+            const int nc = c0 + lane < nu ? P[(int64_t)(c0 + lane) * kWavesPerBlock].ncand : 0;
             int incl = nc;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -451,7 +456,7 @@ __device__ __forceinline__ uint64_t row_topf_wave(const WavePartial* P, const ui
             start[lane] = incl - nc;
             wave_sync_lds();
             for (int j = lane; j < tot; j += kWave) {
-                const uint64_t x = chunk_key(cand, cap, c0, start, j);
+                const uint64_t x = chunk_key(cand, capU, c0, start, j);
                 if (x >= floor_key && x < prev && x > best) best = x;
             }
             wave_sync_lds();
@@ -620,6 +625,7 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     __shared__ u32x4 hot_vec[kWavesPerBlock][kHotCap];
     __shared__ int hot_id[kWavesPerBlock][kHotCap];
     __shared__ uint32_t lane_key[kWavesPerBlock][kWave];
+    __shared__ int unit_cnt[kWavesPerBlock];
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -744,14 +750,18 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         for (int w = 0; w < kWavesPerBlock; ++w) k4[w] = lane_key[w][lane];
         tau = wave_select_regs_u32<kWavesPerBlock>(k4, F);
     }
-    if (topf && tile_ok) {
+    if (topf) {
         const float tauf = tau ? unord32(tau) : -INFINITY;
         const int id0 = (int)tile0 + lane * N;
         const bool full = tile0 + kTile<DT> <= V;
-        uint64_t* out = a.cand + ((r * a.nt) + t) * a.cap;
+        // the unit (this block's four tiles) stores its keys contiguously: this tile's at
+        // the sum of the counts of the tiles before it
+        const int capU = kWavesPerBlock * a.cap;
+        uint64_t* unit = a.cand + ((r * units_per_row(a.nt)) + blk) * (int64_t)capU;
         uint64_t* stage = cand_stage[wave];
         const int cap = a.cap;
         int n = 0;
+        if (tile_ok) {
         // hot (lane, vector) pairs, counted per vector with a ballot (scalar masks)
         int H = 0;
 #pragma unroll
@@ -816,14 +826,22 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
             }
         }
         wave_sync_lds();
-        // the slots a finalisation reads before it knows the count hold 0 past the keys
-        const int fill = spec_slots(F, cap);
-        if (n <= min(cap, kStageCap)) {
-            for (int q = lane; q < max(n, fill); q += kWave) out[q] = q < n ? stage[q] : 0ull;
-            ncand = n;
-        } else {
-            // More tied candidates than slots: store this tile's exact top F, found by
-            // F rounds of a wave maximum below the previous key (re-reading the tile).
+        }  // tile_ok
+        // a tile with more tied keys than its stage stores its exact top F instead
+        const bool exact = n > min(cap, kStageCap);
+        unit_cnt[wave] = exact ? F : n;
+        __syncthreads();
+        int off = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int cw = unit_cnt[w];
+            off += w < wave ? cw : 0;
+            total += cw;
+        }
+        if (tile_ok && !exact) {
+            for (int q = lane; q < n; q += kWave) unit[off + q] = stage[q];
+        } else if (tile_ok) {
+            // F rounds of a wave maximum below the previous key (re-reading the tile)
             uint64_t prev = ~0ull;
 #pragma unroll 1
             for (int q = 0; q < F; ++q) {
@@ -840,16 +858,18 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
                     }
                 }
 #pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const uint64_t o = __shfl_xor(best, off, kWave);
-                    best = o > best ? o : best;
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const uint64_t x = __shfl_xor(best, o, kWave);
+                    best = x > best ? x : best;
                 }
-                if (lane == 0) out[q] = best;
+                if (lane == 0) unit[off + q] = best;
                 prev = best;
             }
-            for (int q = F + lane; q < fill; q += kWave) out[q] = 0ull;
-            ncand = F;
         }
+        // the slots a finalisation reads before it knows the count hold 0 past the keys
+        if (wave == 0)
+            for (int q = total + lane; q < spec_slots(F, capU); q += kWave) unit[q] = 0ull;
+        ncand = wave == 0 ? total : 0;  // the unit's count, in its first tile's partial
     }
 
     if (!tile_ok) return;  // a wave past the row's last tile: nothing to record
@@ -946,7 +966,8 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     const int64_t r = (int64_t)b * K1 + i;
     const WavePartial* Pp = part + (int64_t)i * nt;
     const WavePartial* Pq = part + (int64_t)(K1 + i) * nt;
-    const uint64_t* cr = f.cand + r * nt * f.cap;
+    const int nu = units_per_row(nt), capU = kWavesPerBlock * f.cap;
+    const uint64_t* cr = f.cand + r * nu * (int64_t)capU;
     const int F = f.F[i];
     DraftProbe pr;
     pr.d = i < K ? f.draft[(int64_t)b * K + i] : 0;
@@ -964,8 +985,8 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (fast) {
         const WavePartial qq = lane_partial(Pq, nt), pp = lane_partial(Pp, nt);
         if (F > 0) {
-            Rg = min(spec_slots(F, f.cap), kWave * kCandRegs / nt);
-            gather_slots<kCandRegs>(cr, f.cap, nt, Rg, k);
+            Rg = min(spec_slots(F, capU), kWave * kCandRegs / nu);
+            gather_slots<kCandRegs>(cr, capU, nu, Rg, k);
         }
         stats_from_lanes(qq, f.c, mq, sq, aq);
         stats_from_lanes(pp, f.c, mp, sp, ap);
@@ -975,7 +996,7 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
         cs.tr = wave_max_u32(qq.tau);
         if (F > 0 && F < nt) cs.tr = max(cs.tr, wave_select_u32(lane < nt ? ord32(qq.m) : 0u, F, 10));
         cs.max_nc = (int)wave_max_u32((uint32_t)qq.ncand);
-        nc_lane = qq.ncand;
+        nc_lane = __shfl(qq.ncand, min(kWavesPerBlock * lane, kWave - 1), kWave);  // unit `lane`
     } else {
         CandSummary unused;
         row_stats_wave(Pq, nt, f.c, mq, sq, aq, true, cs, sc.nc);
@@ -998,9 +1019,9 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (F > 0) {
         uint64_t key;
         if (fast && cs.max_nc <= Rg) {
-            // every tile's keys lie in its first Rg slots, and the slots past them hold 0
+            // every unit's keys lie in its first Rg slots, and the slots past them hold 0
             const uint64_t floor_key = cs.tr ? (uint64_t)cs.tr << 32 : 1ull;
-            const int U = uniform((nt * Rg + kWave - 1) / kWave);  // tile-major slots in use
+            const int U = uniform((nu * Rg + kWave - 1) / kWave);  // unit-major slots in use
             if (U <= 4)
                 key = select_sorted<4>(reinterpret_cast<uint64_t(&)[4]>(k), U, F, sc, floor_key);
             else if (U <= 8)
@@ -1011,10 +1032,10 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
                 key = select_sorted<kCandRegs>(k, U, F, sc, floor_key);
         } else {
             if (fast) {
-                if (lane < nt) sc.nc[lane] = (uint8_t)nc_lane;
+                if (lane < nu) sc.nc[lane] = (uint16_t)nc_lane;
                 wave_sync_lds();
             }
-            key = row_topf_wave(Pq, cr, nt, f.cap, F, cs, sc);
+            key = row_topf_wave(Pq, cr, nt, capU, F, cs, sc);
         }
         M = finish_cache_row(key, F, mq, sq, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i], nullptr);
         my_id = lane < F && key ? (int)key_id(key) : -1;
@@ -1575,7 +1596,9 @@ __global__ __launch_bounds__(kBlock) void combine_topf_kernel(const Pass1Args a,
     const int F = a.F[i];
     double M = 0.0;
     if (F > 0) {
-        const uint64_t key = row_topf_wave(a.part + r * a.nt, a.cand + r * a.nt * a.cap, a.nt, a.cap, F, cs, sc[wave]);
+        const int capU = kWavesPerBlock * a.cap;
+        const uint64_t key = row_topf_wave(a.part + r * a.nt, a.cand + r * units_per_row(a.nt) * (int64_t)capU, a.nt,
+                                           capU, F, cs, sc[wave]);
         M = finish_cache_row(key, F, q_max[r], q_sum[r], a.c, a.greedy, cache_ids + (int64_t)b * Bf + a.O[i], nullptr);
     }
     if (lane == 0) cache_mass[r] = M;
