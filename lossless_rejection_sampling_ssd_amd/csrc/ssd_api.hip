@@ -35,8 +35,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 //                                 int32 p_arg (for outputs the caller leaves NULL)
 //   vflag  [B K]                  int32 outcome of each draft-token test
 //   probe  [B K 2]                fp32 logits at the draft tokens (target, draft)
+//   law    [B (K+1)]              LawParams of each row (fused round: written by the
+//                                 finalisation, read by pass 2 and the bonus)
 struct Layout {
-    size_t part, cand, seg, stats, vflag, probe, total;
+    size_t part, cand, seg, stats, vflag, probe, law, total;
     int nt, nt2, cap;
 };
 
@@ -62,6 +64,8 @@ void layout_for(const ssd_shape* s, int32_t Bf, Layout* L) {
     off = align_up(off + (size_t)s->B * s->K * 4);
     L->probe = off;
     off = align_up(off + (size_t)s->B * s->K * 8);
+    L->law = off;
+    off = align_up(off + (size_t)R * sizeof(ssd::LawParams));
     L->total = off;
     L->nt = nt;
     L->nt2 = nt2;
@@ -642,6 +646,7 @@ static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const voi
     f.vflag = at<int32_t>(ws, L.vflag);
     f.cache_values = out->cache_values;
     f.next_draft = out->next_draft;
+    f.law = at<ssd::LawParams>(ws, L.law);
 
     const bool vec = vec_ok(s, p_logits) && vec_ok(s, q_logits);
     hipError_t e;
@@ -694,6 +699,7 @@ static ssd_status round_impl(const ssd_shape* s, const void* p_logits, const voi
     b.hit = out->hit;
     b.slot = out->slot;
     b.fallback_tokens = out->fallback_tokens;
+    b.law = f.law;
     if (ev && ev->pass2_start && (e = hipEventRecord((hipEvent_t)ev->pass2_start, hs)) != hipSuccess)
         return fail_hip(e, "ssd_round event");
     e = ssd::launch_pass2(s->dtype, vec, b, s->B, hs);

@@ -21,6 +21,13 @@ struct WavePartial {
     int pad0, pad1;
 };
 
+// Law parameters of one row (b, i) for pass 2 and the bonus: p(x) = tp inv_p, residual
+// weights max(tp - tq rho_sel, 0), term offsets op (target) and oq (draft).
+struct LawParams {
+    double inv_p, rho, rhoC;
+    float op, oq;
+};
+
 struct Pass1Args {
     const char* logits[2];
     int nmodel;       // 1, or 2 for the fused round (0 = target p, 1 = draft q)
@@ -82,6 +89,7 @@ struct SeqFinal {
     int32_t* next_draft;          // [B, K] when cache_values is set
     int32_t* vflag;       // [B, K] workspace: bit 0 accepted, higher bits error bits
     const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
+    LawParams* law;             // nullable [B (K+1)]: receives each row's law parameters
 };
 
 struct Pass2Args {
@@ -118,6 +126,7 @@ struct Pass2Args {
     int32_t* slot;
     int32_t* fallback_tokens;
     const uint64_t* round_ptr;  // nullable: the round counter in device memory (replaces round)
+    const LawParams* law;       // nullable [B (K+1)]: precomputed law of each row (else from the statistics)
 };
 
 int tile_elems(int dtype);

@@ -909,6 +909,78 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     }
 }
 
+// The weights are kept in the units of the target row's terms tp = term(z_p, c, op)
+// (p(x) = tp * inv_p), so that no per-element scaling is needed: with tq = term(z_q,
+// c, oq) and q'(x) = tq * sc_q * (C if cached else 1),
+//   residual  max(p - q', 0) = inv_p * max(tp - tq * rho_sel, 0),  rho = sc_q / inv_p;
+//   target    p              = inv_p * tp;
+//   draft q'  (its own units)  tq * (C if cached else 1).
+// The inverse CDF is invariant to the common factor; only the reported residual mass
+// is scaled back by inv_p.
+struct WParams {
+    float c;
+    float op, oq;        // offsets of the target / draft rows
+    double inv_p;        // p(x) = tp * inv_p
+    double rho, rhoC;    // draft-to-target unit ratio, off / on the cached ids
+    double Cd;           // C as double (tq * C is exact in fp64)
+};
+
+// Row statistics of one (b, position), loaded together with no branch in between so
+// that they travel with the tile loads.  Without a target law (draft sampling) the
+// draft statistics stand in for it and are not used.
+struct LawIn {
+    float pm, qm;
+    double ps, qs, Z;
+};
+// a / b for a positive normal b, to within about an ulp: the hardware reciprocal refined
+// by two Newton steps, then one correction of the quotient.  Short latency, for the law
+// parameters (their rounding moves each weight by a relative 1e-16 at most).
+__device__ __forceinline__ double fdiv64(double a, double b) {
+    double r = __builtin_amdgcn_rcp(b);
+    double e = __builtin_fma(-b, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-b, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    const double q = a * r;
+    return __builtin_fma(__builtin_fma(-b, q, a), r, q);
+}
+
+// 1 / (row sum in units of 2^{z c - o}) for a row with maximum m and standard sum s.
+__device__ __forceinline__ double law_inv(float m, double s, float c, float o) { return fdiv64(offset_factor(m, c, o), s); }
+__device__ __forceinline__ double law_rho(double inv_q, double Z, double inv_p) { return fdiv64(fdiv64(inv_q, Z), inv_p); }
+
+__device__ __forceinline__ WParams make_wparams(float c, float C, bool with_p, const LawIn& L) {
+    WParams w;
+    w.c = c;
+    w.op = 0.f;
+    w.inv_p = 0.0;
+    w.rho = w.rhoC = 0.0;
+    w.Cd = (double)C;
+    w.oq = offset_of(L.qm, c);
+    if (with_p) {
+        w.op = offset_of(L.pm, c);
+        w.inv_p = law_inv(L.pm, L.ps, c, w.op);
+        w.rho = law_rho(law_inv(L.qm, L.qs, c, w.oq), L.Z, w.inv_p);
+        w.rhoC = w.rho * w.Cd;
+    }
+    return w;
+}
+
+// The law parameters of row r as the finalisation computes them once per (b, i) for the
+// fused round (the same expressions on the same values, so bit-identical to computing
+// them per wave), in the LawParams record pass 2 and the bonus load.
+__device__ __forceinline__ WParams wparams_from(const LawParams& P, float c, float C) {
+    WParams w;
+    w.c = c;
+    w.op = P.op;
+    w.oq = P.oq;
+    w.inv_p = P.inv_p;
+    w.rho = P.rho;
+    w.rhoC = P.rhoC;
+    w.Cd = (double)C;
+    return w;
+}
+
 // ============================================================================ finalise
 // Partial of tile `lane` of a row (the identity past nt), for rows of at most 64 tiles.
 __device__ __forceinline__ WavePartial lane_partial(const WavePartial* P, int nt) {
@@ -957,6 +1029,7 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
 template <int DT, bool DEVRNG>
 __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f) {
     __shared__ TopfScratch sc;
+    __shared__ LawParams law_lds;  // the target-row half of the law, kept across the select
     const int lane = threadIdx.x;
     const int K = f.K, K1 = K + 1, nt = f.nt;
     const int g = blockIdx.x;  // one wave per block
@@ -1013,6 +1086,10 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
         f.p_max[r] = mp;
         f.p_sum[r] = sp;
         if (f.p_arg) f.p_arg[r] = ap;
+        if (f.law && !f.greedy) {
+            law_lds.op = offset_of(mp, f.c);
+            law_lds.inv_p = law_inv(mp, sp, f.c, law_lds.op);
+        }
     }
     double M = 0.0;
     int my_id = -1;
@@ -1044,6 +1121,15 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     if (lane == 0) {
         f.cache_mass[r] = M;
         f.Z[r] = Z;
+        if (f.law && !f.greedy) {  // as make_wparams computes it from the same values
+            LawParams P;
+            P.op = law_lds.op;
+            P.inv_p = law_lds.inv_p;
+            P.oq = offset_of(mq, f.c);
+            P.rho = law_rho(law_inv(mq, sq, f.c, P.oq), Z, P.inv_p);
+            P.rhoC = P.rho * (double)f.C;
+            f.law[r] = P;
+        }
     }
     if (i < K) {
         const bool in_cache = __ballot(my_id >= 0 && my_id == pr.d) != 0ull;
@@ -1083,29 +1169,6 @@ __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f)
 // ============================================================================ pass 2
 enum { kWResid = 0, kWP = 1, kWQprime = 2 };
 
-// The weights are kept in the units of the target row's terms tp = term(z_p, c, op)
-// (p(x) = tp * inv_p), so that no per-element scaling is needed: with tq = term(z_q,
-// c, oq) and q'(x) = tq * sc_q * (C if cached else 1),
-//   residual  max(p - q', 0) = inv_p * max(tp - tq * rho_sel, 0),  rho = sc_q / inv_p;
-//   target    p              = inv_p * tp;
-//   draft q'  (its own units)  tq * (C if cached else 1).
-// The inverse CDF is invariant to the common factor; only the reported residual mass
-// is scaled back by inv_p.
-struct WParams {
-    float c;
-    float op, oq;        // offsets of the target / draft rows
-    double inv_p;        // p(x) = tp * inv_p
-    double rho, rhoC;    // draft-to-target unit ratio, off / on the cached ids
-    double Cd;           // C as double (tq * C is exact in fp64)
-};
-
-// Row statistics of one (b, position), loaded together with no branch in between so
-// that they travel with the tile loads.  Without a target law (draft sampling) the
-// draft statistics stand in for it and are not used.
-struct LawIn {
-    float pm, qm;
-    double ps, qs, Z;
-};
 __device__ __forceinline__ LawIn load_law(const Pass2Args& a, int64_t r) {
     const float* pmx = a.p_max ? a.p_max : a.q_max;
     const double* psx = a.p_sum ? a.p_sum : a.q_sum;
@@ -1116,25 +1179,6 @@ __device__ __forceinline__ LawIn load_law(const Pass2Args& a, int64_t r) {
     L.qs = a.q_sum[r];
     L.Z = a.Z[r];
     return L;
-}
-
-__device__ __forceinline__ WParams make_wparams(float c, float C, bool with_p, const LawIn& L) {
-    WParams w;
-    w.c = c;
-    w.op = 0.f;
-    w.inv_p = 0.0;
-    w.rho = w.rhoC = 0.0;
-    w.Cd = (double)C;
-    const RowNorm nq = row_norm(L.qm, L.qs, c);
-    w.oq = nq.o;
-    if (with_p) {
-        const RowNorm np = row_norm(L.pm, L.ps, c);
-        w.op = np.o;
-        w.inv_p = np.inv;
-        w.rho = nq.inv / L.Z / np.inv;
-        w.rhoC = w.rho * w.Cd;
-    }
-    return w;
 }
 
 // Weight of one element for the inverse-CDF scan (fp64, in the units above); *pw
@@ -1193,8 +1237,7 @@ __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const c
     if (MODE != kWP) load_tile<DT, VEC, kVecPass2>(qrow, t0, a.V, lane, rq);
     int my_id = -1;
     if (MODE != kWP && lane < Fk) my_id = ids[lane];
-    const LawIn L = load_law(a, r);
-    const WParams wp = make_wparams(a.c, a.C, MODE != kWQprime, L);
+    const WParams wp = a.law ? wparams_from(a.law[r], a.c, a.C) : make_wparams(a.c, a.C, MODE != kWQprime, load_law(a, r));
     if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
 #pragma unroll
     for (int j = 0; j < kVecPass2; ++j) {
@@ -1449,9 +1492,8 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
         if (mode != kWP) load_tile<DT, VEC, 1>(qrow, v0id, a.V, lane, tq);
         rp = tp[0];
         rq = tq[0];
-        const LawIn L = load_law(a, r);
         my_id = cached_id(a.cache_ids, b, a.Bf, pos, K, a.F, a.O);
-        wp = make_wparams(a.c, a.C, mode != kWQprime, L);
+        wp = a.law ? wparams_from(a.law[r], a.c, a.C) : make_wparams(a.c, a.C, mode != kWQprime, load_law(a, r));
         Zused = Z * wp.inv_p;  // the residual (or target) mass in probability units
         if (mode == kWResid)
             ls = rescan_vector_sums<DT, kWResid>(wp, rp, rq, t0, a.V, my_id, bits, wave, sh);
