@@ -39,6 +39,19 @@ namespace ssd {
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange = 8 };
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
+
+// Blocks are dealt to the XCDs round-robin (block x runs on XCD x mod 8), and each XCD
+// has its own L2.  Every kernel of a round puts the work of sequence b on XCD b mod 8,
+// so that what one kernel writes for a sequence (test outcomes, law parameters, cache
+// ids, tile sums) is still in that XCD's L2 when the next kernel reads it.  Slot s of a
+// per-(sequence, position) launch holds pair (b, i) with b mod 8 = s mod 8; the slots
+// of an XCD take its sequences in order, positions innermost.
+__host__ __device__ constexpr int xcd_slots(int B, int K1) { return (B + kXcds - 1) / kXcds * kXcds * K1; }
+__device__ __forceinline__ void xcd_pair(int s, int K1, int& b, int& i) {
+    const int y = s / kXcds;
+    i = y % K1;
+    b = (y / K1) * kXcds + s % kXcds;
+}
 constexpr int kSurvivorCap = 256;  // LDS slots per wave for the row's filtered candidates
 constexpr int kStageCap = 160;     // LDS slots per wave for one tile's candidate keys (>= any cap)
 constexpr int kHotCap = 128;       // LDS slots per wave for the vectors that hold candidates
@@ -629,16 +642,15 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
     constexpr int N = ElemTraits<DT>::kPerVec;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    // Block -> (row pair, model, tile group): the blocks of one (b, i) pair go to the
-    // same XCD (blocks are dealt to the 8 XCDs round-robin), where the finalisation
-    // wave of that pair later reads the partials; each XCD streams its rows in order.
+    // Block -> (row pair, model, tile group): the blocks of pair (b, i) go to XCD b mod 8,
+    // where the finalisation of that pair later runs; each XCD streams its rows in order.
     const int bid = blockIdx.x;
     const int per = a.nmodel * nblk;
     const int y = bid / kXcds;
-    const int pr = (y / per) * kXcds + bid % kXcds;
-    if (pr >= a.B * a.K1) return;
+    int b, i;
+    xcd_pair((y / per) * kXcds + bid % kXcds, a.K1, b, i);
+    if (b >= a.B) return;
     const int model = (y % per) / nblk, blk = (y % per) % nblk;
-    const int i = pr % a.K1, b = pr / a.K1;
     const int t = blk * kWavesPerBlock + wave;
     const int F = a.F[i];
     // draft rows of the cache: the block's waves meet at a barrier, so a wave past the
@@ -1032,8 +1044,9 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
     __shared__ LawParams law_lds;  // the target-row half of the law, kept across the select
     const int lane = threadIdx.x;
     const int K = f.K, K1 = K + 1, nt = f.nt;
-    const int g = blockIdx.x;  // one wave per block
-    const int b = g / K1, i = g % K1;
+    int b, i;  // one wave per block, pair (b, i) on XCD b mod 8
+    xcd_pair(blockIdx.x, K1, b, i);
+    if (b >= f.B) return;
     const WavePartial* part = f.part + (int64_t)b * 2 * K1 * nt;
     const bool fast = nt <= kWave;
     const int64_t r = (int64_t)b * K1 + i;
@@ -1148,7 +1161,8 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
 template <bool DEVRNG>
 __global__ __launch_bounds__(kBlock) void finish_greedy_kernel(const SeqFinal f) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int b = blockIdx.x * kWavesPerBlock + wave;
+    // sequence b on XCD b mod 8, four to a block
+    const int b = ((int)(blockIdx.x / kXcds) * kWavesPerBlock + wave) * kXcds + (int)(blockIdx.x % kXcds);
     if (b >= f.B) return;
     const int K = f.K;
     int errs;
@@ -1572,13 +1586,15 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a) {
+__global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a, int ngroups) {
     __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int g = blockIdx.x / nblk;
-    const int t = (blockIdx.x % nblk) * kWavesPerBlock + wave;
-    if (t >= a.nt) return;
+    // group g on XCD g mod 8 (the bonus block of group g is block g)
+    const int y = blockIdx.x / kXcds;
+    const int g = (y / nblk) * kXcds + blockIdx.x % kXcds;
+    const int t = (y % nblk) * kWavesPerBlock + wave;
+    if (g >= ngroups || t >= a.nt) return;
     int b, pos;
     bool valid;
     pass2_group(a, g, b, pos, valid);
@@ -1890,7 +1906,7 @@ static hipError_t by_type(int dtype, bool vec, Fn&& fn) {
 
 hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st) {
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t grid = ((int64_t)a.B * a.K1 + kXcds - 1) / kXcds * kXcds * a.nmodel * nblk;
+    const int64_t grid = (int64_t)xcd_slots(a.B, a.K1) * a.nmodel * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
         if (a.greedy)
@@ -1901,7 +1917,7 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
 }
 
 hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
-    const int grid = f.B * (f.K + 1);
+    const int grid = xcd_slots(f.B, f.K + 1);
     const bool dev = f.round_ptr != nullptr;  // round counter in device memory
     if (dtype == 1 && dev)
         finalize_pos_kernel<1, true><<<grid, kWave, 0, st>>>(f);
@@ -1915,7 +1931,7 @@ hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
 }
 
 hipError_t launch_finish_greedy(const SeqFinal& f, hipStream_t st) {
-    const int grid = (f.B + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int grid = (f.B + kXcds * kWavesPerBlock - 1) / (kXcds * kWavesPerBlock) * kXcds;
     if (f.round_ptr)
         finish_greedy_kernel<true><<<grid, kBlock, 0, st>>>(f);
     else
@@ -1925,10 +1941,10 @@ hipError_t launch_finish_greedy(const SeqFinal& f, hipStream_t st) {
 
 hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hipStream_t st) {
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t grid = (int64_t)ngroups * nblk;
+    const int64_t grid = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
-        pass2_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a);
+        pass2_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a, ngroups);
     });
 }
 
