@@ -121,7 +121,7 @@ def main():
     import torch
 
     import lossless_rejection_sampling_ssd_amd as ssd
-    from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits
+    from lossless_rejection_sampling_ssd_amd.workloads import WORKLOADS, make_histories, make_logits, plant_contexts
 
     w = WORKLOADS[args.workload]
     if args.r is not None or args.Bf is not None:
@@ -280,6 +280,21 @@ def main():
     r1.record()
     torch.cuda.synchronize()
     ngram_us = r0.elapsed_time(r1) * 1e3 / nr
+    # the same calls with every other served sequence's context planted mid-history,
+    # so that about half of them find a match (the histories above match none)
+    plant = np.nonzero(served)[0][::2]
+    h_pl = plant_contexts(h_np_tok, h_len, d_last.cpu().numpy(), outb["accept_len"].cpu().numpy(),
+                          outb["bonus"].cpu().numpy(), NG_MAX, plant)
+    ng_hist = torch.as_tensor(h_pl, device=dev)
+    ngram()
+    torch.cuda.synchronize()
+    ng_match_pl = float((ng_n.cpu().numpy()[served] > 0).mean()) if served.any() else 0.0
+    r0.record()
+    for i in range(nr):
+        ngram()
+    r1.record()
+    torch.cuda.synchronize()
+    ngram_pl_us = r0.elapsed_time(r1) * 1e3 / nr
     rows2 = np.where(ks < K, 2, 1).sum(axis=1).mean() if T > 0 else 0.0
     pass2_bytes = rows2 * V * esize
     round_bytes = pass1_bytes + pass2_bytes
@@ -366,6 +381,8 @@ def main():
             "ngram_history": "%d-token synthetic histories, n = %d..%d, misses of the last round (%d of %d)" % (
                 NG_L, NG_MIN, NG_MAX, int(served.sum()), B),
             "ngram_match_rate": round(ng_match, 4),
+            "ngram_fallback_planted_us": round(ngram_pl_us, 2),
+            "ngram_planted_match_rate": round(ng_match_pl, 4),
             "wall_s": round(wall, 3),
         },
         "roofline": {

@@ -163,3 +163,18 @@ def make_histories(B: int, L: int, V: int, seed: int, min_frac: float = 0.5, p_c
                 row[cur:cur + w] = perm[(rng.zipf(zipf_a, w) - 1) % V]
             cur += w
     return hist, lens
+
+
+def plant_contexts(hist, lens, draft, accept_len, bonus, n: int, rows):
+    """A copy of the histories in which each sequence b of ``rows`` holds, at position
+    lens[b] // 2, the last ``n`` tokens of its context (history, the k = accept_len[b]
+    accepted draft tokens, the bonus), so that the n-gram fallback finds a match of
+    length n there.  Host numpy arrays; the histories must be at least 2n + 2 long."""
+    import numpy as np
+    out = hist.copy()
+    for b in rows:
+        k = int(accept_len[b])
+        tail = np.concatenate([hist[b, :lens[b]][-n:], draft[b, :k], [bonus[b]]]).astype(np.int32)[-n:]
+        p = int(lens[b]) // 2
+        out[b, p:p + len(tail)] = tail
+    return out

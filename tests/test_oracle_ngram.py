@@ -143,3 +143,25 @@ def test_ngram_mutations_fail_a_pin(orc):
 
     for wrong in (earliest, shortest, self_match):
         assert any(wrong(c, 1, 4) != _rfind_match(c, 1, 4) for c in ctxs)
+
+
+def test_planted_contexts_match_at_the_plant(orc):
+    """The bench's planted histories (workloads.plant_contexts): every planted sequence
+    matches with n = n_max, at the plant or later, and the unplanted rows keep their
+    original histories."""
+    from lossless_rejection_sampling_ssd_amd.workloads import make_histories, plant_contexts
+    B, L, V, K, n = 12, 512, 1000, 4, 5
+    hist, lens = make_histories(B, L, V, seed=9)
+    rng = np.random.default_rng(3)
+    draft = rng.integers(0, V, (B, K)).astype(np.int32)
+    k = rng.integers(0, K + 1, B).astype(np.int32)
+    bonus = rng.integers(0, V, B).astype(np.int32)
+    rows = np.arange(0, B, 2)
+    h2 = plant_contexts(hist, lens, draft, k, bonus, n, rows)
+    _, mn, me, err = orc.ngram_fallback(K, V, h2, lens, draft, k, bonus, None, 2, n, 1, 1)
+    assert not err.any()
+    for b in range(B):
+        if b in rows:
+            assert mn[b] == n and me[b] >= lens[b] // 2 + n - 1, b
+        else:
+            assert (h2[b] == hist[b]).all()
