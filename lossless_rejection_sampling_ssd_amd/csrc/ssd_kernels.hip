@@ -39,6 +39,7 @@ namespace ssd {
 enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallback = 3 };
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange = 8 };
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
+constexpr int kFinalizeTwoWaveMaxPairs = 1024;  // (b, i) pairs up to the chip's SIMD count
 
 // Blocks are dealt to the XCDs round-robin (block x runs on XCD x mod 8), and each XCD
 // has its own L2.  Every kernel of a round puts the work of sequence b on XCD b mod 8,
@@ -1034,8 +1035,8 @@ __device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int 
 // One wave per (sequence b, position i): the statistics of target row i and draft
 // row i, the cache ids of draft row i, its cached mass M, the Saguaro normaliser
 // Z = 1 - (1 - C) M and the lossless test of draft token d_i.  For rows of at most 64
-// tiles the tile partials, the first 2 F_i + 2 candidate slots of every tile and the
-// logits at d_i are requested together.
+// tiles the tile partials, the first candidate slots of every unit and the logits at
+// d_i are requested together.
 // Three waves per SIMD (at most 168 VGPRs; unbounded it takes 170 and two), so that the
 // 2,560 waves of a B=512 K=4 round are resident at once.
 template <int DT, bool DEVRNG>
@@ -1149,6 +1150,147 @@ __global__ __launch_bounds__(kWave, 3) void finalize_pos_kernel(const SeqFinal f
         double ratio;
         int err;
         const bool acc = draft_decide(pr, dt, ap, Z, in_cache, f.C, f.greedy, &ratio, &err);
+        if (lane == 0) {
+            f.vflag[(int64_t)b * K + i] = (acc ? 1 : 0) | (err << 1);
+            if (f.accept_prob) f.accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
+        }
+    }
+}
+
+// The same finalisation by a block of two waves per (b, i), for rounds of at most one
+// (b, i) per SIMD, where the one-wave kernel leaves SIMDs idle and each wave's chain of
+// steps is the kernel's time.
+template <int DT, bool DEVRNG>
+__global__ __launch_bounds__(2 * kWave, 3) void finalize_pos2_kernel(const SeqFinal f) {
+    // Two waves per (b, i).  Wave 0 takes the draft row: its statistics, the cache ids,
+    // M, Z and whether d_i is cached.  Wave 1 takes the target row and the test of d_i:
+    // it forms the draft row's statistics again from the same partials by the same merges
+    // (the same values), so the test's exponentials run while wave 0 selects the cache;
+    // the two meet once, for Z and the membership of d_i.
+    __shared__ TopfScratch sc;  // wave 0
+    __shared__ double hand_Z;
+    __shared__ int hand_in;
+    const int wave = uniform((int)(threadIdx.x / kWave)), lane = threadIdx.x % kWave;
+    const int K = f.K, K1 = K + 1, nt = f.nt;
+    int b, i;  // pair (b, i) on XCD b mod 8
+    xcd_pair(blockIdx.x, K1, b, i);
+    if (b >= f.B) return;  // uniform over the block
+    const WavePartial* part = f.part + (int64_t)b * 2 * K1 * nt;
+    const bool fast = nt <= kWave;
+    const int64_t r = (int64_t)b * K1 + i;
+    const WavePartial* Pp = part + (int64_t)i * nt;
+    const WavePartial* Pq = part + (int64_t)(K1 + i) * nt;
+    float mp = 0.f, mq = 0.f;
+    double sp = 0.0, sq = 0.0;
+    int ap = INT_MAX, aq = INT_MAX;
+    DraftProbe pr;
+    DraftTerms dt{0.0, 0.0, 0, false};
+    if (wave == 0) {
+        const int nu = units_per_row(nt), capU = kWavesPerBlock * f.cap;
+        const uint64_t* cr = f.cand + r * nu * (int64_t)capU;
+        const int F = f.F[i];
+        const int d = i < K ? f.draft[(int64_t)b * K + i] : -1;
+        CandSummary cs;
+        uint64_t k[kCandRegs];
+        int Rg = 0;
+        int nc_lane = 0;
+        if (fast) {
+            const WavePartial qq = lane_partial(Pq, nt);
+            if (F > 0) {
+                Rg = min(spec_slots(F, capU), kWave * kCandRegs / nu);
+                gather_slots<kCandRegs>(cr, capU, nu, Rg, k);
+            }
+            stats_from_lanes(qq, f.c, mq, sq, aq);
+            // Floor of the row's F-th largest value: the largest tile threshold, or a lower
+            // bound of the F-th largest tile maximum (F tiles hold an element at or above
+            // it; its 10 leading differing bits suffice) if higher.
+            cs.tr = wave_max_u32(qq.tau);
+            if (F > 0 && F < nt) cs.tr = max(cs.tr, wave_select_u32(lane < nt ? ord32(qq.m) : 0u, F, 10));
+            cs.max_nc = (int)wave_max_u32((uint32_t)qq.ncand);
+            nc_lane = __shfl(qq.ncand, min(kWavesPerBlock * lane, kWave - 1), kWave);  // unit `lane`
+        } else {
+            row_stats_wave(Pq, nt, f.c, mq, sq, aq, true, cs, sc.nc);
+        }
+        sq = f.greedy ? 1.0 : std_sum(mq, sq, f.c);
+        if (lane == 0) {
+            f.q_max[r] = mq;
+            f.q_sum[r] = sq;
+            if (f.q_arg) f.q_arg[r] = aq;
+        }
+        double M = 0.0;
+        int my_id = -1;
+        if (F > 0) {
+            uint64_t key;
+            if (fast && cs.max_nc <= Rg) {
+                // every unit's keys lie in its first Rg slots, and the slots past them hold 0
+                const uint64_t floor_key = cs.tr ? (uint64_t)cs.tr << 32 : 1ull;
+                const int U = uniform((nu * Rg + kWave - 1) / kWave);  // unit-major slots in use
+                if (U <= 4)
+                    key = select_sorted<4>(reinterpret_cast<uint64_t(&)[4]>(k), U, F, sc, floor_key);
+                else if (U <= 8)
+                    key = select_sorted<8>(reinterpret_cast<uint64_t(&)[8]>(k), U, F, sc, floor_key);
+                else if (U <= 12)
+                    key = select_sorted<12>(reinterpret_cast<uint64_t(&)[12]>(k), U, F, sc, floor_key);
+                else
+                    key = select_sorted<kCandRegs>(k, U, F, sc, floor_key);
+            } else {
+                if (fast) {
+                    if (lane < nu) sc.nc[lane] = (uint16_t)nc_lane;
+                    wave_sync_lds();
+                }
+                key = row_topf_wave(Pq, cr, nt, capU, F, cs, sc);
+            }
+            M = finish_cache_row(key, F, mq, sq, f.c, f.greedy, f.cache_ids + (int64_t)b * f.Bf + f.O[i], nullptr);
+            my_id = lane < F && key ? (int)key_id(key) : -1;
+        }
+        const double Z = 1.0 - (1.0 - (double)f.C) * M;
+        const bool in_cache = __ballot(my_id >= 0 && my_id == d) != 0ull;
+        if (lane == 0) {
+            f.cache_mass[r] = M;
+            f.Z[r] = Z;
+            hand_Z = Z;
+            hand_in = in_cache ? 1 : 0;
+        }
+    } else {
+        pr.d = i < K ? f.draft[(int64_t)b * K + i] : 0;
+        pr.zp = i < K ? f.probe[((int64_t)b * K + i) * 2 + 0] : 0.f;  // valid when d_i is in range
+        pr.zq = i < K ? f.probe[((int64_t)b * K + i) * 2 + 1] : 0.f;
+        const uint64_t round = DEVRNG ? *f.round_ptr : f.round;
+        pr.u = (i < K && !f.greedy) ? philox_uniform(f.seed, round, kPurposeAccept, (uint64_t)b, (uint64_t)i) : 0.f;
+        if (fast) {
+            const WavePartial qq = lane_partial(Pq, nt), pp = lane_partial(Pp, nt);
+            stats_from_lanes(qq, f.c, mq, sq, aq);
+            stats_from_lanes(pp, f.c, mp, sp, ap);
+        } else {
+            CandSummary unused;
+            row_stats_wave(Pq, nt, f.c, mq, sq, aq, false, unused, nullptr);
+            row_stats_wave(Pp, nt, f.c, mp, sp, ap, false, unused, nullptr);
+        }
+        sq = f.greedy ? 1.0 : std_sum(mq, sq, f.c);
+        sp = f.greedy ? 1.0 : std_sum(mp, sp, f.c);
+        if (i < K) dt = draft_terms(pr, f.V, mp, sp, mq, sq, f.c, f.greedy);
+        if (lane == 0) {
+            f.p_max[r] = mp;
+            f.p_sum[r] = sp;
+            if (f.p_arg) f.p_arg[r] = ap;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) return;
+    const double Z = hand_Z;
+    if (lane == 0 && f.law && !f.greedy) {  // as make_wparams computes it from the same values
+        LawParams P;
+        P.op = offset_of(mp, f.c);
+        P.inv_p = law_inv(mp, sp, f.c, P.op);
+        P.oq = offset_of(mq, f.c);
+        P.rho = law_rho(law_inv(mq, sq, f.c, P.oq), Z, P.inv_p);
+        P.rhoC = P.rho * (double)f.C;
+        f.law[r] = P;
+    }
+    if (i < K) {
+        double ratio;
+        int err;
+        const bool acc = draft_decide(pr, dt, ap, Z, hand_in != 0, f.C, f.greedy, &ratio, &err);
         if (lane == 0) {
             f.vflag[(int64_t)b * K + i] = (acc ? 1 : 0) | (err << 1);
             if (f.accept_prob) f.accept_prob[(int64_t)b * K + i] = (float)(ratio < 1.0 ? ratio : 1.0);
@@ -1919,14 +2061,25 @@ hipError_t launch_pass1(int dtype, bool vec, const Pass1Args& a, hipStream_t st)
 hipError_t launch_finalize_pos(int dtype, const SeqFinal& f, hipStream_t st) {
     const int grid = xcd_slots(f.B, f.K + 1);
     const bool dev = f.round_ptr != nullptr;  // round counter in device memory
-    if (dtype == 1 && dev)
-        finalize_pos_kernel<1, true><<<grid, kWave, 0, st>>>(f);
-    else if (dtype == 1)
-        finalize_pos_kernel<1, false><<<grid, kWave, 0, st>>>(f);
-    else if (dev)
-        finalize_pos_kernel<0, true><<<grid, kWave, 0, st>>>(f);
-    else
-        finalize_pos_kernel<0, false><<<grid, kWave, 0, st>>>(f);
+    if (f.B * (f.K + 1) <= kFinalizeTwoWaveMaxPairs) {
+        if (dtype == 1 && dev)
+            finalize_pos2_kernel<1, true><<<grid, 2 * kWave, 0, st>>>(f);
+        else if (dtype == 1)
+            finalize_pos2_kernel<1, false><<<grid, 2 * kWave, 0, st>>>(f);
+        else if (dev)
+            finalize_pos2_kernel<0, true><<<grid, 2 * kWave, 0, st>>>(f);
+        else
+            finalize_pos2_kernel<0, false><<<grid, 2 * kWave, 0, st>>>(f);
+    } else {
+        if (dtype == 1 && dev)
+            finalize_pos_kernel<1, true><<<grid, kWave, 0, st>>>(f);
+        else if (dtype == 1)
+            finalize_pos_kernel<1, false><<<grid, kWave, 0, st>>>(f);
+        else if (dev)
+            finalize_pos_kernel<0, true><<<grid, kWave, 0, st>>>(f);
+        else
+            finalize_pos_kernel<0, false><<<grid, kWave, 0, st>>>(f);
+    }
     return hipGetLastError();
 }
 

@@ -123,6 +123,9 @@ EDGE_CASES = [
     # the finalisation's general path and the bonus's multi-chunk scans
     ("V=300k bf16", "bf16", 3, 2, 300001, 1.0, [12, 6, 3], 0.5, 2.0, 0.5, 0.0),
     ("V=200k f32", "f32", 2, 3, 200003, 0.8, [9, 5, 3, 2], 0.6, 2.0, 0.5, 0.0),
+    # more than 1024 (sequence, position) pairs with more than 64 tiles per row: the
+    # one-wave finalisation (large rounds) on its general path
+    ("1025 pairs V=140k f32", "f32", 205, 4, 140001, 1.0, [8, 4, 2, 1, 1], 0.5, 2.0, 0.5, 0.0),
 ]
 
 
