@@ -40,6 +40,10 @@ enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallbac
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange = 8 };
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
 constexpr int kFinalizeTwoWaveMaxPairs = 1024;  // (b, i) pairs up to the chip's SIMD count
+// Pass-2 grids of more than 8 tiles per SIMD are bound by their VALU work and take the
+// lean weighing; smaller ones (all waves resident at once) by load latency, where its
+// per-vector register pins cost more than its fewer instructions save.
+constexpr int64_t kPass2LeanMinTiles = 8192;
 
 // Blocks are dealt to the XCDs round-robin (block x runs on XCD x mod 8), and each XCD
 // has its own L2.  Every kernel of a round puts the work of sequence b on XCD b mod 8,
@@ -1364,8 +1368,11 @@ __device__ inline void tile_bitmap(uint32_t* bits, int64_t t0, int my_id) {
 }
 
 // Weights of one lane's vector j of a tile from the raw vectors of the target and
-// draft rows.  The tile loads hold -inf past V, so those elements weigh 0.
-template <int DT, int MODE>
+// draft rows.  The tile loads hold -inf past V, so those elements weigh 0.  LEAN weighs
+// every element as uncached and weighs again, in a branch, the cached ones (F of V ids,
+// so rarely any in a vector): the same values with fewer instructions per element, for
+// grids whose time is their VALU work.
+template <int DT, int MODE, bool LEAN = false>
 __device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 rq, int64_t e0, int V,
                                             const uint32_t* bits, int64_t t0, double* w, double* p) {
     constexpr int N = ElemTraits<DT>::kPerVec;
@@ -1374,6 +1381,21 @@ __device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 r
     if (MODE != kWP) unpack_vec<DT>(rq, zq);
     uint32_t cbits = 0u;
     if (MODE != kWP) cbits = bits[(e0 - t0) >> 5] >> ((e0 - t0) & 31);
+    if (LEAN) {
+        if (MODE != kWP) cbits &= (1u << N) - 1u;
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+            w[e] = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f, false, &p[e]);
+        if (MODE != kWP && cbits != 0u) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                double pw;
+                if ((cbits >> e) & 1u)
+                    w[e] = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, zq[e], true, &pw);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < N; ++e) {
         w[e] = elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f, (cbits >> e) & 1u,
@@ -1383,7 +1405,7 @@ __device__ __forceinline__ void vec_weights(const WParams& wp, u32x4 rp, u32x4 r
 
 // Sums over one lane's part of a wave tile: sw of the weights, sp of p(x).  The tile
 // and the row statistics are requested before any of them is used.
-template <int DT, bool VEC, int MODE>
+template <int DT, bool VEC, int MODE, bool LEAN>
 __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const char* prow, const char* qrow, int64_t t0,
                                           const int32_t* ids, int Fk, uint32_t* bits, double& sw, double& sp) {
     constexpr int N = ElemTraits<DT>::kPerVec;
@@ -1399,7 +1421,7 @@ __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const c
     for (int j = 0; j < kVecPass2; ++j) {
         const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
         double w[N], p[N];
-        vec_weights<DT, MODE>(wp, rp[j], rq[j], e0, a.V, bits, t0, w, p);
+        vec_weights<DT, MODE, LEAN>(wp, rp[j], rq[j], e0, a.V, bits, t0, w, p);
         double vw = 0.0, vp = 0.0;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
@@ -1408,6 +1430,9 @@ __device__ __forceinline__ void tile_sums(const Pass2Args& a, int64_t r, const c
         }
         sw += vw;
         sp += vp;
+        // LEAN: each vector's sums complete here (left free, the compiler keeps every
+        // vector's weights live at once, about twice the registers)
+        if (LEAN) __asm__ volatile("" : "+v"(sw), "+v"(sp));
     }
 }
 
@@ -1727,7 +1752,7 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
 }
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool LEAN>
 __global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a, int ngroups) {
     __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -1750,11 +1775,11 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a, int ng
         const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
         const int Fk = a.F[pos];
         if (mode == kWResid)
-            tile_sums<DT, VEC, kWResid>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+            tile_sums<DT, VEC, kWResid, LEAN>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
         else if (mode == kWP)
-            tile_sums<DT, VEC, kWP>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+            tile_sums<DT, VEC, kWP, LEAN>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
         else
-            tile_sums<DT, VEC, kWQprime>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
+            tile_sums<DT, VEC, kWQprime, LEAN>(a, r, prow, qrow, t0, ids, Fk, bits[wave], sw, sp);
     }
     sw = wave_sum_f64(sw);
     sp = wave_sum_f64(sp);
@@ -2096,8 +2121,12 @@ hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hi
     const int nblk = (a.nt + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t grid = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
+    const bool lean = (int64_t)ngroups * a.nt > kPass2LeanMinTiles;
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
-        pass2_kernel<decltype(DT)::value, decltype(VEC)::value><<<(unsigned)grid, kBlock, 0, st>>>(a, ngroups);
+        if (lean)
+            pass2_kernel<decltype(DT)::value, decltype(VEC)::value, true><<<(unsigned)grid, kBlock, 0, st>>>(a, ngroups);
+        else
+            pass2_kernel<decltype(DT)::value, decltype(VEC)::value, false><<<(unsigned)grid, kBlock, 0, st>>>(a, ngroups);
     });
 }
 

@@ -114,13 +114,8 @@ def test_build_cache(dtype, V, F, kind, T):
 
 
 # ----------------------------------------------------------------------------- Saguaro + draft
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("T,C", [(1.0, 0.5), (0.7, 0.2), (1.0, 1.0), (0.0, 0.5)])
-def test_saguaro_and_draft(dtype, T, C):
-    V, B, K = 6007, 8, 3
-    _case("saguaro dtype=%s T=%g C=%g" % (dtype, T, C))
+def _saguaro_draft_case(dtype, T, C, V, B, K, F):
     zq, _ = _rand(B, K, V, dtype, 21)
-    F = [6, 3, 2, 1]
     z = zq.cuda()
     m, s, a = _gpu_stats(z, T)
     ids = torch.zeros((B, sum(F)), dtype=torch.int32, device="cuda")
@@ -139,6 +134,23 @@ def test_saguaro_and_draft(dtype, T, C):
     od, flags = oracle.draft_sample(zq_np, T, np.array(F, np.int32), oids, oZ, C, 77, 5)
     ok = flags == 0
     assert np.array_equal(d.cpu().numpy()[ok], od[ok])
+    return int((~ok).sum())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,C", [(1.0, 0.5), (0.7, 0.2), (1.0, 1.0), (0.0, 0.5)])
+def test_saguaro_and_draft(dtype, T, C):
+    _case("saguaro dtype=%s T=%g C=%g" % (dtype, T, C))
+    _saguaro_draft_case(dtype, T, C, 6007, 8, 3, [6, 3, 2, 1])
+
+
+def test_draft_sampling_large_grid():
+    """Draft sampling over 64 sequences x 8 positions of 20 pass-2 tiles each (10,240
+    tiles, above the size from which pass 2 weighs every element as uncached first and
+    the cached ids again), against the oracle."""
+    _case("draft sampling, large grid")
+    flagged = _saguaro_draft_case("bf16", 1.0, 0.5, 40000, 64, 8, [8, 4, 3, 2, 2, 1, 1, 1, 1])
+    assert flagged == 0  # the oracle flags none of these 512 draws, so every one is compared
 
 
 # ----------------------------------------------------------------------------- chain of the six calls
