@@ -1027,13 +1027,16 @@ __device__ __forceinline__ void stats_from_lanes(const WavePartial& q, float c, 
 
 // Accepted length of sequence b from the per-position test outcomes (the first
 // rejected position, K if none) and the OR of their error bits; every lane returns
-// both.  Outcomes: bit 0 accepted, the bits above it the error bits.
-__device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int K, int* errs) {
-    const int lane = lane_id();
-    const int v = lane < K ? vflag[(int64_t)b * K + lane] : 1;
+// both.  Outcomes: bit 0 accepted, the bits above it the error bits.  v: lane j's
+// outcome of position j (1 past K).
+__device__ __forceinline__ int accepted_length_of(int v, int* errs) {
     const uint64_t rm = __ballot((v & 1) == 0);
     *errs = (int)wave_or_u32((uint32_t)(v >> 1));
-    return rm ? (__ffsll((long long)rm) - 1) : K;
+    return rm ? (__ffsll((long long)rm) - 1) : kWave;
+}
+__device__ __forceinline__ int accepted_length(const int32_t* vflag, int b, int K, int* errs) {
+    const int v = lane_id() < K ? vflag[(int64_t)b * K + lane_id()] : 1;
+    return min(accepted_length_of(v, errs), K);
 }
 
 // One wave per (sequence b, position i): the statistics of target row i and draft
@@ -1586,7 +1589,7 @@ __device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_
 // together.
 template <int DT, bool VEC, bool DEVRNG>
 __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
-                                            double2 v0, uint32_t* bits, BonusShare& sh, int wave) {
+                                            double2 v0, uint32_t* bits, BonusShare& sh, int wave, float upre) {
     const int lane = lane_id();
     const int K = a.K;
     const uint64_t round = DEVRNG ? *a.round_ptr : a.round;
@@ -1602,9 +1605,14 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
     u32x4 rp = neg_inf_vec<DT>(), rq = neg_inf_vec<DT>();
     if (valid) {
         const int64_t r = (int64_t)b * (K + 1) + pos;
-        const uint32_t purpose = a.mode == 0 ? kPurposeBonus : kPurposeDraft;
-        const double u = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos, 0);
-        u2 = (double)philox_uniform(a.seed, round, purpose, (uint64_t)b, (uint64_t)pos, 1);
+        double u;
+        if (a.mode == 0) {  // computed for every position before the accepted length was known
+            u = (double)__shfl(upre, pos, kWave);
+            u2 = (double)__shfl(upre, K + 1 + pos, kWave);
+        } else {
+            u = (double)philox_uniform(a.seed, round, kPurposeDraft, (uint64_t)b, (uint64_t)pos, 0);
+            u2 = (double)philox_uniform(a.seed, round, kPurposeDraft, (uint64_t)b, (uint64_t)pos, 1);
+        }
         // one chunk of at most 64 tiles (the usual case): the scan that gives the total
         // also locates the crossing
         const double incl_w = nt <= kWave ? wave_scan_incl(v0.x) : 0.0;
@@ -1745,10 +1753,30 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     const int lane = threadIdx.x % kWave;
     // the group's tile sums do not depend on the accepted length: request them first
     const double2 v0 = lane < a.nt ? a.seg[(int64_t)g * a.nt + lane] : make_double2(0.0, 0.0);
+    // the sequence's test outcomes (or its given accepted length), requested before the
+    // uniforms below so that they load while those are computed
+    int vf_or_len = 0;
+    if (a.mode == 0) vf_or_len = a.vflag ? (lane < a.K ? a.vflag[(int64_t)g * a.K + lane] : 1) : a.accept_len[g];
+    // the draw's two uniforms of each position k of sequence g, which lane j computes for
+    // k = j mod (K+1), counter word j / (K+1), before the accepted length is known
+    float upre = 0.f;
+    if (a.mode == 0 && lane < 2 * (a.K + 1)) {
+        const uint64_t round = DEVRNG ? *a.round_ptr : a.round;
+        upre = philox_uniform(a.seed, round, kPurposeBonus, (uint64_t)g, (uint64_t)(lane % (a.K + 1)),
+                              (uint64_t)(lane / (a.K + 1)));
+    }
     int b, pos, verrs = 0;
     bool valid;
-    pass2_group(a, g, b, pos, valid, &verrs);
-    bonus_block<DT, VEC, DEVRNG>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave);
+    if (a.mode == 0) {
+        b = g;
+        pos = vf_or_len;
+        if (a.vflag) pos = min(accepted_length_of(vf_or_len, &verrs), a.K);
+        valid = pos >= 0 && pos <= a.K;
+        if (!valid) pos = 0;
+    } else {
+        pass2_group(a, g, b, pos, valid, &verrs);
+    }
+    bonus_block<DT, VEC, DEVRNG>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave, upre);
 }
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
