@@ -459,9 +459,11 @@ __device__ inline uint64_t wave_select_regs(const uint64_t (&k)[KREG], int F) {
 // has at least F keys at or above it.
 // The F-th largest of the nonzero keys the wave holds in R registers per lane (0 when at
 // most F are nonzero), by the same most-significant-bit-first search over the bits
-// where the keys differ.
+// where the keys differ.  Only the differing bits in bit_mask are resolved; the others
+// are left at the bits every key shares, which gives a lower bound of the F-th largest
+// key with at least F keys at or above it.
 template <int R>
-__device__ inline uint32_t wave_select_regs_u32(const uint32_t (&k)[R], int F) {
+__device__ inline uint32_t wave_select_regs_u32(const uint32_t (&k)[R], int F, uint32_t bit_mask = ~0u) {
     int n = 0;
     uint32_t orv = 0u, andv = ~0u;
 #pragma unroll
@@ -475,6 +477,7 @@ __device__ inline uint32_t wave_select_regs_u32(const uint32_t (&k)[R], int F) {
     andv = wave_and_u32(andv);
     uint32_t diff = orv ^ andv;
     uint32_t T = andv & ~diff;
+    diff &= bit_mask;
     for (int it = 0; diff && it < 32; ++it) {
         const int bit = 31 - __clz(diff);
         diff &= ~(1u << bit);

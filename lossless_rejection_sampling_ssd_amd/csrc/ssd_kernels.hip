@@ -765,7 +765,13 @@ __global__ __launch_bounds__(kBlock) void pass1_kernel(const Pass1Args a) {
         uint32_t k4[kWavesPerBlock];
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w) k4[w] = lane_key[w][lane];
-        tau = wave_select_regs_u32<kWavesPerBlock>(k4, F);
+        // The 16 high bits of the order keys suffice (all of a bf16 value's): any tau
+        // at or below the F-th largest lane maximum keeps the row's top F, one lower by
+        // less than a bf16 step only admits a few more fp32 keys, and each further bit
+        // costs a round of four ballots.  A bound below the key of -inf (a negative NaN
+        // pattern as a float) means every element: it becomes the key of -inf.
+        tau = wave_select_regs_u32<kWavesPerBlock>(k4, F, 0xFFFF0000u);
+        if (tau != 0u && tau < ord32(-INFINITY)) tau = ord32(-INFINITY);
     }
     if (topf) {
         const float tauf = tau ? unord32(tau) : -INFINITY;
