@@ -2057,7 +2057,7 @@ __global__ __launch_bounds__(kRankWaves * kWave) void rank_finish_kernel(const R
 // Read-only stream over a buffer in pass 1's access shape: one wave per 8 KiB (each
 // lane eight non-temporal 16-byte loads, vector j of lane l at (j*64 + l)*16 bytes),
 // nothing computed but an XOR that keeps the loads alive.  Its rate on the same
-// buffers is the reference the vocabulary pass is judged against.
+// buffers is the reference the vocabulary pass is measured against.
 __global__ __launch_bounds__(kBlock) void stream_read_kernel(const u32x4* __restrict__ buf, int64_t nvec,
                                                              uint32_t* sink) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;

@@ -86,7 +86,7 @@ C1_ROUNDS = 1000
 
 
 def full_case(label):
-    """A workload's whole batch at its full size, round 1."""
+    """A workload's whole batch at its full size, at round counter 1."""
     _, name, T, C, sig, V = next(c for c in FULL_CASES if c[0] == label)
     w = WORKLOADS[name] if V is None else scaled(WORKLOADS[name], V=V)
     zq, zp = make_logits(w, target_sigma=sig, device="cpu")

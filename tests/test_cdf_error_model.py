@@ -9,7 +9,7 @@ A worst-case bound of that error (every rounding of every term aligned) is about
 would exclude most rows.  The error that occurs is far smaller, because it is a
 weighted mean of many independent roundings.  This file measures it with a numpy
 model of the kernels' arithmetic -- not a copy of the kernels, and not run on the
-device it judges:
+device it checks:
 
   * c = fp32(log2(e) / T); every term is exp2 of the fp32 exponent fma(z, c, -o)
     (one rounding) with an integer offset o = rint(fp32(m c)) from a running lane
