@@ -40,9 +40,10 @@ enum { kPurposeAccept = 0, kPurposeBonus = 1, kPurposeDraft = 2, kPurposeFallbac
 enum { kErrTokenRange = 1, kErrQprimeZero = 2, kErrLenRange = 4, kErrSlotRange = 8 };
 constexpr int kXcds = 8;            // accelerator complex dies of MI355X
 constexpr int kFinalizeTwoWaveMaxPairs = 1024;  // (b, i) pairs up to the chip's SIMD count
-// Pass-2 grids of more than 8 tiles per SIMD are bound by their VALU work and take the
-// lean weighing; smaller ones (all waves resident at once) by load latency, where its
-// per-vector register pins cost more than its fewer instructions save.
+// Pass-2 grids of more than 8 tiles per SIMD take the lean weighing, for the bonus two
+// tiles per wave where rows are 16-byte aligned; smaller ones (all waves resident at
+// once) are bound by load latency, where the lean form's per-vector register pins cost
+// more than its fewer instructions save and fewer waves would load less at once.
 constexpr int64_t kPass2LeanMinTiles = 8192;
 
 // Blocks are dealt to the XCDs round-robin (block x runs on XCD x mod 8), and each XCD
@@ -1820,6 +1821,167 @@ __global__ __launch_bounds__(kBlock) void pass2_kernel(const Pass2Args a, int ng
     if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
 }
 
+// Sums of one lane's vector (vw of the weights, vp of p(x)), every element weighed as
+// uncached and summed as it is formed; a vector holding a cached id (F of V ids, so
+// rarely) is summed again with each element's own weight.  Both are the select form's
+// sums in its order, without the per-element arrays.
+template <int DT, int MODE>
+__device__ __forceinline__ void vec_sums(const WParams& wp, u32x4 rp, u32x4 rq, int64_t e0, const uint32_t* bits,
+                                         int64_t t0, double& vw, double& vp) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    uint32_t cbits = 0u;
+    if (MODE != kWP) cbits = (bits[(e0 - t0) >> 5] >> ((e0 - t0) & 31)) & ((1u << N) - 1u);
+    float zp[N], zq[N];
+    if (MODE != kWQprime) unpack_vec<DT>(rp, zp);
+    if (MODE != kWP) unpack_vec<DT>(rq, zq);
+    vw = 0.0;
+    vp = 0.0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        double pw;
+        vw += elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, MODE != kWP ? zq[e] : 0.f, false, &pw);
+        vp += pw;
+    }
+    if (MODE != kWP && cbits != 0u) {
+        // formed again from the raw vectors (kept from the compiler as new values, so the
+        // fast path's terms are not held for this branch)
+        __asm__ volatile("" : "+v"(rp), "+v"(rq));
+        if (MODE != kWQprime) unpack_vec<DT>(rp, zp);
+        unpack_vec<DT>(rq, zq);
+        vw = 0.0;
+        vp = 0.0;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            double pw;
+            vw += elem_weight_t<MODE>(wp, MODE != kWQprime ? zp[e] : 0.f, zq[e], (cbits >> e) & 1u, &pw);
+            vp += pw;
+        }
+    }
+}
+
+// The law of a row (the same in every lane) in scalar registers.
+__device__ __forceinline__ double uniform_f64(double v) {
+    return __builtin_bit_cast(double, uniform(__builtin_bit_cast(uint64_t, v)));
+}
+__device__ __forceinline__ float uniform_f32(float v) {
+    return __builtin_bit_cast(float, uniform(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ WParams uniform_wparams(WParams w) {
+    w.c = uniform_f32(w.c);
+    w.op = uniform_f32(w.op);
+    w.oq = uniform_f32(w.oq);
+    w.inv_p = uniform_f64(w.inv_p);
+    w.rho = uniform_f64(w.rho);
+    w.rhoC = uniform_f64(w.rhoC);
+    w.Cd = uniform_f64(w.Cd);
+    return w;
+}
+
+// Non-temporal loads of a pass-2 tile that lies inside the row (16-byte aligned rows).
+template <int DT>
+__device__ __forceinline__ void load_full_tile(const char* row, int t, int lane, u32x4 (&raw)[kVecPass2]) {
+    const u32x4* base =
+        reinterpret_cast<const u32x4*>(row + (int64_t)t * kTile2<DT> * ElemTraits<DT>::kBytes) + lane;
+#pragma unroll
+    for (int j = 0; j < kVecPass2; ++j) raw[j] = __builtin_nontemporal_load(base + j * kWave);
+}
+
+// Sums of one tile from its raw vectors, written to the tile's slot.
+template <int DT, int MODE>
+__device__ __forceinline__ void tile_sums_raw(const Pass2Args& a, int g, int t, const WParams& wp, int my_id,
+                                              uint32_t* bits, const u32x4 (&rp)[kVecPass2],
+                                              const u32x4 (&rq)[kVecPass2]) {
+    constexpr int N = ElemTraits<DT>::kPerVec;
+    const int lane = lane_id();
+    const int64_t t0 = (int64_t)t * kTile2<DT>;
+    if (MODE != kWP) tile_bitmap<DT>(bits, t0, my_id);
+    double sw = 0.0, sp = 0.0;
+#pragma unroll
+    for (int j = 0; j < kVecPass2; ++j) {
+        const int64_t e0 = t0 + (int64_t)(j * kWave + lane) * N;
+        double vw, vp;
+        vec_sums<DT, MODE>(wp, rp[j], rq[j], e0, bits, t0, vw, vp);
+        sw += vw;
+        sp += vp;
+        __asm__ volatile("" : "+v"(sw), "+v"(sp));  // one vector's terms live at a time
+    }
+    sw = wave_sum_f64(sw);
+    sp = wave_sum_f64(sp);
+    if (lane == 0) a.seg[(int64_t)g * a.nt + t] = make_double2(sw, sp);
+}
+
+// Sums of tiles t and t + 1 (if t + 1 < te) of one row pair by one wave.  The second
+// tile's loads are issued before the first tile is weighed (two register buffers), so
+// its HBM reads overlap the first tile's arithmetic; they are issued on every path that
+// weighs the first tile, so the wait before it covers that tile's loads alone.  A tile
+// that reaches past V is loaded on its own.  Each tile's sums are those of tile_sums.
+template <int DT, int MODE>
+__device__ __forceinline__ void tile_pair(const Pass2Args& a, int g, int64_t r, const char* prow, const char* qrow,
+                                          int t, int te, const int32_t* ids, int Fk, uint32_t* bits) {
+    const int lane = lane_id();
+    const int tf = min(te, a.V / kTile2<DT>);  // [t, tf): tiles inside the row
+    u32x4 rp[2][kVecPass2], rq[2][kVecPass2];
+    if (t < tf) {
+        if (MODE != kWQprime) load_full_tile<DT>(prow, t, lane, rp[0]);
+        if (MODE != kWP) load_full_tile<DT>(qrow, t, lane, rq[0]);
+    }
+    int my_id = -1;
+    if (MODE != kWP && lane < Fk) my_id = ids[lane];
+    WParams wp = a.law ? wparams_from(a.law[r], a.c, a.C) : make_wparams(a.c, a.C, MODE != kWQprime, load_law(a, r));
+    wp = uniform_wparams(wp);
+    if (t + 1 < tf) {
+        if (MODE != kWQprime) load_full_tile<DT>(prow, t + 1, lane, rp[1]);
+        if (MODE != kWP) load_full_tile<DT>(qrow, t + 1, lane, rq[1]);
+        tile_sums_raw<DT, MODE>(a, g, t, wp, my_id, bits, rp[0], rq[0]);
+        tile_sums_raw<DT, MODE>(a, g, t + 1, wp, my_id, bits, rp[1], rq[1]);
+    } else if (t < tf) {
+        tile_sums_raw<DT, MODE>(a, g, t, wp, my_id, bits, rp[0], rq[0]);
+    }
+    for (int tt = max(t, tf); tt < te; ++tt) {  // the row's ragged last tile
+        if (MODE != kWQprime) load_tile<DT, true, kVecPass2>(prow, (int64_t)tt * kTile2<DT>, a.V, lane, rp[0]);
+        if (MODE != kWP) load_tile<DT, true, kVecPass2>(qrow, (int64_t)tt * kTile2<DT>, a.V, lane, rq[0]);
+        tile_sums_raw<DT, MODE>(a, g, tt, wp, my_id, bits, rp[0], rq[0]);
+    }
+}
+
+// Large grids of 16-byte aligned rows: one wave per two adjacent tiles of a group, which
+// halves the waves' chains of loads before their first tile (the group's test outcomes,
+// then its law and tiles) and overlaps the second tile's reads with the first's weighing.
+// Bounded to 4 waves per SIMD (two tile buffers).
+template <int DT>
+__global__ __launch_bounds__(kBlock, 4) void pass2_pair_kernel(const Pass2Args a, int ngroups) {
+    __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
+    const int wave = threadIdx.x / kWave;
+    const int wpg = (a.nt + 1) / 2;  // waves per group
+    const int nblk = (wpg + kWavesPerBlock - 1) / kWavesPerBlock;
+    // group g on XCD g mod 8 (the bonus block of group g is block g)
+    const int y = blockIdx.x / kXcds;
+    const int g = (y / nblk) * kXcds + blockIdx.x % kXcds;
+    const int u = (y % nblk) * kWavesPerBlock + wave;
+    if (g >= ngroups || u >= wpg) return;
+    const int t = 2 * u, te = min(t + 2, a.nt);
+    int b, pos;
+    bool valid;
+    pass2_group(a, g, b, pos, valid);
+    if (!valid) {
+        if (lane_id() == 0)
+            for (int tt = t; tt < te; ++tt) a.seg[(int64_t)g * a.nt + tt] = make_double2(0.0, 0.0);
+        return;
+    }
+    const int64_t r = (int64_t)b * (a.K + 1) + pos;
+    const int mode = pass2_mode(a, pos);
+    const char* prow = a.p_logits ? a.p_logits + r * a.ld_bytes : nullptr;
+    const char* qrow = a.q_logits + r * a.ld_bytes;
+    const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
+    const int Fk = a.F[pos];
+    if (mode == kWResid)
+        tile_pair<DT, kWResid>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+    else if (mode == kWP)
+        tile_pair<DT, kWP>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+    else
+        tile_pair<DT, kWQprime>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+}
+
 // ============================================================================ small kernels
 // Per-row merges for the separate calls: one wave per row (same code as the round).
 __global__ __launch_bounds__(kBlock) void combine_stats_kernel(const Pass1Args a, float* m_out, double* s_out,
@@ -2156,6 +2318,16 @@ hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hi
     const int64_t grid = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * nblk;
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     const bool lean = (int64_t)ngroups * a.nt > kPass2LeanMinTiles;
+    if (lean && vec && a.mode == 0) {  // two tiles per wave (the draft law's one-row tiles keep one)
+        const int nb = ((a.nt + 1) / 2 + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int64_t g2 = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * nb;
+        if (g2 > INT_MAX) return hipErrorInvalidValue;
+        if (dtype == 1)
+            pass2_pair_kernel<1><<<(unsigned)g2, kBlock, 0, st>>>(a, ngroups);
+        else
+            pass2_pair_kernel<0><<<(unsigned)g2, kBlock, 0, st>>>(a, ngroups);
+        return hipGetLastError();
+    }
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
         if (lean)
             pass2_kernel<decltype(DT)::value, decltype(VEC)::value, true><<<(unsigned)grid, kBlock, 0, st>>>(a, ngroups);

@@ -126,6 +126,11 @@ EDGE_CASES = [
     # more than 1024 (sequence, position) pairs with more than 64 tiles per row: the
     # one-wave finalisation (large rounds) on its general path
     ("1025 pairs V=140k f32", "f32", 205, 4, 140001, 1.0, [8, 4, 2, 1, 1], 0.5, 2.0, 0.5, 0.0),
+    # bonus passes of more than 8192 tiles on 16-byte aligned rows (two tiles per wave):
+    # the row's last wave with a whole and a ragged tile (bf16, 64 tiles of 2048), or
+    # with a ragged tile alone (fp32, 117 tiles of 1024)
+    ("paired tiles bf16", "bf16", 130, 1, 130072, 1.0, [8, 4], 0.5, 2.0, 0.5, 0.0),
+    ("paired tiles f32", "f32", 72, 3, 119000, 1.0, [8, 4, 2, 1], 0.5, 2.0, 0.5, 0.0),
 ]
 
 
