@@ -427,13 +427,15 @@ def test_full_size_whole_batch(label):
     benchmark times, against the oracle sequence by sequence (c4 at three of its
     (target spread, C) points, c2 on its own recipe at each temperature).  c3 odd V:
     V = 128257, so every row after the first starts off a 16-byte boundary.  At most
-    max(1, 1e-3 B) sequences may be flagged; the count must equal the stored one."""
+    max(1, 1e-3 B) sequences may be flagged; the count must equal the stored one.  The
+    six separate calls, chained, must give the round's outputs bit for bit."""
     _case("full-size %s: inputs and oracle" % label)
     c = pc.full_case(label)
     w, F = c.w, np.array(c.F)
     o = c.oracle_round()
     _case("full-size %s: GPU round" % label)
-    g = gpu_round(c.zp.cuda(), c.zq.cuda(), c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, values=c.values)
+    zpd, zqd = c.zp.cuda(), c.zq.cuda()
+    g = gpu_round(zpd, zqd, c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback, values=c.values)
     flagged = compare_round(g, o, w.K, w.Bf, label=label, values=c.values)
     _check_flags(label, flagged)
     assert flagged <= max(1, w.B // 1000), (label, flagged)
@@ -446,6 +448,16 @@ def test_full_size_whole_batch(label):
         S = g["cache_ids"][b, O[k]:O[k + 1]]
         assert g["hit"][b] == (g["bonus"][b] in S)
     assert np.all(g["dev_err"] == 0)
+    # the six separate calls give the fused round's outputs bit for bit (at c4 and c5
+    # the residual draw's pass runs two tiles per wave in both)
+    _case("full-size %s: separate calls" % label)
+    ch = _chain(zpd, zqd, c.T, c.F, c.C, c.draft, c.seed, c.rnd, c.fallback)
+    for k in ch:
+        a, b = g[k], ch[k]
+        if k == "cache_ids":
+            a, b = a[:, :w.Bf], b[:, :w.Bf]
+        assert np.array_equal(a, b), (label, k)
+    del ch
     # coverage statistics of this round: the bonus ranks below F_k exactly on a hit,
     # and every rank equals the oracle's
     _case("full-size %s: bonus rank" % label)
