@@ -1947,18 +1947,17 @@ __device__ __forceinline__ void tile_pair(const Pass2Args& a, int g, int64_t r, 
 // Large grids of 16-byte aligned rows: one wave per two adjacent tiles of a group, which
 // halves the waves' chains of loads before their first tile (the group's test outcomes,
 // then its law and tiles) and overlaps the second tile's reads with the first's weighing.
-// Bounded to 4 waves per SIMD (two tile buffers).
+// Bounded to 4 waves per SIMD (two tile buffers).  One wave per block: a wave that ends
+// frees a slot that the next wave can take at once (a block of four waits for four).
 template <int DT>
-__global__ __launch_bounds__(kBlock, 4) void pass2_pair_kernel(const Pass2Args a, int ngroups) {
-    __shared__ uint32_t bits[kWavesPerBlock][kTile2<1> / 32];
-    const int wave = threadIdx.x / kWave;
-    const int wpg = (a.nt + 1) / 2;  // waves per group
-    const int nblk = (wpg + kWavesPerBlock - 1) / kWavesPerBlock;
+__global__ __launch_bounds__(kWave, 4) void pass2_pair_kernel(const Pass2Args a, int ngroups) {
+    __shared__ uint32_t bits[kTile2<1> / 32];
+    const int wpg = (a.nt + 1) / 2;  // waves (blocks) per group
     // group g on XCD g mod 8 (the bonus block of group g is block g)
     const int y = blockIdx.x / kXcds;
-    const int g = (y / nblk) * kXcds + blockIdx.x % kXcds;
-    const int u = (y % nblk) * kWavesPerBlock + wave;
-    if (g >= ngroups || u >= wpg) return;
+    const int g = (y / wpg) * kXcds + blockIdx.x % kXcds;
+    const int u = y % wpg;
+    if (g >= ngroups) return;
     const int t = 2 * u, te = min(t + 2, a.nt);
     int b, pos;
     bool valid;
@@ -1975,11 +1974,11 @@ __global__ __launch_bounds__(kBlock, 4) void pass2_pair_kernel(const Pass2Args a
     const int32_t* ids = a.cache_ids + (int64_t)b * a.Bf + a.O[pos];
     const int Fk = a.F[pos];
     if (mode == kWResid)
-        tile_pair<DT, kWResid>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+        tile_pair<DT, kWResid>(a, g, r, prow, qrow, t, te, ids, Fk, bits);
     else if (mode == kWP)
-        tile_pair<DT, kWP>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+        tile_pair<DT, kWP>(a, g, r, prow, qrow, t, te, ids, Fk, bits);
     else
-        tile_pair<DT, kWQprime>(a, g, r, prow, qrow, t, te, ids, Fk, bits[wave]);
+        tile_pair<DT, kWQprime>(a, g, r, prow, qrow, t, te, ids, Fk, bits);
 }
 
 // ============================================================================ small kernels
@@ -2319,13 +2318,12 @@ hipError_t launch_pass2(int dtype, bool vec, const Pass2Args& a, int ngroups, hi
     if (grid <= 0 || grid > INT_MAX) return hipErrorInvalidValue;
     const bool lean = (int64_t)ngroups * a.nt > kPass2LeanMinTiles;
     if (lean && vec && a.mode == 0) {  // two tiles per wave (the draft law's one-row tiles keep one)
-        const int nb = ((a.nt + 1) / 2 + kWavesPerBlock - 1) / kWavesPerBlock;
-        const int64_t g2 = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * nb;
+        const int64_t g2 = ((int64_t)ngroups + kXcds - 1) / kXcds * kXcds * ((a.nt + 1) / 2);
         if (g2 > INT_MAX) return hipErrorInvalidValue;
         if (dtype == 1)
-            pass2_pair_kernel<1><<<(unsigned)g2, kBlock, 0, st>>>(a, ngroups);
+            pass2_pair_kernel<1><<<(unsigned)g2, kWave, 0, st>>>(a, ngroups);
         else
-            pass2_pair_kernel<0><<<(unsigned)g2, kBlock, 0, st>>>(a, ngroups);
+            pass2_pair_kernel<0><<<(unsigned)g2, kWave, 0, st>>>(a, ngroups);
         return hipGetLastError();
     }
     return by_type(dtype, vec, [&](auto DT, auto VEC) {
