@@ -1,7 +1,8 @@
 """The no-allocation round: ssd_round_noalloc, whose scratch is the library's static
 per-GPU array, gives exactly the outputs of ssd_round with a caller workspace, on
 two calls in a row, the second with a smaller input (then the first shape again, over
-the scratch the smaller call left), and allocates nothing through torch."""
+the scratch the smaller call left, then a larger batch whose bonus pass takes two tiles
+per wave), and allocates nothing through torch."""
 import pytest
 import torch
 
@@ -41,9 +42,11 @@ def _run(w, T, zq, zp, draft, Fv, values, noalloc):
 def test_noalloc_matches_round():
     big = WORKLOADS["c3"]                                  # B=64 K=8 V=128256 bf16
     small = scaled(WORKLOADS["c2"], B=8, V=32001)          # fp32, odd vocabulary, 2 fewer positions
-    need = ssd.ssd_workspace_bytes(ssd.ssd_shape(big.B, big.K, big.V, big.V, ssd.SSD_BF16, 1.0), big.Bf)
-    assert need <= ssd.SSD_NOALLOC_SCRATCH_BYTES
-    for step, (w, T) in enumerate(((big, 1.0), (small, 0.7), (big, 1.0))):
+    large = WORKLOADS["c4"]                                # B=256 K=6: the two-tile bonus pass
+    for w in (big, large):
+        need = ssd.ssd_workspace_bytes(ssd.ssd_shape(w.B, w.K, w.V, w.V, ssd.SSD_BF16, 1.0), w.Bf)
+        assert need <= ssd.SSD_NOALLOC_SCRATCH_BYTES
+    for step, (w, T) in enumerate(((big, 1.0), (small, 0.7), (big, 1.0), (large, 1.2))):
         print("no-alloc step %d: %s B=%d K=%d V=%d %s T=%g" % (step, w.name, w.B, w.K, w.V, w.dtype, T), flush=True)
         zq, zp, draft, Fv, values = _inputs(w, step)
         ref, _ = _run(w, T, zq, zp, draft, Fv, values, noalloc=False)
