@@ -1596,7 +1596,8 @@ __device__ __forceinline__ double wave_scan_incl(double x) { return wave_prefix_
 // together.
 template <int DT, bool VEC, bool DEVRNG>
 __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, int pos, bool valid, int verrs,
-                                            double2 v0, uint32_t* bits, BonusShare& sh, int wave, float upre) {
+                                            double2 v0, double2 v1, uint32_t* bits, BonusShare& sh, int wave,
+                                            float upre) {
     const int lane = lane_id();
     const int K = a.K;
     const uint64_t round = DEVRNG ? *a.round_ptr : a.round;
@@ -1630,7 +1631,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
             for (int g0 = 0; g0 < nt; g0 += kWave) {
                 const int j = g0 + lane;
                 double2 v = v0;
-                if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+                if (g0 > 0) v = g0 == kWave ? v1 : (j < nt ? seg[j] : make_double2(0.0, 0.0));
                 tot_w += lane_f64(wave_scan_incl(v.x), kWave - 1);
             }
         }
@@ -1640,7 +1641,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
             for (int g0 = 0; g0 < nt; g0 += kWave) {
                 const int j = g0 + lane;
                 double2 v = v0;
-                if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+                if (g0 > 0) v = g0 == kWave ? v1 : (j < nt ? seg[j] : make_double2(0.0, 0.0));
                 tot_p += lane_f64(wave_scan_incl(v.y), kWave - 1);
             }
             mode = kWP;
@@ -1652,7 +1653,7 @@ __device__ __forceinline__ void bonus_block(const Pass2Args& a, int g, int b, in
         for (int g0 = 0; g0 < nt; g0 += kWave) {
             const int j = g0 + lane;
             double2 v = v0;
-            if (g0 > 0) v = j < nt ? seg[j] : make_double2(0.0, 0.0);
+            if (g0 > 0) v = g0 == kWave ? v1 : (j < nt ? seg[j] : make_double2(0.0, 0.0));
             const double x = use_p ? v.y : v.x;
             const double incl = (nt <= kWave && !use_p ? incl_w : wave_scan_incl(x)) + carry;
             const double excl = incl - x;
@@ -1758,8 +1759,10 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     const int g = blockIdx.x;
     if (g >= ngroups) return;  // uniform over the block
     const int lane = threadIdx.x % kWave;
-    // the group's tile sums do not depend on the accepted length: request them first
+    // the group's tile sums (their first two chunks of 64) do not depend on the accepted
+    // length: request them first
     const double2 v0 = lane < a.nt ? a.seg[(int64_t)g * a.nt + lane] : make_double2(0.0, 0.0);
+    const double2 v1 = kWave + lane < a.nt ? a.seg[(int64_t)g * a.nt + kWave + lane] : make_double2(0.0, 0.0);
     // the sequence's test outcomes (or its given accepted length), requested before the
     // uniforms below so that they load while those are computed
     int vf_or_len = 0;
@@ -1783,7 +1786,7 @@ __global__ __launch_bounds__(kBlock) void finalize_bonus_kernel(const Pass2Args 
     } else {
         pass2_group(a, g, b, pos, valid, &verrs);
     }
-    bonus_block<DT, VEC, DEVRNG>(a, g, b, pos, valid, verrs, v0, bits[wave], sh, wave, upre);
+    bonus_block<DT, VEC, DEVRNG>(a, g, b, pos, valid, verrs, v0, v1, bits[wave], sh, wave, upre);
 }
 
 // One wave per (group, tile): the residual (or target-law) sums of the tile.
