@@ -372,14 +372,18 @@ def test_bonus_rank_oracle_fed(case):
         assert np.array_equal(hist.cpu().numpy().astype(np.uint32), ohist), (case, rep)
 
 
-def test_residual_bad_len_and_greedy():
+@pytest.mark.parametrize("B,K,V,dtype", [(4, 3, 999, "f32"), (130, 1, 130072, "bf16")],
+                         ids=["small", "two-tile grid"])
+def test_residual_bad_len_and_greedy(B, K, V, dtype):
     """ssd_residual_sample with accepted lengths outside [0, K] reports the error and
-    returns -1; at T = 0 it returns argmax p_k."""
-    B, K, V = 4, 3, 999
-    zq, zp = _rand(B, K, V, "f32", 8)
-    F = [3, 2, 1, 1]
+    returns -1, and leaves every other sequence's bonus as it is with valid lengths
+    only; at T = 0 it returns argmax p_k.  The second case (8,320 pass-2 tiles on
+    aligned rows) takes the two-tile bonus pass."""
+    zq, zp = _rand(B, K, V, dtype, 8)
+    F = [3, 2, 1, 1][:K + 1]
+    bad = {2: -1, 3: K + 1}  # sequence: accepted length outside [0, K]
     for T in (1.0, 0.0):
-        _case("residual bad len T=%g" % T)
+        _case("residual bad len %s B=%d T=%g" % (dtype, B, T))
         zpd, zqd = zp.cuda(), zq.cuda()
         pm, ps, pa = _gpu_stats(zpd, T)
         qm, qs, qa = _gpu_stats(zqd, T)
@@ -389,19 +393,28 @@ def test_residual_bad_len_and_greedy():
         ssd.ssd_build_cache(shape, zqd, qm, qs, F, ids, mass)
         Z = torch.zeros(B * (K + 1), dtype=torch.float64, device="cuda")
         ssd.ssd_saguaro_reweight(shape, mass, 0.5, Z)
-        acc = torch.tensor([0, 3, -1, 4], dtype=torch.int32, device="cuda")
-        bonus = torch.zeros(B, dtype=torch.int32, device="cuda")
-        err = torch.zeros(B, dtype=torch.int32, device="cuda")
-        ssd.ssd_residual_sample(shape, zpd, zqd, pm, ps, pa, qm, qs, F, ids, Z, 0.5, acc, 1, 2, bonus, None, err)
-        torch.cuda.synchronize()
-        bo = bonus.cpu().numpy()
-        eo = err.cpu().numpy()
-        assert bo[2] == -1 and bo[3] == -1
-        assert eo[2] == ssd.SSD_DEVERR_LEN_RANGE and eo[3] == ssd.SSD_DEVERR_LEN_RANGE
-        assert eo[0] == 0 and eo[1] == 0
+        good = torch.arange(B, dtype=torch.int32, device="cuda") % (K + 1)
+        out = {}
+        for name, acc in (("good", good), ("bad", good.clone())):
+            if name == "bad":
+                for b_, v_ in bad.items():
+                    acc[b_] = v_
+            bonus = torch.zeros(B, dtype=torch.int32, device="cuda")
+            err = torch.zeros(B, dtype=torch.int32, device="cuda")
+            ssd.ssd_residual_sample(shape, zpd, zqd, pm, ps, pa, qm, qs, F, ids, Z, 0.5, acc, 1, 2, bonus, None, err)
+            torch.cuda.synchronize()
+            out[name] = (bonus.cpu().numpy(), err.cpu().numpy())
+        bo, eo = out["bad"]
+        for b_ in bad:
+            assert bo[b_] == -1 and eo[b_] == ssd.SSD_DEVERR_LEN_RANGE
+        rest = np.array([b_ not in bad for b_ in range(B)])
+        assert np.all(eo[rest] == 0) and np.all(out["good"][1] == 0)
+        assert np.array_equal(bo[rest], out["good"][0][rest])
+        assert np.all((bo[rest] >= 0) & (bo[rest] < V))
         if T == 0.0:
-            ap = np.argmax(zp.numpy(), -1)
-            assert bo[0] == ap[0, 0] and bo[1] == ap[1, 3]
+            ap = np.argmax(zp.float().numpy(), -1)  # bf16 widens exactly; lowest id on ties
+            k = good.cpu().numpy()
+            assert all(bo[b_] == ap[b_, k[b_]] for b_ in range(B) if rest[b_])
 
 
 # ----------------------------------------------------------------------------- workloads
