@@ -35,10 +35,13 @@ def _inputs(w, buffer):
     return zp, zq, d
 
 
-@pytest.mark.parametrize("wl,T", [("c3", 1.0), ("c5", 1.0), ("c2", 0.0)])
-def test_round_graph_replays_match_eager(wl, T):
-    print("\n[case] graph capture of the round, %s recipe, T=%g" % (wl, T), flush=True)
-    w = replace(scaled(WORKLOADS[wl], B=16, V=20000), temps=(T,))
+# (recipe, T, B, V); the last case has 8,320 pass-2 tiles on aligned rows, so its bonus
+# pass takes two tiles per wave
+@pytest.mark.parametrize("wl,T,B,V", [("c3", 1.0, 16, 20000), ("c5", 1.0, 16, 20000), ("c2", 0.0, 16, 20000),
+                                      ("c4", 1.2, 130, 130072)])
+def test_round_graph_replays_match_eager(wl, T, B, V):
+    print("\n[case] graph capture of the round, %s recipe, T=%g, B=%d, V=%d" % (wl, T, B, V), flush=True)
+    w = replace(scaled(WORKLOADS[wl], B=B, V=V), temps=(T,))
     F = ssd.ssd_fanout(w.K, w.Bf, w.r)
     C = w.Cs[0]
     fallback = ssd.SSD_FALLBACK_UNIFORM if w.fallback_uniform else ssd.SSD_FALLBACK_NONE
